@@ -1,0 +1,103 @@
+"""Batched per-request sampler (oracle side; test infrastructure only).
+
+Semantics follow "Engine 与采样器", section 采样器 (Sampler.sample and the
+torch reference sample_torch), and "Mini-SGLang 源码解析（四）：GPU 计算引擎系统"
+sections 14.3-14.4:
+
+* no temperature array -> the whole batch is greedy -> argmax of the logits;
+* otherwise per row: probabilities softmax(logits / T); rank tokens by
+  probability; top-k keeps ranks < k; the kept mass is renormalised; top-p
+  keeps a token iff the renormalised mass ranked *before* it is < p (so the
+  most probable token always survives); top-k is applied before top-p; one
+  token is drawn from what is left.
+
+Readings where the pages leave the step open (each listed in the design
+notes):
+
+* a row whose temperature is <= 1e-6 is an exact argmax (the pages give greedy
+  rows of a mixed batch T = 1e-6 and say the effect is argmax);
+* argmax ties go to the lowest index; ranking ties (equal logits) are broken
+  by ascending index, so top-k keeps exactly k tokens; the ranking is taken on
+  the logits, which orders tokens exactly like the probabilities for T > 0;
+* top_k <= 0 or >= vocab means no top-k; top_p >= 1 means no top-p;
+* the draw is inverse-CDF sampling with one caller-supplied uniform u in
+  [0, 1) per row, scanning the kept weights in vocabulary index order: the
+  token is the smallest index whose running kept mass exceeds u * (total kept
+  mass), or the last kept index if rounding finds none (the pages fix only the
+  distribution, via torch.multinomial or FlashInfer's rejection sampler);
+* a row is *flagged* when a floating-point boundary lies within DELTA
+  (relative to the kept mass) of the decision: the top-p cut or the draw. The
+  GPU computes those sums in another order and precision, so flagged rows are
+  excluded from the bit-exact comparison and counted. Argmax and top-k are
+  pure order comparisons and are never flagged.
+"""
+
+import numpy as np
+
+from .sampling_params import MIN_P, MIN_T
+
+DELTA = 1e-5
+
+
+def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
+               delta: float = DELTA, info: dict | None = None):
+    """logits: f64 [V]. T, top_k, top_p are this row's device-side values
+    (float32/int32 as the kernel sees them). Returns (token, flagged)."""
+    l = np.asarray(logits, dtype=np.float64)
+    V = l.shape[0]
+    if np.float32(T) <= np.float32(MIN_T):
+        return int(np.argmax(l)), False                      # first maximum = lowest index
+    z = l / np.float64(np.float32(T))
+    e = np.exp(z - z.max())                                  # unnormalised probabilities
+    order = np.lexsort((np.arange(V), -l))                   # logit desc, index asc
+    k = V if (top_k <= 0 or top_k >= V) else int(top_k)
+    ranked = order[:k]                                       # top-k: ranks < k
+    flagged = False
+    p = np.float64(np.float32(top_p))
+    if p < 1.0:
+        p = max(p, MIN_P)
+        q = e[ranked] / e[ranked].sum()                      # renormalise the kept mass
+        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))  # mass ranked before each token
+        n_keep = int(np.count_nonzero(before < p))           # a prefix; >= 1 since before[0] = 0
+        margin = p - before[n_keep - 1]
+        if n_keep < k:
+            margin = min(margin, before[n_keep] - p)
+        if margin < delta:
+            flagged = True
+        ranked = ranked[:n_keep]
+        if info is not None:
+            info["top_p_margin"] = float(margin)
+    w = np.zeros(V, dtype=np.float64)
+    w[ranked] = e[ranked]
+    c = np.cumsum(w)
+    W = c[-1]
+    target = np.float64(np.float32(u)) * W
+    i = int(np.searchsorted(c, target, side="right"))      # first index with c > target
+    if i >= V:
+        i = int(ranked.max())
+    lo = c[i - 1] if i > 0 else 0.0
+    draw_margin = min(target - lo, c[i] - target) / W
+    if draw_margin < delta:
+        flagged = True
+    if info is not None:
+        info.update(kept=int(len(ranked)), draw_margin=float(draw_margin), W=float(W))
+    return i, flagged
+
+
+def sample(logits: np.ndarray, temperature, top_k, top_p, uniforms, delta: float = DELTA,
+           rows=None):
+    """logits: f64 [bs, V]; temperature / top_k / top_p: per-row device
+    arrays or None (None temperature = all-greedy batch). Returns
+    (tokens int32 [bs], flagged bool [bs])."""
+    bs = logits.shape[0]
+    tokens = np.full(bs, -1, dtype=np.int32)
+    flagged = np.zeros(bs, dtype=bool)
+    for r in (range(bs) if rows is None else rows):
+        if temperature is None:
+            tokens[r] = int(np.argmax(logits[r]))
+            continue
+        k = -1 if top_k is None else int(top_k[r])
+        p = 1.0 if top_p is None else float(top_p[r])
+        tokens[r], flagged[r] = sample_row(logits[r], float(temperature[r]), k, p,
+                                           float(uniforms[r]), delta)
+    return tokens, flagged
