@@ -1,0 +1,25 @@
+"""paged_kv_attention_scatter_amd: paged KV attention, KV scatter and batched
+sampling for MI355X (gfx950).
+
+The product is libpkv.so (hand-written HIP kernels behind the C ABI of
+include/pkv.h). This package is its thin Python binding:
+
+* store_kv                  -- pkv_store_kv
+* paged_attention_decode    -- pkv_paged_attention_decode
+* paged_attention_extend    -- pkv_paged_attention_extend
+* sample                    -- pkv_sample
+* num_pages, prepare_sampling, read_faults -- host helpers
+
+Build the library with ``python -m paged_kv_attention_scatter_amd.build``.
+"""
+
+from .api import (HEAD_DIM, decode_workspace_size, extend_workspace_size, make_pool, num_pages,
+                  paged_attention_decode, paged_attention_extend, prepare_sampling, read_faults,
+                  sample, sample_workspace_size, store_kv, version)
+from ._lib import LIB_PATH, PkvError, lib
+
+__all__ = [
+    "HEAD_DIM", "LIB_PATH", "PkvError", "lib", "make_pool", "store_kv", "paged_attention_decode",
+    "paged_attention_extend", "sample", "num_pages", "prepare_sampling", "read_faults",
+    "decode_workspace_size", "extend_workspace_size", "sample_workspace_size", "version",
+]

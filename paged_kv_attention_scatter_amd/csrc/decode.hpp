@@ -1,0 +1,352 @@
+// Paged GQA decode attention: split-K over a flattened key space.
+//
+// Definition ("第 0 步：一个能跑的最小推理引擎", the dense attention function,
+// with one query row): query head h of request r reads KV head
+// g = h / (HQ / HKV); s_j = scale * q . K[slot(r, j)] over the request's
+// device_len keys; o = softmax(s) . V. The slots come from the request's row
+// of the token-granular page table ("核心数据结构：Req、Batch、Context",
+// section Context).
+//
+// Work split (an intra-GPU split-KV, not the pages' design, which calls
+// FlashInfer's decode kernel): the keys of all requests are laid end to end
+// (cu = exclusive prefix sum of device_len) and cut into P equal items, so the
+// work per workgroup is the same whatever the length mix. Item i covers keys
+// [i*T/P, (i+1)*T/P). A request cut by item boundaries yields one partial
+// (running max m, sum l, unnormalised accumulator) per item it touches,
+// stored at partial slot (item + request); a second kernel merges them. A
+// request that lies inside one item is finished in place.
+//
+// Inside an item, each of the NWAVE waves takes a contiguous quarter of the
+// segment's keys. One token row of the pool (all HKV heads x 128 dims, 2 KiB
+// in bf16) is read by one wave: lane l covers KV head l / (64 / HKV) and
+// DPL = 2 * HKV consecutive dims, so every load instruction moves one whole
+// row, coalesced, whatever the slot. The q.K partial dot of a lane is
+// reduced over the 64 / HKV lanes of its head with DPP. Each lane keeps the
+// online-softmax state of its head's G query heads for its dims; the waves of
+// the workgroup merge through LDS at the end of a segment. No LDS staging of
+// K/V: every K/V element is used by exactly one wave.
+#pragma once
+
+#include "common.hpp"
+
+namespace pkv {
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+struct DecodeArgs {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t pool_row;     // elements between slots
+  int64_t num_slots;
+  const void* q;
+  int64_t q_stride;     // elements between query tokens
+  void* o;
+  int64_t o_stride;
+  int32_t bs;
+  int32_t num_items;    // P
+  const int32_t* page_table;
+  int32_t pt_rows;
+  int64_t pt_stride;
+  const int32_t* table_idx;
+  const int32_t* device_len;
+  float scale_log2;     // sm_scale * log2(e)
+  float* part_ml;       // [P + bs][HQ][2]  (m in log2 units, l)
+  float* part_acc;      // [P + bs][HQ][128]
+  int32_t* cu_out;      // [bs + 1] prefix of valid lengths (written by block 0)
+  uint32_t* faults;
+};
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kPerWord = 2;
+};
+template <>
+struct ElemTraits<float> {
+  static constexpr int kPerWord = 1;
+};
+
+// Item containing flattened key position p (largest i with floor(i*T/P) <= p).
+__device__ __forceinline__ int item_of(int64_t p, int64_t T, int P) {
+  return (int)(((p + 1) * (int64_t)P - 1) / T);
+}
+__device__ __forceinline__ int64_t item_begin(int i, int64_t T, int P) {
+  return ((int64_t)i * T) / P;
+}
+
+template <typename T, int NWD>
+__device__ __forceinline__ void load_lane_row(uint32_t (&w)[NWD], const T* base) {
+  // NWD words = NWD * 4 bytes, 16-byte aligned (DPL * sizeof(T) >= 16 for the
+  // supported shapes).
+  const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < NWD / 4; ++i) {
+    u32x4 x = __builtin_nontemporal_load(p + i);
+    w[4 * i + 0] = x.x;
+    w[4 * i + 1] = x.y;
+    w[4 * i + 2] = x.z;
+    w[4 * i + 3] = x.w;
+  }
+}
+
+template <typename T, int NWD>
+__device__ __forceinline__ float lane_dot(const uint32_t (&qw)[NWD], const uint32_t (&kw)[NWD]) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NWD; ++i)
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, qw[i]),
+                                          __builtin_bit_cast(bf16x2_v, kw[i]), s, false);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) s = fmaf(__uint_as_float(qw[i]), __uint_as_float(kw[i]), s);
+  }
+  return s;
+}
+
+template <typename T, int NWD>
+__device__ __forceinline__ void lane_axpy(float (&acc)[NWD * ElemTraits<T>::kPerWord], float p,
+                                          const uint32_t (&vw)[NWD]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) {
+      acc[2 * i] = fmaf(p, bf16_lo(vw[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(p, bf16_hi(vw[i]), acc[2 * i + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) acc[i] = fmaf(p, __uint_as_float(vw[i]), acc[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* o, float x);
+template <>
+__device__ __forceinline__ void store_out<bf16_t>(bf16_t* o, float x) {
+  *o = (bf16_t)f32_to_bf16_bits(x);
+}
+template <>
+__device__ __forceinline__ void store_out<float>(float* o, float x) {
+  *o = x;
+}
+
+template <typename T, int HKV, int G, int NWAVE, int KB>
+__global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a) {
+  constexpr int HQ = HKV * G;
+  constexpr int LPH = kWave / HKV;              // lanes per KV head
+  constexpr int DPL = kHeadDim / LPH;           // dims per lane
+  constexpr int EPW = ElemTraits<T>::kPerWord;
+  constexpr int NWD = DPL / EPW;                // 32-bit words per lane per row
+  constexpr int NT = NWAVE * kWave;
+  static_assert(NWD % 4 == 0, "lane share of a row must be a multiple of 16 bytes");
+
+  extern __shared__ int32_t cu[];               // [bs + 1]
+  __shared__ float sm_m[NWAVE][HQ];
+  __shared__ float sm_l[NWAVE][HQ];
+  __shared__ float sm_acc[NWAVE][HQ][kHeadDim];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane / LPH;
+  const int dofs = (lane % LPH) * DPL;
+  const int bs = a.bs;
+
+  const bool report = blockIdx.x == 0;
+  block_exclusive_scan<NT>(cu, bs, [&](int r) -> int32_t {
+    const int32_t s = a.device_len[r];
+    const int32_t row = a.table_idx ? a.table_idx[r] : r;
+    const bool row_ok = row >= 0 && row < a.pt_rows;
+    const bool len_ok = s >= 1 && (int64_t)s <= a.pt_stride;
+    if (report && !row_ok) raise_fault(a.faults, 0x8u);
+    if (report && !len_ok) raise_fault(a.faults, 0x2u);
+    return (row_ok && len_ok) ? s : 0;
+  });
+  if (report)
+    for (int i = threadIdx.x; i <= bs; i += NT) a.cu_out[i] = cu[i];
+
+  const int64_t total = cu[bs];
+  const int P = a.num_items;
+  const int item = blockIdx.x;
+  if (total == 0) return;
+  const int64_t b0 = item_begin(item, total, P), b1 = item_begin(item + 1, total, P);
+  if (b0 >= b1) return;
+
+  // First request whose key range contains b0: largest r with cu[r] <= b0.
+  int lo = 0, hi = bs;  // invariant: cu[lo] <= b0 < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= b0) lo = mid; else hi = mid;
+  }
+  int r = lo;
+
+  const T* kpool = reinterpret_cast<const T*>(a.k_pool);
+  const T* vpool = reinterpret_cast<const T*>(a.v_pool);
+  const int64_t head_ofs = (int64_t)g * kHeadDim + dofs;
+
+  int64_t pos = b0;
+  while (pos < b1) {
+    while (cu[r + 1] <= pos) ++r;  // skip empty requests
+    const int64_t seg_end = min(b1, (int64_t)cu[r + 1]);
+    const int32_t S = cu[r + 1] - cu[r];
+    const int32_t j0 = (int32_t)(pos - cu[r]), j1 = (int32_t)(seg_end - cu[r]);
+    const int32_t row = a.table_idx ? a.table_idx[r] : r;
+    const int32_t* pt = a.page_table + (int64_t)row * a.pt_stride;
+
+    // q of this lane's G heads.
+    uint32_t qw[G][NWD];
+    {
+      const T* qb = reinterpret_cast<const T*>(a.q) + (int64_t)r * a.q_stride;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+        load_lane_row<T, NWD>(qw[hh], qb + (int64_t)(g * G + hh) * kHeadDim + dofs);
+    }
+
+    float m[G], l[G], acc[G][DPL];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
+    }
+
+    const int32_t len = j1 - j0;
+    const int32_t per = (len + NWAVE - 1) / NWAVE;
+    const int32_t wj0 = min(j1, j0 + wave * per);
+    const int32_t wj1 = min(j1, wj0 + per);
+
+    for (int32_t jb = wj0; jb < wj1; jb += kWave) {
+      const int32_t nchunk = min(kWave, wj1 - jb);
+      int32_t myslot = -1;
+      if (lane < nchunk) {
+        const int32_t s = pt[jb + lane];
+        if (s >= 0 && (int64_t)s < a.num_slots) myslot = s;
+        else raise_fault(a.faults, 0x4u);
+      }
+      for (int32_t kb = 0; kb < nchunk; kb += KB) {
+        uint32_t kw[KB][NWD], vw[KB][NWD];
+        int32_t sl[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          sl[kk] = (kb + kk < nchunk) ? __builtin_amdgcn_readlane(myslot, kb + kk) : -1;
+          if (sl[kk] >= 0) {
+            load_lane_row<T, NWD>(kw[kk], kpool + (int64_t)sl[kk] * a.pool_row + head_ofs);
+            load_lane_row<T, NWD>(vw[kk], vpool + (int64_t)sl[kk] * a.pool_row + head_ofs);
+          } else {
+#pragma unroll
+            for (int i = 0; i < NWD; ++i) kw[kk][i] = vw[kk][i] = 0u;
+          }
+        }
+        float sc[KB][G];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            const float d = group_sum<LPH>(lane_dot<T, NWD>(qw[hh], kw[kk]));
+            sc[kk][hh] = sl[kk] >= 0 ? d * a.scale_log2 : -INFINITY;
+          }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float mb = sc[0][hh];
+#pragma unroll
+          for (int kk = 1; kk < KB; ++kk) mb = fmaxf(mb, sc[kk][hh]);
+          const float mn = fmaxf(m[hh], mb);
+          if (mn == -INFINITY) continue;          // nothing valid yet for this head
+          if (mn > m[hh]) {
+            const float corr = fast_exp2(m[hh] - mn);
+            l[hh] *= corr;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr;
+            m[hh] = mn;
+          }
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) {
+            const float p = fast_exp2(sc[kk][hh] - mn);
+            l[hh] += p;
+            lane_axpy<T, NWD>(acc[hh], p, vw[kk]);
+          }
+        }
+      }
+    }
+
+    // Merge the waves of this workgroup.
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = g * G + hh;
+      if (lane % LPH == 0) {
+        sm_m[wave][h] = m[hh];
+        sm_l[wave][h] = l[hh];
+      }
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) sm_acc[wave][h][dofs + d] = acc[hh][d];
+    }
+    __syncthreads();
+    const bool final_out = (j0 == 0 && j1 == S);
+    const int slot = item + r;
+    for (int idx = threadIdx.x; idx < HQ * kHeadDim; idx += NT) {
+      const int h = idx / kHeadDim, d = idx % kHeadDim;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, sm_m[w][h]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) {
+        const float mw = sm_m[w][h];
+        const float c = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        L += sm_l[w][h] * c;
+        A += sm_acc[w][h][d] * c;
+      }
+      if (final_out) {
+        T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride + (int64_t)h * kHeadDim + d;
+        store_out<T>(ob, L > 0.f ? A / L : 0.f);
+      } else {
+        a.part_acc[((int64_t)slot * HQ + h) * kHeadDim + d] = A;
+        if (d == 0) {
+          a.part_ml[((int64_t)slot * HQ + h) * 2 + 0] = M;
+          a.part_ml[((int64_t)slot * HQ + h) * 2 + 1] = L;
+        }
+      }
+    }
+    __syncthreads();
+    pos = seg_end;
+  }
+}
+
+// Merge the partials of every request that was cut by item boundaries; zero
+// the output of requests whose lengths were invalid. One workgroup per request.
+template <typename T, int HQ>
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+  const int r = blockIdx.x;
+  const int32_t* cu = a.cu_out;
+  const int64_t total = cu[a.bs];
+  const int32_t c0 = cu[r], c1 = cu[r + 1];
+  T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride;
+  if (c1 == c0) {  // invalid request: skipped by the main kernel
+    for (int idx = threadIdx.x; idx < HQ * kHeadDim; idx += blockDim.x) store_out<T>(ob + idx, 0.f);
+    return;
+  }
+  const int P = a.num_items;
+  const int i0 = item_of(c0, total, P), i1 = item_of(c1 - 1, total, P);
+  if (i0 == i1) return;  // finished in place
+  for (int idx = threadIdx.x; idx < HQ * kHeadDim; idx += blockDim.x) {
+    const int h = idx / kHeadDim, d = idx % kHeadDim;
+    float M = -INFINITY;
+    for (int i = i0; i <= i1; ++i) {
+      if (item_begin(i, total, P) == item_begin(i + 1, total, P)) continue;  // empty item
+      M = fmaxf(M, a.part_ml[((int64_t)(i + r) * HQ + h) * 2]);
+    }
+    float L = 0.f, A = 0.f;
+    for (int i = i0; i <= i1; ++i) {
+      if (item_begin(i, total, P) == item_begin(i + 1, total, P)) continue;
+      const int64_t s = (int64_t)(i + r) * HQ + h;
+      const float mi = a.part_ml[s * 2];
+      const float c = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+      L += a.part_ml[s * 2 + 1] * c;
+      A += a.part_acc[s * kHeadDim + d] * c;
+    }
+    store_out<T>(ob + (int64_t)h * kHeadDim + d, L > 0.f ? A / L : 0.f);
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,365 @@
+// libpkv: host side of the C ABI declared in include/pkv.h.
+//
+// Every entry point validates its arguments on the host (returning a
+// negative pkv_status before anything is enqueued), then launches the gfx950
+// kernels on the caller's stream. The library allocates no device memory;
+// the only device state it owns is the 4-byte fault word below.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "pkv.h"
+#include "common.hpp"
+#include "store_kv.hpp"
+#include "decode.hpp"
+#include "extend.hpp"
+#include "sample.hpp"
+
+// Kernels OR PKV_FAULT_* bits into this word when they meet out-of-range data.
+__device__ uint32_t pkv_fault_word;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return PKV_OK;
+}
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  bool init = false;
+  int status = PKV_OK;
+  uint32_t* faults = nullptr;  // device address of pkv_fault_word on this device
+  int num_cus = 0;
+};
+
+std::mutex g_dev_mutex;
+DeviceState g_dev[kMaxDevices];
+
+// Per-device set-up: check the part is gfx950 and resolve the fault word's
+// device address (the symbol's host-side name is not a device pointer).
+int device_state(DeviceState** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_DEVICE, "device index %d unsupported", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceState& s = g_dev[dev];
+  if (!s.init) {
+    s.init = true;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      s.status = PKV_ERR_HIP;
+    } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      s.status = PKV_ERR_DEVICE;
+    } else {
+      s.num_cus = prop.multiProcessorCount;
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(pkv_fault_word));
+      if (e != hipSuccess) s.status = PKV_ERR_HIP;
+      else s.faults = static_cast<uint32_t*>(p);
+    }
+  }
+  if (s.status != PKV_OK)
+    return fail(s.status, "device %d unusable (needs gfx950; HIP set-up failed or wrong arch)", dev);
+  *out = &s;
+  return PKV_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int itemsize(int32_t dtype) { return dtype == PKV_BF16 ? 2 : (dtype == PKV_F32 ? 4 : 0); }
+
+// Validates the pool descriptor; on success *isz is the element size.
+int check_pool(const pkv_pool* pool, int* isz) {
+  if (!pool) return fail(PKV_ERR_NULL, "pool is NULL");
+  if (!pool->k || !pool->v) return fail(PKV_ERR_NULL, "pool.k / pool.v is NULL");
+  *isz = itemsize(pool->dtype);
+  if (!*isz) return fail(PKV_ERR_DTYPE, "pool.dtype %d is not PKV_F32 or PKV_BF16", pool->dtype);
+  if (pool->head_dim != pkv::kHeadDim)
+    return fail(PKV_ERR_SHAPE, "head_dim %d unsupported (must be 128)", pool->head_dim);
+  if (pool->kv_heads < 1 || pool->kv_heads > 64)
+    return fail(PKV_ERR_SHAPE, "kv_heads %d out of range", pool->kv_heads);
+  if (pool->num_slots < 1) return fail(PKV_ERR_SHAPE, "num_slots %lld < 1", (long long)pool->num_slots);
+  if (pool->page_size < 1) return fail(PKV_ERR_SHAPE, "page_size %d < 1", pool->page_size);
+  const int64_t row = (int64_t)pool->kv_heads * pool->head_dim;
+  if (pool->row_stride < row)
+    return fail(PKV_ERR_SHAPE, "row_stride %lld < kv_heads * head_dim %lld",
+                (long long)pool->row_stride, (long long)row);
+  if (!aligned16(pool->k) || !aligned16(pool->v) || (pool->row_stride * *isz) % 16)
+    return fail(PKV_ERR_ALIGN, "pool pointers and row_stride * itemsize must be 16-byte aligned");
+  return PKV_OK;
+}
+
+int check_rows(const void* p, int64_t stride, int64_t min_stride, int isz, const char* name) {
+  if (!p) return fail(PKV_ERR_NULL, "%s is NULL", name);
+  if (stride < min_stride)
+    return fail(PKV_ERR_SHAPE, "%s row stride %lld < %lld", name, (long long)stride, (long long)min_stride);
+  if (!aligned16(p) || (stride * isz) % 16)
+    return fail(PKV_ERR_ALIGN, "%s pointer and row stride * itemsize must be 16-byte aligned", name);
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------------ decode plan
+
+constexpr int kDecodeMaxItems = 1024;     // 256 CUs x 4 resident workgroups
+constexpr int kDecodeKeysPerItem = 256;   // smallest item worth a workgroup
+constexpr int kDecodeMaxBatch = 4096;     // prefix sums of lengths live in LDS
+
+int decode_items(int64_t max_total_kv) {
+  int64_t p = (max_total_kv + kDecodeKeysPerItem - 1) / kDecodeKeysPerItem;
+  if (p < 1) p = 1;
+  if (p > kDecodeMaxItems) p = kDecodeMaxItems;
+  return (int)p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct DecodeWs {
+  size_t cu, ml, acc, total;
+};
+
+DecodeWs decode_ws_layout(int32_t bs, int32_t hq, int64_t max_total_kv) {
+  const int64_t slots = (int64_t)decode_items(max_total_kv) + bs;
+  DecodeWs w;
+  w.cu = 0;
+  w.ml = align256((size_t)(bs + 1) * 4);
+  w.acc = w.ml + align256((size_t)slots * hq * 2 * 4);
+  w.total = w.acc + align256((size_t)slots * hq * pkv::kHeadDim * 4);
+  return w;
+}
+
+template <typename T, int HKV, int G>
+int launch_decode(const pkv::DecodeArgs& a, hipStream_t s) {
+  constexpr int NWAVE = 4;
+  constexpr int KB = sizeof(T) == 2 ? 4 : 2;
+  const size_t dyn = (size_t)(a.bs + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL((pkv::decode_splitk_kernel<T, HKV, G, NWAVE, KB>), dim3(a.num_items),
+                     dim3(NWAVE * 64), dyn, s, a);
+  int rc = check_launch("decode_splitk");
+  if (rc) return rc;
+  hipLaunchKernelGGL((pkv::decode_combine_kernel<T, HKV * G>), dim3(a.bs), dim3(256), 0, s, a);
+  return check_launch("decode_combine");
+}
+
+template <typename T>
+int dispatch_decode(int hkv, int g, const pkv::DecodeArgs& a, hipStream_t s) {
+#define PKV_DECODE_CASE(H, GG) \
+  if (hkv == H && g == GG) return launch_decode<T, H, GG>(a, s);
+  if constexpr (sizeof(T) == 2) {
+    PKV_DECODE_CASE(8, 1) PKV_DECODE_CASE(8, 2) PKV_DECODE_CASE(8, 4)
+    PKV_DECODE_CASE(4, 1) PKV_DECODE_CASE(4, 2) PKV_DECODE_CASE(4, 4)
+  } else {
+    PKV_DECODE_CASE(8, 1) PKV_DECODE_CASE(8, 2) PKV_DECODE_CASE(8, 4)
+    PKV_DECODE_CASE(4, 1) PKV_DECODE_CASE(4, 2) PKV_DECODE_CASE(4, 4)
+    PKV_DECODE_CASE(2, 2) PKV_DECODE_CASE(2, 4)
+  }
+#undef PKV_DECODE_CASE
+  return fail(PKV_ERR_SHAPE, "decode: kv_heads %d with %d query heads per KV head is not built", hkv, g);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+int pkv_read_faults(void* stream, uint32_t* faults) {
+  if (!faults) return fail(PKV_ERR_NULL, "faults is NULL");
+  DeviceState* ds;
+  int rc = device_state(&ds);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ds->faults, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemsetAsync(ds->faults, 0, sizeof v, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "reading the fault word: %s", hipGetErrorString(e));
+  *faults = v;
+  return ok();
+}
+
+int pkv_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,
+                 const void* k, int64_t k_stride, const void* v, int64_t v_stride, void* stream) {
+  int isz = 0;
+  int rc = check_pool(pool, &isz);
+  if (rc) return rc;
+  if (n < 0) return fail(PKV_ERR_SHAPE, "n = %lld < 0", (long long)n);
+  if (loc_type != PKV_I32 && loc_type != PKV_I64)
+    return fail(PKV_ERR_DTYPE, "loc_type %d is not PKV_I32 or PKV_I64", loc_type);
+  if (n == 0) return ok();
+  if (!out_loc) return fail(PKV_ERR_NULL, "out_loc is NULL");
+  const int64_t row = (int64_t)pool->kv_heads * pool->head_dim;
+  if ((rc = check_rows(k, k_stride, row, isz, "k"))) return rc;
+  if ((rc = check_rows(v, v_stride, row, isz, "v"))) return rc;
+  DeviceState* ds;
+  if ((rc = device_state(&ds))) return rc;
+  constexpr int PK = 4;
+  const int32_t packets = (int32_t)(row * isz / 16);
+  const int64_t threads = n * (packets / PK);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "n = %lld too large", (long long)n);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t pool_pk = pool->row_stride * isz / 16, k_pk = k_stride * isz / 16, v_pk = v_stride * isz / 16;
+  pkv::u32x4* kp = static_cast<pkv::u32x4*>(pool->k);
+  pkv::u32x4* vp = static_cast<pkv::u32x4*>(pool->v);
+  if (loc_type == PKV_I32)
+    hipLaunchKernelGGL((pkv::store_kv_kernel<int32_t, PK>), dim3((uint32_t)blocks), dim3(256), 0, s, kp, vp,
+                       pool_pk, pool->num_slots, static_cast<const int32_t*>(out_loc), n,
+                       static_cast<const pkv::u32x4*>(k), k_pk, static_cast<const pkv::u32x4*>(v), v_pk, packets,
+                       ds->faults);
+  else
+    hipLaunchKernelGGL((pkv::store_kv_kernel<int64_t, PK>), dim3((uint32_t)blocks), dim3(256), 0, s, kp, vp,
+                       pool_pk, pool->num_slots, static_cast<const int64_t*>(out_loc), n,
+                       static_cast<const pkv::u32x4*>(k), k_pk, static_cast<const pkv::u32x4*>(v), v_pk, packets,
+                       ds->faults);
+  return check_launch("store_kv");
+}
+
+size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv) {
+  if (bs < 1 || num_q_heads < 1) return 0;
+  return decode_ws_layout(bs, num_q_heads, max_total_kv).total;
+}
+
+int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_stride, void* o,
+                               int64_t o_stride, int32_t bs, int32_t num_q_heads,
+                               const int32_t* page_table, int32_t pt_rows, int64_t pt_stride,
+                               const int32_t* table_idx, const int32_t* cached_len,
+                               const int32_t* device_len, int64_t max_total_kv, float sm_scale,
+                               void* ws, size_t ws_bytes, void* stream) {
+  (void)cached_len;
+  int isz = 0;
+  int rc = check_pool(pool, &isz);
+  if (rc) return rc;
+  if (bs < 0 || bs > kDecodeMaxBatch) return fail(PKV_ERR_SHAPE, "bs %d outside [0, %d]", bs, kDecodeMaxBatch);
+  if (bs == 0) return ok();
+  if (num_q_heads < 1 || num_q_heads % pool->kv_heads)
+    return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of kv_heads %d", num_q_heads,
+                pool->kv_heads);
+  const int64_t qrow = (int64_t)num_q_heads * pkv::kHeadDim;
+  if (q_stride == 0) q_stride = qrow;
+  if (o_stride == 0) o_stride = qrow;
+  if ((rc = check_rows(q, q_stride, qrow, isz, "q"))) return rc;
+  if ((rc = check_rows(o, o_stride, qrow, isz, "o"))) return rc;
+  if (!page_table || !device_len) return fail(PKV_ERR_NULL, "page_table / device_len is NULL");
+  if (pt_rows < 1 || pt_stride < 1) return fail(PKV_ERR_SHAPE, "page table must have >= 1 row and column");
+  if (max_total_kv < 1 || max_total_kv > 0x7fffffffLL)
+    return fail(PKV_ERR_LENGTHS, "max_total_kv %lld outside [1, 2^31)", (long long)max_total_kv);
+  const DecodeWs lay = decode_ws_layout(bs, num_q_heads, max_total_kv);
+  if (!ws || ws_bytes < lay.total)
+    return fail(PKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", lay.total, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  DeviceState* ds;
+  if ((rc = device_state(&ds))) return rc;
+  if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)pkv::kHeadDim);
+  pkv::DecodeArgs a;
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.pool_row = pool->row_stride;
+  a.num_slots = pool->num_slots;
+  a.q = q;
+  a.q_stride = q_stride;
+  a.o = o;
+  a.o_stride = o_stride;
+  a.bs = bs;
+  a.num_items = decode_items(max_total_kv);
+  a.page_table = page_table;
+  a.pt_rows = pt_rows;
+  a.pt_stride = pt_stride;
+  a.table_idx = table_idx;
+  a.device_len = device_len;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  char* w = static_cast<char*>(ws);
+  a.cu_out = reinterpret_cast<int32_t*>(w + lay.cu);
+  a.part_ml = reinterpret_cast<float*>(w + lay.ml);
+  a.part_acc = reinterpret_cast<float*>(w + lay.acc);
+  a.faults = ds->faults;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int g = num_q_heads / pool->kv_heads;
+  if (pool->dtype == PKV_BF16) return dispatch_decode<pkv::bf16_t>(pool->kv_heads, g, a, s);
+  return dispatch_decode<float>(pool->kv_heads, g, a, s);
+}
+
+size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_q) {
+  (void)bs;
+  (void)num_q_heads;
+  (void)total_q;
+  return 0;
+}
+
+// ------------------------------------------------------------------ host-only helpers
+
+int64_t pkv_num_pages(int32_t head_dim, int32_t kv_heads, int32_t tp_size, int32_t page_size,
+                      int32_t itemsize, int32_t num_layers, int64_t free_before, int64_t model_bytes,
+                      double memory_ratio) {
+  if (head_dim < 1 || kv_heads < 1 || tp_size < 1 || page_size < 1 || itemsize < 1 || num_layers < 1)
+    return fail(PKV_ERR_SHAPE, "sizes must be positive");
+  int64_t heads;
+  if (kv_heads >= tp_size) {
+    if (kv_heads % tp_size) return fail(PKV_ERR_SHAPE, "kv_heads %d not divisible by tp %d", kv_heads, tp_size);
+    heads = kv_heads / tp_size;
+  } else {
+    if (tp_size % kv_heads) return fail(PKV_ERR_SHAPE, "tp %d not a multiple of kv_heads %d", tp_size, kv_heads);
+    heads = 1;
+  }
+  const int64_t per_page = 2LL * head_dim * heads * page_size * itemsize * num_layers;
+  const int64_t available = (int64_t)(memory_ratio * (double)free_before) - model_bytes;
+  const int64_t n = available >= 0 ? available / per_page : -1;
+  if (n <= 1) return fail(PKV_ERR_LENGTHS, "Not enough memory for KV cache (%lld pages)", (long long)n);
+  ok();
+  return n;
+}
+
+int pkv_prepare_sampling(int32_t n, const float* T, const int32_t* K, const float* P, int32_t vocab,
+                         float* T_out, int32_t* K_out, float* P_out, int32_t* flags) {
+  if (n < 0 || vocab < 1) return fail(PKV_ERR_SHAPE, "n must be >= 0 and vocab >= 1");
+  if (!flags || (n > 0 && (!T || !K || !P || !T_out || !K_out || !P_out)))
+    return fail(PKV_ERR_NULL, "a required array is NULL");
+  const float kMin = 1e-6f;
+  bool all_greedy = true, use_k = false, use_p = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const bool greedy = (T[i] <= 0.f || K[i] == 1) && P[i] == 1.f;
+    all_greedy = all_greedy && greedy;
+    T_out[i] = std::fmax(greedy ? 0.f : T[i], kMin);
+    K_out[i] = K[i] >= 1 ? K[i] : vocab;
+    P_out[i] = std::fmin(std::fmax(P[i], kMin), 1.f);
+    use_k = use_k || K_out[i] != vocab;
+    use_p = use_p || P_out[i] < 1.f;
+  }
+  *flags = (all_greedy ? PKV_PREP_ALL_GREEDY : 0) | (use_k ? PKV_PREP_USE_TOP_K : 0) |
+           (use_p ? PKV_PREP_USE_TOP_P : 0);
+  return ok();
+}
+
+}  // extern "C"
+
+// Entry points whose host code lives next to their kernels.
+#include "extend_host.inc"
+#include "sample_host.inc"

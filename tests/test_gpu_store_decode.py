@@ -1,0 +1,198 @@
+"""GPU parity: store_kv (bit-exact) and decode attention (fp32 max-abs 1e-5;
+bf16 max-abs 2e-2 and relative L2 1e-2) against the oracle, through the C ABI."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import config, draw_case, f32_to_bf16_bits
+from gpu_util import check_attention, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+pkv = pytest.importorskip("paged_kv_attention_scatter_amd")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv.read_faults()  # clear
+
+
+def _upload_case(case):
+    dt = case["cfg"].dtype
+    return dict(
+        k_pool=to_dev(case["k_pool"], dt), v_pool=to_dev(case["v_pool"], dt),
+        new_k=to_dev(case["new_k"], dt), new_v=to_dev(case["new_v"], dt),
+        out_loc=to_dev(case["out_loc"]), q=to_dev(case["q"], dt),
+        page_table=to_dev(case["page_table"]), cached_len=to_dev(case["cached_len"]),
+        device_len=to_dev(case["device_len"]))
+
+
+def _store_and_check(case, d, loc_dtype=torch.int32):
+    ps = case["cfg"].page_size
+    print(f"store_kv case {case['cfg'].name} rows={len(case['out_loc'])}", flush=True)
+    pkv.store_kv(d["k_pool"], d["v_pool"], d["out_loc"].to(loc_dtype), d["new_k"], d["new_v"], page_size=ps)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.store_kv(case["k_pool"], case["v_pool"], case["out_loc"], case["new_k"],
+                                   case["new_v"])
+    gk, gv = to_host(d["k_pool"]), to_host(d["v_pool"])
+    assert np.array_equal(gk.view(np.uint8), ref_k.view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), ref_v.view(np.uint8))
+    assert pkv.read_faults() == 0
+    return ref_k, ref_v
+
+
+@pytest.mark.parametrize("cid,loc_dtype", [(1, torch.int32), (1, torch.int64), (2, torch.int32),
+                                           (4, torch.int64)])
+def test_store_kv_bit_exact(cid, loc_dtype):
+    case = draw_case(config(cid))
+    _store_and_check(case, _upload_case(case), loc_dtype)
+
+
+def test_store_kv_strided_rows():
+    """k and v as column slices of one fused [n, (HQ + 2 HKV) * 128] buffer."""
+    rng = np.random.default_rng(3)
+    n, HKV, slots = 37, 8, 300
+    qkv = f32_to_bf16_bits(rng.standard_normal((n, (16 + 2 * HKV) * 128), dtype=np.float32))
+    qkv_d = to_dev(qkv, "bf16")
+    k = qkv_d[:, 16 * 128:24 * 128].view(n, HKV, 128)
+    v = qkv_d[:, 24 * 128:].view(n, HKV, 128)
+    pool_k = np.full((slots, HKV, 128), 0x7FC0, np.uint16)
+    pool_v = pool_k.copy()
+    loc = rng.permutation(slots)[:n].astype(np.int32)
+    dk, dv = to_dev(pool_k, "bf16"), to_dev(pool_v, "bf16")
+    pkv.store_kv(dk, dv, to_dev(loc), k, v)
+    torch.cuda.synchronize()
+    rk, rv = oracle.store_kv(pool_k, pool_v, loc, qkv[:, 16 * 128:24 * 128].reshape(n, HKV, 128),
+                             qkv[:, 24 * 128:].reshape(n, HKV, 128))
+    assert np.array_equal(to_host(dk), rk) and np.array_equal(to_host(dv), rv)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_decode_after_store_matches_oracle(cid):
+    case = draw_case(config(cid))
+    d = _upload_case(case)
+    ref_k, ref_v = _store_and_check(case, d)
+    dt = case["cfg"].dtype
+    print(f"decode case {case['cfg'].name} bs={len(case['device_len'])}", flush=True)
+    o = pkv.paged_attention_decode(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["cached_len"],
+                                   d["device_len"], max_total_kv=int(case["device_len"].sum()))
+    torch.cuda.synchronize()
+    ref = oracle.attention_decode(case["q"], ref_k, ref_v, case["page_table"], case["cached_len"],
+                                  case["device_len"], dt)
+    mx, rel = check_attention(to_host(o), ref, dt, case["cfg"].name)
+    print(f"  max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0
+
+
+def _random_decode(seed, bs, lens, HKV=8, G=2, dtype="bf16", slots_extra=64, q_pad=0, table_idx=False,
+                   ps=1):
+    """A decode batch with explicit lengths, random slots, pool fully random."""
+    rng = np.random.default_rng(seed)
+    HQ = HKV * G
+    S = np.asarray(lens, np.int32)
+    total = int(S.sum())
+    width = (int(S.max()) + 31) // 32 * 32
+    n_slots = total + slots_extra
+    perm = rng.permutation(n_slots)
+    table = np.full((bs + 3, width), n_slots - 1, np.int32)
+    rows = rng.permutation(bs + 3)[:bs].astype(np.int32) if table_idx else np.arange(bs, dtype=np.int32)
+    off = 0
+    for r in range(bs):
+        table[rows[r], :S[r]] = perm[off:off + S[r]]
+        off += S[r]
+    kv = rng.standard_normal((2, n_slots, HKV, 128), dtype=np.float32)
+    qf = rng.standard_normal((bs, HQ * 128 + q_pad), dtype=np.float32)
+    if dtype == "bf16":
+        kv, qf = f32_to_bf16_bits(kv), f32_to_bf16_bits(qf)
+    return dict(S=S, C=S - 1, table=table, rows=rows if table_idx else None, kv=kv, q=qf, HQ=HQ, HKV=HKV)
+
+
+def _run_decode(c, dtype, max_total_kv=None):
+    dk, dv = to_dev(c["kv"][0], dtype), to_dev(c["kv"][1], dtype)
+    qd = to_dev(c["q"], dtype)
+    bs = len(c["S"])
+    qv = qd[:, :c["HQ"] * 128].view(bs, c["HQ"], 128)
+    o = pkv.paged_attention_decode(
+        qv, dk, dv, to_dev(c["table"]), to_dev(c["C"]), to_dev(c["S"]),
+        table_idx=None if c["rows"] is None else to_dev(c["rows"]),
+        max_total_kv=int(c["S"].sum()) if max_total_kv is None else max_total_kv)
+    torch.cuda.synchronize()
+    qh = c["q"][:, :c["HQ"] * 128].reshape(bs, c["HQ"], 128)
+    ref = oracle.attention_decode(qh, c["kv"][0], c["kv"][1], c["table"], c["C"], c["S"], dtype,
+                                  table_idx=c["rows"])
+    return to_host(o), ref
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("one_long", dict(bs=1, lens=[20000])),
+    ("ragged_small", dict(bs=7, lens=[1, 2, 3, 64, 65, 127, 300])),
+    ("many_tiny", dict(bs=300, lens=list(range(1, 301)))),
+    ("tp2_shard_hkv4", dict(bs=5, lens=[100, 900, 33, 5000, 1], HKV=4, G=2)),
+    ("mha_g1", dict(bs=3, lens=[50, 700, 129], HKV=8, G=1)),
+    ("g4", dict(bs=3, lens=[50, 700, 129], HKV=4, G=4)),
+    ("q_strided_table_idx", dict(bs=6, lens=[10, 400, 2000, 3, 77, 1024], q_pad=8 * 256, table_idx=True)),
+    ("f32_hkv2", dict(bs=4, lens=[5, 9, 17, 333], HKV=2, G=2, dtype="f32")),
+    ("f32_g1", dict(bs=4, lens=[5, 900, 17, 33], HKV=8, G=1, dtype="f32")),
+])
+def test_decode_shapes(name, kw):
+    dtype = kw.get("dtype", "bf16")
+    c = _random_decode(zlib.crc32(name.encode()) % 1000, **kw)
+    print(f"decode shape case {name}", flush=True)
+    got, ref = _run_decode(c, dtype)
+    check_attention(got, ref, dtype, name)
+    assert pkv.read_faults() == 0
+
+
+def test_decode_loose_bound_same_result():
+    """A loose max_total_kv bound changes the work split, not the answer
+    (beyond float reassociation)."""
+    c = _random_decode(5, 9, [300, 1, 4000, 77, 2048, 9, 15, 1000, 600])
+    a, ref = _run_decode(c, "bf16")
+    b, _ = _run_decode(c, "bf16", max_total_kv=10_000_000)
+    check_attention(a, ref, "bf16", "tight")
+    check_attention(b, ref, "bf16", "loose")
+
+
+def test_decode_paged_equals_contiguous_bitwise():
+    """Identity page table over contiguous rows vs a random permutation of the
+    same rows: the kernel's arithmetic must not depend on where rows sit."""
+    rng = np.random.default_rng(9)
+    S = np.array([700, 5, 1500, 64], np.int32)
+    total, HKV, HQ = int(S.sum()), 8, 16
+    K = f32_to_bf16_bits(rng.standard_normal((total, HKV, 128), dtype=np.float32))
+    V = f32_to_bf16_bits(rng.standard_normal((total, HKV, 128), dtype=np.float32))
+    q = to_dev(f32_to_bf16_bits(rng.standard_normal((4, HQ, 128), dtype=np.float32)), "bf16")
+    width = 1536
+    ident = np.zeros((4, width), np.int32)
+    permt = np.zeros((4, width), np.int32)
+    perm = rng.permutation(total + 100)[:total]
+    Kp = np.zeros((total + 100, HKV, 128), np.uint16)
+    Vp = np.zeros_like(Kp)
+    Kp[perm], Vp[perm] = K, V
+    off = 0
+    for r, s in enumerate(S):
+        ident[r, :s] = np.arange(off, off + s)
+        permt[r, :s] = perm[off:off + s]
+        off += s
+    outs = []
+    for table, kk, vv in ((ident, K, V), (permt, Kp, Vp)):
+        outs.append(to_host(pkv.paged_attention_decode(
+            q, to_dev(kk, "bf16"), to_dev(vv, "bf16"), to_dev(table), to_dev(S - 1), to_dev(S),
+            max_total_kv=total)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_single_key_returns_v():
+    c = _random_decode(12, 3, [1, 1, 1])
+    got, ref = _run_decode(c, "bf16")
+    for r in range(3):
+        slot = c["table"][r, 0]
+        for h in range(16):
+            assert np.array_equal(got[r, h], c["kv"][1][slot, h // 2])
