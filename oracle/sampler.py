@@ -29,7 +29,16 @@ notes):
   (relative to the kept mass) of the decision: the top-p cut or the draw. The
   GPU computes those sums in another order and precision, so flagged rows are
   excluded from the bit-exact comparison and counted. Argmax and top-k are
-  pure order comparisons and are never flagged.
+  pure order comparisons and are never flagged. Two boundaries are exact on
+  any hardware and never flag: the start of the first kept token (no kept
+  mass precedes it) and the end of the last kept token (running past it
+  returns that same token).
+
+DELTA = 1e-5 leaves room for an implementation that computes each weight in
+fp32 as 2^((l - l_max) * log2(e) / T) (relative error below ~2e-6 for every
+weight above 1e-6 of the maximum) and sums in fp32 within small groups and
+fp64 above: it can only move a decision whose boundary lies within a few
+1e-6 of the target.
 """
 
 import numpy as np
@@ -76,7 +85,9 @@ def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
     if i >= V:
         i = int(ranked.max())
     lo = c[i - 1] if i > 0 else 0.0
-    draw_margin = min(target - lo, c[i] - target) / W
+    lo_margin = (target - lo) if lo > 0.0 else np.inf          # no kept mass before: exact
+    hi_margin = (c[i] - target) if i != int(ranked.max()) else np.inf   # last kept: exact
+    draw_margin = min(lo_margin, hi_margin) / W
     if draw_margin < delta:
         flagged = True
     if info is not None:

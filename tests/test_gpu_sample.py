@@ -1,0 +1,174 @@
+"""GPU parity of pkv_sample against the oracle: sampled token ids must be
+bit-exact on every row the oracle does not flag (argmax rows always), given
+the same uniforms. Flagged rows (a top-p cut or draw boundary within the oracle's margin
+of the decision) are counted and reported."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (config, draw_logits, draw_sampling_params, draw_uniforms, f32_to_bf16_bits)
+from gpu_util import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+pkv = pytest.importorskip("paged_kv_attention_scatter_amd")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(logits, dtype, T, K, P, u, what, max_flag_frac=0.05):
+    """logits: numpy in kernel dtype ([bs, V]); T/K/P: prepared arrays or None."""
+    print(f"sample case {what} shape={logits.shape} dtype={dtype}", flush=True)
+    d = lambda x: None if x is None else to_dev(x)
+    tok = pkv.sample(to_dev(logits, dtype), d(T), d(K), d(P), d(u))
+    torch.cuda.synchronize()
+    got = to_host(tok)
+    lf = oracle.widen(logits, dtype)
+    want, flagged = oracle.sample(lf, T, K, P, u)
+    bad = np.nonzero((got != want) & ~flagged)[0]
+    assert bad.size == 0, f"{what}: rows {bad[:10].tolist()} got {got[bad[:10]].tolist()} " \
+                          f"want {want[bad[:10]].tolist()}"
+    assert np.all((got >= 0) & (got < logits.shape[1]))
+    if max_flag_frac is not None:
+        assert flagged.mean() <= max_flag_frac, f"{what}: {flagged.sum()} flagged rows"
+    else:
+        assert (~flagged).sum() >= max(1, len(got) // 8), f"{what}: too few unflagged rows to check"
+    print(f"  {what}: {len(got)} rows exact, {int(flagged.sum())} flagged")
+    return got, want, flagged
+
+
+def _prepared(rows, vocab):
+    T, K, P = zip(*rows)
+    return pkv.prepare_sampling(T, K, P, vocab)
+
+
+@pytest.mark.parametrize("cid,literal", [(1, False), (1, True), (2, False), (3, False), (5, False)])
+def test_sample_configs(cid, literal):
+    cfg = config(cid)
+    logits = draw_logits(cfg)
+    T, K, P = _prepared(draw_sampling_params(cfg, literal), cfg.vocab)
+    u = draw_uniforms(cfg)
+    if cid == 2:
+        assert T is None                       # all greedy -> argmax path
+    _run(logits, cfg.dtype, T, K, P, u, f"{cfg.name}{'-literal' if literal else ''}")
+
+
+def _bf16(x):
+    return f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _rng(name):
+    return np.random.default_rng(zlib.crc32(name.encode()))
+
+
+def test_argmax_ties_lowest_index():
+    V = 151936
+    rng = _rng("ties")
+    x = rng.standard_normal((6, V)).astype(np.float32)
+    for r, pos in enumerate([[5, 100, 151935], [0, 1], [151934, 151935], [77], [3000, 9000], [1, 2, 3]]):
+        x[r, pos] = 9.0
+    x[5, :] = 0.0                              # one row all equal (+0) ...
+    x[5, 10:20] = -0.0                         # ... with some -0: still equal
+    got, _, _ = _run(_bf16(x), "bf16", None, None, None, np.zeros(6, np.float32), "argmax-ties")
+    assert got.tolist() == [5, 0, 151934, 77, 3000, 0]
+
+
+def test_topk_ties_at_threshold():
+    """Equal logits straddling the k-th rank: the lower indices are kept."""
+    V, bs = 4096, 64
+    rng = _rng("topk-ties")
+    x = np.round(rng.standard_normal((bs, V)) * 2, 0).astype(np.float32)   # few distinct values
+    T = np.full(bs, 1.0, np.float32)
+    K = rng.integers(1, 300, bs).astype(np.int32)
+    u = rng.random(bs, dtype=np.float32)
+    _run(_bf16(x), "bf16", T, K, None, u, "topk-ties")
+    _run(x, "f32", T, K, None, u, "topk-ties-f32")
+
+
+def test_topp_ties_at_cut():
+    V, bs = 2048, 64
+    rng = _rng("topp-ties")
+    x = np.round(rng.standard_normal((bs, V)) * 1.5, 0).astype(np.float32)
+    T = np.full(bs, 0.8, np.float32)
+    P = rng.uniform(0.05, 0.99, bs).astype(np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    _run(_bf16(x), "bf16", T, None, P, u, "topp-ties")
+    K = rng.integers(1, 50, bs).astype(np.int32)
+    _run(_bf16(x), "bf16", T, K, P, u, "topk-topp-ties")
+
+
+@pytest.mark.parametrize("name,V,T,k,p", [
+    ("plain", 151936, 1.0, -1, 1.0),          # no filter: full softmax sampling
+    ("flat-topp", 1024, 50.0, -1, 0.5),       # cut far below the 256-key window -> radix path
+    ("deep-p", 1024, 1.5, -1, 0.98),           # cut deep in the tail -> radix path
+    ("big-k", 1024, 0.7, 600, 1.0),          # top-k threshold below the window -> radix select
+    ("big-k-p", 1024, 2.0, 500, 0.97),
+    ("k1", 151936, 0.9, 1, 0.3),
+    ("tiny-T", 151936, 2e-6, 20, 0.9),
+    ("k50-p95", 151936, 1.0, 50, 0.95),
+])
+def test_sample_paths(name, V, T, k, p):
+    """Every path of the kernel. On the full vocabulary a flat distribution
+    gives each token less mass than the oracle's margin, so the paths that
+    only flat distributions reach are exercised on 1024 tokens."""
+    bs = 32
+    rng = _rng(name)
+    x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+    Ta = np.full(bs, T, np.float32)
+    Ka = None if k < 0 else np.full(bs, k, np.int32)
+    Pa = None if p >= 1.0 else np.full(bs, p, np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    u[0], u[1] = 0.0, np.float32(0.99999994)
+    _run(_bf16(x), "bf16", Ta, Ka, Pa, u, name, max_flag_frac=None)
+
+
+def test_sample_fp32_large_vocab_and_odd_sizes():
+    """fp32 rows too long for registers (re-read path); vocab not a multiple
+    of the 16-byte chunk; row stride larger than the vocabulary."""
+    rng = _rng("odd")
+    for V, pad, dtype in ((151936, 0, "f32"), (1000, 0, "bf16"), (50257, 7, "bf16"), (777, 5, "f32")):
+        bs = 12
+        full = (rng.standard_normal((bs, V + pad)) * 2.5).astype(np.float32)
+        if dtype == "bf16":
+            pad2 = (-(V + pad)) % 8
+            full = np.pad(full, ((0, 0), (0, pad2)))
+            x = _bf16(full)
+        else:
+            pad2 = (-(V + pad)) % 4
+            full = np.pad(full, ((0, 0), (0, pad2)))
+            x = full
+        T = rng.choice([1e-7, 0.5, 1.0, 1.7], bs).astype(np.float32)
+        K = rng.choice([0, 1, 5, 40, V + 3], bs).astype(np.int32)
+        P = rng.choice([1.0, 0.2, 0.9, 0.999], bs).astype(np.float32)
+        u = rng.random(bs, dtype=np.float32)
+        dev = to_dev(x, dtype)[:, :V]
+        tok = pkv.sample(dev, to_dev(T), to_dev(K), to_dev(P), to_dev(u))
+        torch.cuda.synchronize()
+        got = to_host(tok)
+        want, flagged = oracle.sample(oracle.widen(x, dtype)[:, :V], T, K, P, u)
+        bad = np.nonzero((got != want) & ~flagged)[0]
+        assert bad.size == 0, (V, dtype, bad.tolist(), got[bad].tolist(), want[bad].tolist())
+
+
+def test_mixed_batch_greedy_rows_exact():
+    """Half the rows greedy (T = 1e-6 after the argument builder), half
+    sampled: greedy rows are exact argmax whatever the uniforms."""
+    cfg = config(3)
+    logits = draw_logits(cfg)[:64]
+    rows = draw_sampling_params(cfg)[:64]
+    T, K, P = _prepared(rows, cfg.vocab)
+    greedy = T <= np.float32(1e-6)
+    assert greedy.any() and (~greedy).any()
+    for u_val in (0.0, 0.5, 0.9999):
+        u = np.full(64, u_val, np.float32)
+        got, _, _ = _run(logits, "bf16", T, K, P, u, f"mixed-u{u_val}")
+        lf = oracle.widen(logits, "bf16")
+        assert np.array_equal(got[greedy], np.argmax(lf[greedy], axis=1))
