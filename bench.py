@@ -1,0 +1,263 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3|2|5] [--skip-cpu]
+
+A step is one decode step of the whole path over one synthetic batch, on the
+current HIP stream: store_kv of the batch's new K/V rows, decode attention
+over the paged pool, then the sampler over the batch's logits. The default
+workload is the 256-request decode batch (device_len ~ U[1024, 8192], bf16,
+16 query / 8 KV heads, head_dim 128, page_size 1, pool sized for 28 layers
+from 0.9 x free HBM at 114688 bytes per page; logits [256, 151936], 128
+greedy rows and 128 at T=0.7, top_p=0.9). The causal extend kernel is timed
+on the 8-request prefill case (extend_len ~ U[512, 4096] over a 0-50% cached
+prefix) over the same pool.
+
+Inputs are resident in HBM before timing. The pool's contents are seeded
+N(0, 1) values written by torch on the device; lengths, page tables, q,
+logits, sampling parameters and uniforms come from the seeded generators in
+workloads/. Rotation defeats the 256 MB Infinity Cache: successive steps use
+different layers of the pool and four different logits buffers.
+
+Prints ONE JSON line (see the keys below).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+LAYERS_FILLED = 2               # layers of the pool written with data and rotated through
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3])
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--skip-extend", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import paged_kv_attention_scatter_amd as pkv
+    from workloads import (HEAD_DIM, HKV, HQ, LAYERS, config, draw_lengths, draw_logits, draw_page_table,
+                           draw_q, draw_sampling_params, draw_uniforms)
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = config(args.config)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + cfg.cid)
+
+    # ---------------------------------------------------------------- pool sized for 28 layers
+    free, total = torch.cuda.mem_get_info()
+    num_pages = pkv.num_pages(HEAD_DIM, HKV, 1, 2, LAYERS, free, 0, 0.9)
+    num_slots = num_pages + 1
+    log(f"free {free / 2**30:.1f} GiB -> {num_pages} pages x 28 layers "
+        f"({num_slots * HKV * HEAD_DIM * 2 * 2 * LAYERS / 2**30:.1f} GiB pool)")
+    pool = torch.empty((2, LAYERS, num_slots, HKV, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    for layer in range(LAYERS_FILLED):
+        pool[0, layer].normal_(generator=gen)
+        pool[1, layer].normal_(generator=gen)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- the decode batch
+    C, S = draw_lengths(cfg)
+    bs = len(S)
+    table = draw_page_table(cfg, S, num_pages)
+    q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
+    out_loc_h = table[np.arange(bs), S - 1].astype(np.int32)       # slot of each new token
+    d_table = torch.from_numpy(table).to(dev)
+    d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
+    d_loc = torch.from_numpy(out_loc_h).to(dev)
+    new_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+    new_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+    total_kv = int(S.sum())
+    ws = torch.empty(pkv.decode_workspace_size(bs, HQ, total_kv), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+
+    # ---------------------------------------------------------------- sampler inputs
+    logits0 = draw_logits(cfg)
+    logit_bufs = [torch.from_numpy(logits0.view(np.int16)).to(dev).view(torch.bfloat16)]
+    for _ in range(3):
+        logit_bufs.append((torch.randn((bs, cfg.vocab), generator=gen, device=dev) * cfg.logit_sigma)
+                          .to(torch.bfloat16))
+    rows = draw_sampling_params(cfg)
+    T, K, P = pkv.prepare_sampling(*zip(*rows), vocab=cfg.vocab)
+    d_T = None if T is None else torch.from_numpy(T).to(dev)
+    d_K = None if K is None else torch.from_numpy(K).to(dev)
+    d_P = None if P is None else torch.from_numpy(P).to(dev)
+    d_u = torch.from_numpy(draw_uniforms(cfg)).to(dev)
+    tokens = torch.empty(bs, dtype=torch.int32, device=dev)
+
+    def step(i):
+        layer = i % LAYERS_FILLED
+        kp, vp = pool[0, layer], pool[1, layer]
+        pkv.store_kv(kp, vp, d_loc, new_k, new_v)
+        pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
+        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens)
+
+    # ---------------------------------------------------------------- timed region
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    kv_bytes = total_kv * HKV * HEAD_DIM * 2 * 2           # K and V rows read, bf16
+    logit_bytes = bs * cfg.vocab * 2
+
+    # per-op durations with HIP events (same stream as the launches)
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    n = args.steps
+    ev = [[E() for _ in range(4)] for _ in range(n)]
+    for i in range(n):
+        layer = i % LAYERS_FILLED
+        kp, vp = pool[0, layer], pool[1, layer]
+        ev[i][0].record()
+        pkv.store_kv(kp, vp, d_loc, new_k, new_v)
+        ev[i][1].record()
+        pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
+        ev[i][2].record()
+        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(n)])
+    store_ms, decode_ms, sample_ms = (float(np.mean(ms[:, j])) for j in range(3))
+    decode_p = np.percentile(ms[:, 1], [10, 50, 90])
+    decode_gbs = kv_bytes / (decode_ms * 1e-3) / 1e9
+    sample_gbs = logit_bytes / (sample_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms | store {store_ms * 1e3:.1f} us | decode {decode_ms * 1e3:.1f} us "
+        f"({decode_gbs:.0f} GB/s) | sample {sample_ms * 1e3:.1f} us ({sample_gbs:.0f} GB/s)")
+
+    result = {
+        "metric": "decode-attn KV GB/s (% HBM peak) at bs=256; sampler tokens/s; extend TFLOP/s",
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: decode step (store_kv + decode attention + sampler), "
+                               f"bs={bs}, device_len~U[{int(S.min())}..{int(S.max())}], sum={total_kv}, "
+                               "16q/8kv heads, head_dim 128, page_size 1, 28-layer pool, "
+                               f"logits [{bs}, {cfg.vocab}] bf16",
+                   "bs": bs, "sum_device_len": total_kv, "num_pages": num_pages, "page_size": 1},
+        "roofline": {"bound": "hbm", "kernel": "decode attention (split-K + combine, one call)",
+                     "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": kv_bytes, "avg_launch_us": round(decode_ms * 1e3, 2),
+                     "p10_p50_p90_us": [round(x * 1e3, 2) for x in decode_p]},
+        "components": {
+            "store_kv_us": round(store_ms * 1e3, 2),
+            "decode_us": round(decode_ms * 1e3, 2),
+            "decode_kv_gbs": round(decode_gbs, 1),
+            "sample_us": round(sample_ms * 1e3, 2),
+            "sampler_tokens_per_s": round(bs / (sample_ms * 1e-3), 1),
+            "sampler_gbs": round(sample_gbs, 1),
+            "sampler_frac_hbm": round(sample_gbs / HBM_PEAK_GBS, 4),
+        },
+    }
+
+    if not args.skip_extend:
+        result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
+
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
+    print(json.dumps(result), flush=True)
+
+
+def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
+    """Causal extend over a cached prefix: 8 requests, E ~ U[512, 4096],
+    prefix 0-50%, page_size 1, over layer 0 of the same pool."""
+    from workloads import HEAD_DIM, HQ, config, draw_lengths, draw_page_table, draw_q
+    cfg = config(4)
+    C, S = draw_lengths(cfg)
+    E = S - C
+    table = draw_page_table(cfg, S, num_pages)
+    q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
+    d_table = torch.from_numpy(table).to(dev)
+    d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
+    kp, vp = pool[0, 0], pool[1, 0]
+    o = torch.empty_like(q)
+    flops = 4.0 * HEAD_DIM * HQ * float(np.sum(E.astype(np.float64) * C + E * (E + 1) / 2.0))
+    try:
+        for _ in range(3):
+            pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
+    except pkv.PkvError as e:
+        log(f"extend skipped: {e}")
+        return {"extend": f"unavailable: {e}"}
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"extend {us:.1f} us, {flops / 1e12:.3f} TFLOP -> {tflops:.1f} TFLOP/s")
+    return {"extend_us": round(us, 2), "extend_tflop": round(flops / 1e12, 4),
+            "extend_tflops": round(tflops, 1), "extend_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "extend_workload": f"8 requests, extend_len {int(E.min())}..{int(E.max())}, "
+                               f"prefix {int(C.min())}..{int(C.max())}, bf16, page_size 1"}
+
+
+def cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg):
+    """The oracle, as it stands, on the GPU machine's host cores: decode attention
+    for as many requests as fit in ~10 s of CPU time (their K/V rows copied
+    from layer 0 of the pool), reported as KV GB/s like the GPU figure."""
+    import oracle
+    k0 = pool[0, 0]
+    v0 = pool[1, 0]
+    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    done, kv_bytes, elapsed = 0, 0, 0.0
+    budget = 10.0
+    while done < len(S) and elapsed < budget:
+        r = done
+        s = int(S[r])
+        slots = torch.from_numpy(table[r, :s].astype(np.int64)).to(k0.device)
+        K = k0.index_select(0, slots).view(torch.int16).cpu().numpy().view(np.uint16)
+        V = v0.index_select(0, slots).view(torch.int16).cpu().numpy().view(np.uint16)
+        tab = np.arange(s, dtype=np.int64)[None, :]
+        t0 = time.perf_counter()
+        oracle.attention_decode(qh[r:r + 1], K, V, tab, C[r:r + 1], S[r:r + 1], "bf16")
+        elapsed += time.perf_counter() - t0
+        kv_bytes += s * 8 * 128 * 2 * 2
+        done += 1
+    return {"value": round(kv_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"decode attention of the first {done} of {len(S)} requests (fp64 NumPy, one thread, "
+                      f"{elapsed:.1f} s)", "host_cpus_available": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

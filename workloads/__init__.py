@@ -23,11 +23,12 @@ Recipe (identical for every case):
 """
 
 from .configs import (HQ, HKV, HEAD_DIM, VOCAB, LAYERS, CaseConfig, CONFIGS, config,
-                      f32_to_bf16_bits, draw_lengths, draw_page_table, draw_case,
-                      draw_logits, draw_sampling_params, draw_uniforms)
+                      f32_to_bf16_bits, draw_lengths, draw_page_table, draw_case, draw_q,
+                      draw_request_kv, draw_logits, draw_sampling_params, draw_uniforms,
+                      default_num_pages, table_width)
 
 __all__ = [
     "HQ", "HKV", "HEAD_DIM", "VOCAB", "LAYERS", "CaseConfig", "CONFIGS", "config",
-    "f32_to_bf16_bits", "draw_lengths", "draw_page_table", "draw_case", "draw_logits",
-    "draw_sampling_params", "draw_uniforms",
+    "f32_to_bf16_bits", "draw_lengths", "draw_page_table", "draw_case", "draw_q", "draw_request_kv",
+    "draw_logits", "draw_sampling_params", "draw_uniforms", "default_num_pages", "table_width",
 ]
