@@ -1,3 +1,313 @@
-// Paged causal extend attention (MFMA). Filled in below.
+// Paged causal extend (prefill over a cached prefix) on bf16 MFMA tiles.
+//
+// Definition ("第 0 步：一个能跑的最小推理引擎", the dense attention function;
+// "Mini-SGLang 完整剖析" section 4.6.5 for the ragged query layout): request r
+// has C = cached_len and S = device_len tokens; its E = S - C query rows are
+// the new tokens at absolute positions C .. S-1, stored contiguously from row
+// sum_{r' < r} E_r' of q. Query t sees keys j <= C + t, all read from the pool
+// through the token-granular page table. GQA: query head h uses KV head
+// h / (HQ / HKV). Scale sm_scale, fp32 online softmax.
+//
+// Work: one workgroup (4 waves) per (request, KV head, pair of query heads
+// sharing it, block of 64 query positions); wave w owns positions
+// [16w, 16w + 16) of the block for both query heads. Key blocks of 64 are
+// gathered row by row (256 B per head per token) into LDS, so every K/V
+// element fetched from HBM serves 64 positions x 2 heads.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16): the kernel computes S^T = K . Q^T,
+// so each lane's four accumulators belong to ONE query (lane % 16) and four
+// keys -- the softmax row statistics stay lane-local up to a 4-lane
+// reduction -- and O^T = V^T . P^T, whose accumulators again belong to the
+// lane's query, so rescaling is lane-local too. P^T is fed straight from the
+// S^T accumulators as the B operand; that fixes the order in which keys enter
+// the contraction, and V is stored in LDS transposed with the same key order,
+// so every MFMA operand is one 16-byte LDS read.
 #pragma once
+
 #include "common.hpp"
+
+namespace pkv {
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+struct ExtendArgs {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t pool_row;      // elements between slots
+  int64_t num_slots;
+  const void* q;
+  int64_t q_stride;      // elements between query rows
+  void* o;
+  int64_t o_stride;
+  int32_t bs;
+  int32_t kv_heads;
+  int32_t group;         // query heads per KV head
+  int32_t head_pairs;    // workgroups per KV head along the query heads
+  const int32_t* page_table;
+  int32_t pt_rows;
+  int64_t pt_stride;
+  const int32_t* table_idx;
+  const int32_t* cached_len;
+  const int32_t* device_len;
+  int64_t total_q;
+  int32_t max_extend;
+  float scale_log2;      // sm_scale * log2(e)
+  uint32_t* faults;
+};
+
+constexpr int kExtBlockQ = 64;   // query positions per workgroup
+constexpr int kExtBlockK = 64;   // keys per LDS tile
+constexpr int kKPad = 136;       // K tile row: 128 dims + 8 pad (272 B)
+constexpr int kVPad = 72;        // V^T tile row: 64 keys + 8 pad (144 B)
+
+// Position of key k (0..63) inside a V^T row: within each 32-key chunk the
+// order is (key % 16) / 4, then (key % 32) / 16, then key % 4 -- the order in
+// which the MFMA B operand built from S^T accumulators presents keys.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k & 31) >> 4) + (k & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // [a.lo, b.lo]
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // [a.hi, b.hi]
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+template <int NH>
+__global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kExtBlockK][kKPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim][kVPad];
+  __shared__ int32_t sh_qstart;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 15, lg = lane >> 4;   // MFMA row-in-tile and k-group of this lane
+
+  const int nqb = gridDim.y;
+  const int qb = nqb - 1 - (int)blockIdx.y;   // longest blocks first
+  const int x = blockIdx.x;
+  const int hp = x % a.head_pairs;
+  const int g = (x / a.head_pairs) % a.kv_heads;
+  const int r = x / (a.head_pairs * a.kv_heads);
+
+  const int32_t C = a.cached_len[r], S = a.device_len[r];
+  const int32_t row = a.table_idx ? a.table_idx[r] : r;
+  const bool len_ok = C >= 0 && C < S && (int64_t)S <= a.pt_stride && S - C <= a.max_extend;
+  const bool row_ok = row >= 0 && row < a.pt_rows;
+  if (!len_ok || !row_ok) {
+    if (tid == 0 && qb == 0 && g == 0 && hp == 0) raise_fault(a.faults, !row_ok ? 0x8u : 0x2u);
+    return;
+  }
+  const int32_t E = S - C;
+  if (qb * kExtBlockQ >= E) return;
+
+  // Query row offset of this request: sum of the earlier requests' extend lengths.
+  {
+    int64_t part = 0;
+    for (int i = tid; i < r; i += 256) {
+      const int32_t ci = a.cached_len[i], si = a.device_len[i];
+      part += (si > ci) ? (si - ci) : 0;
+    }
+    __shared__ int64_t red[4];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    if (tid == 0) {
+      const int64_t qs = red[0] + red[1] + red[2] + red[3];
+      sh_qstart = (qs + E <= a.total_q) ? (int32_t)qs : -1;
+    }
+    __syncthreads();
+  }
+  const int32_t qstart = sh_qstart;
+  if (qstart < 0) {
+    if (tid == 0 && qb == 0 && g == 0 && hp == 0) raise_fault(a.faults, 0x10u);
+    return;
+  }
+
+  const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q);
+  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(a.k_pool);
+  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(a.v_pool);
+  const int32_t* pt = a.page_table + (int64_t)row * a.pt_stride;
+
+  // This lane's query (MFMA column) and its validity.
+  const int t = qb * kExtBlockQ + wave * 16 + lq;
+  const bool t_ok = t < E;
+  const int t_eff = t_ok ? t : E - 1;          // invalid rows mask like the last valid one
+  const int h0 = g * a.group + hp * NH;
+
+  // Q^T as B operands: 4 k-steps of 32 dims, 8 dims per lane.
+  bf16x8_v qreg[NH][4];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    const bf16_t* qrow = qg + (int64_t)(qstart + t_eff) * a.q_stride + (int64_t)(h0 + hh) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (t_ok) w = *reinterpret_cast<const u32x4*>(qrow + ks * 32 + lg * 8);
+      qreg[hh][ks] = __builtin_bit_cast(bf16x8_v, w);
+    }
+  }
+
+  f32x4_v oacc[NH][8];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+  float m[NH], l[NH];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+  }
+
+  // Keys this workgroup needs: j <= C + (last valid position of the block).
+  const int t_last = min(E, (qb + 1) * kExtBlockQ) - 1;
+  const int n_keys = C + t_last + 1;
+  const int nkb = (n_keys + kExtBlockK - 1) / kExtBlockK;
+
+  // Tile loader: thread -> 4 consecutive keys (kq*4 ..) x 8 dims (dg*8 ..).
+  const int kq = tid >> 4, dg = tid & 15;
+  u32x4 kreg[4], vreg[4];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = kb * kExtBlockK + kq * 4 + e;
+      int32_t slot = -1;
+      if (j < n_keys) {
+        slot = pt[j];
+        if (slot < 0 || (int64_t)slot >= a.num_slots) {
+          raise_fault(a.faults, 0x4u);
+          slot = -1;
+        }
+      }
+      if (slot >= 0) {
+        const int64_t off = (int64_t)slot * a.pool_row + (int64_t)g * kHeadDim + dg * 8;
+        kreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
+        vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
+      } else {
+        kreg[e] = (u32x4){0u, 0u, 0u, 0u};
+        vreg[e] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(&Ks[kq * 4 + e][dg * 8]) = kreg[e];
+    const int p0 = vt_pos(kq * 4);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // dims dg*8 + 2w (lo halves) and + 2w + 1 (hi halves)
+      uint2 lo, hi;
+      lo.x = pack_lo(vreg[0][w], vreg[1][w]);
+      lo.y = pack_lo(vreg[2][w], vreg[3][w]);
+      hi.x = pack_hi(vreg[0][w], vreg[1][w]);
+      hi.y = pack_hi(vreg[2][w], vreg[3][w]);
+      *reinterpret_cast<uint2*>(&Vt[dg * 8 + 2 * w][p0]) = lo;
+      *reinterpret_cast<uint2*>(&Vt[dg * 8 + 2 * w + 1][p0]) = hi;
+    }
+  };
+
+  const float sc = a.scale_log2;
+  const int t_min_wave = qb * kExtBlockQ + wave * 16;
+  load_tile(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (kb + 1 < nkb) load_tile(kb + 1);  // in flight while this tile is computed
+
+    // S^T = K . Q^T for 4 key tiles of 16.
+    f32x4_v s[NH][4];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[hh][kt] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_v ka =
+            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Ks[kt * 16 + lq][ks * 32 + lg * 8]));
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
+      }
+
+    // Online softmax for this lane's query; key of s[kt][i] is kb*64 + kt*16 + 4*lg + i.
+    const bool need_mask = kb * kExtBlockK + kExtBlockK - 1 > C + t_min_wave;
+    const int lim = C + t_eff;
+    bf16x8_v pb[NH][2];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      float v[16];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[hh][kt][i] * sc;
+          if (need_mask && kb * kExtBlockK + kt * 16 + 4 * lg + i > lim) x = -INFINITY;
+          v[kt * 4 + i] = x;
+        }
+      float mb = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mb = fmaxf(mb, v[i]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float mn = fmaxf(m[hh], mb);
+      const float corr = fast_exp2(m[hh] - mn);  // m = -inf on the first tile: corr = 0
+      m[hh] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[i] = fast_exp2(v[i] - mn);
+        ls += v[i];
+      }
+      l[hh] = l[hh] * corr + ls;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8_v b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (__bf16)v[(2 * k2 + (j >> 2)) * 4 + (j & 3)];
+        pb[hh][k2] = b;
+      }
+    }
+
+    // O^T += V^T . P^T: 8 tiles of 16 dims, 2 k-steps of 32 keys.
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8_v va =
+            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Vt[dt * 16 + lq][k2 * 32 + lg * 8]));
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
+      }
+  }
+
+  // Normalise and write: lane holds dims dt*16 + 4*lg + i of query t.
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float lt = l[hh];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (t_ok) {
+      bf16_t* orow = reinterpret_cast<bf16_t*>(a.o) + (int64_t)(qstart + t) * a.o_stride +
+                     (int64_t)(h0 + hh) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[hh][dt][0] * inv, oacc[hh][dt][1] * inv);
+        w.y = pack_bf16x2(oacc[hh][dt][2] * inv, oacc[hh][dt][3] * inv);
+        *reinterpret_cast<uint2*>(orow + dt * 16 + lg * 4) = w;
+      }
+    }
+  }
+}
+
+}  // namespace pkv

@@ -307,13 +307,6 @@ int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_st
   return dispatch_decode<float>(pool->kv_heads, g, a, s);
 }
 
-size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_q) {
-  (void)bs;
-  (void)num_q_heads;
-  (void)total_q;
-  return 0;
-}
-
 // ------------------------------------------------------------------ host-only helpers
 
 int64_t pkv_num_pages(int32_t head_dim, int32_t kv_heads, int32_t tp_size, int32_t page_size,
