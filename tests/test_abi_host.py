@@ -145,3 +145,42 @@ def test_decode_workspace_size_grows_with_batch(L):
     a = L.pkv_decode_workspace_size(4, 16, 1000)
     b = L.pkv_decode_workspace_size(256, 16, 1_200_000)
     assert 0 < a < b and L.pkv_decode_workspace_size(0, 16, 10) == 0
+
+
+def _sample(L, logits=0x100000, dt=1, bs=4, V=1024, stride=1024, T=0x200000, K=None, P=None, u=0x300000,
+            out=0x400000):
+    return L.pkv_sample(logits, dt, bs, V, stride, T, K, P, u, out, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), -1), (dict(dt=7), -2), (dict(V=0), -3), (dict(bs=-1), -3), (dict(stride=1000), -3),
+    (dict(stride=1028), -5), (dict(logits=0x100004), -5), (dict(out=None), -1), (dict(u=None), -1),
+    (dict(V=2097153, stride=2097160), -3), (dict(dt=0, V=1048577, stride=1048580), -3),
+])
+def test_sample_argument_errors(L, kw, status):
+    assert _sample(L, **kw) == status
+    assert L.pkv_last_error().decode()
+
+
+def test_sample_zero_rows_is_noop(L):
+    assert _sample(L, bs=0) == 0
+
+
+def _extend(L, pool, bs=2, hq=16, q=0x60000, o=0x70000, pt=0x80000, cl=0x88000, dl=0x90000, total_q=10,
+            max_e=8, rows=2, pts=64):
+    return L.pkv_paged_attention_extend(ctypes.byref(pool), q, 0, o, 0, bs, hq, pt, rows, pts, None, cl, dl,
+                                        total_q, max_e, 0.0, None, 0, None)
+
+
+@pytest.mark.parametrize("pool,kw,status", [
+    (dict(dtype=0), {}, -2), (dict(), dict(hq=12), -3), (dict(), dict(q=None), -1), (dict(), dict(o=0x70002), -5),
+    (dict(), dict(cl=None), -1), (dict(), dict(max_e=0), -4), (dict(), dict(rows=0), -3),
+    (dict(), dict(max_e=64 * 65536), -3),
+])
+def test_extend_argument_errors(L, pool, kw, status):
+    assert _extend(L, _pool(**pool), **kw) == status
+    assert L.pkv_last_error().decode()
+
+
+def test_extend_empty_batch_is_noop(L):
+    assert _extend(L, _pool(), bs=0) == 0 and _extend(L, _pool(), total_q=0) == 0

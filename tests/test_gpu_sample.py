@@ -114,6 +114,9 @@ def test_topp_ties_at_cut():
     ("k1", 151936, 0.9, 1, 0.3),
     ("tiny-T", 151936, 2e-6, 20, 0.9),
     ("k50-p95", 151936, 1.0, 50, 0.95),
+    ("k9000", 151936, 1.0, 9000, 1.0),        # more candidates than the LDS list holds -> generic path
+    ("k3000-p999", 151936, 1.0, 3000, 0.999),
+    ("p-only", 151936, 0.7, -1, 0.9),          # top-p over the whole row's mass
 ])
 def test_sample_paths(name, V, T, k, p):
     """Every path of the kernel. On the full vocabulary a flat distribution
