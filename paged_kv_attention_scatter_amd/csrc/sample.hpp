@@ -7,32 +7,40 @@
 // the rest. Greedy rows (T <= 1e-6, or no temperature array) are argmax.
 //
 // The pages' GPU path calls FlashInfer's rejection-sampling kernels; this is
-// a different, exact design with one workgroup per row:
+// a different, exact design with one workgroup per row. Ranking uses
+// order-preserving integer keys of the logits (-0 ranks with +0), so argmax
+// and top-k are exact and ties go to the lower index; weights are
+// w(l) = exp2((l - l_max) * log2(e) / T), so equal logits weigh the same.
 //
-// * The row is read from HBM once into registers: wave w owns a contiguous
-//   range of 16-byte chunks and lane l holds chunk w * CPW + c * 64 + l in
-//   round c, so every load is coalesced and index order is (wave, round,
-//   lane, element). As chunks arrive each thread folds them into its maximum,
-//   the first index of it and, for rows whose top-p runs over the whole row,
-//   the mass relative to a running maximum.
-// * Ranking uses order-preserving integer keys of the logits (-0 ranks with
-//   +0), so argmax and top-k are exact; ties go to the lower index. Weights
-//   are w(l) = exp2((l - l_max) * log2(e) / T), so equal logits weigh the same.
-// * Fast path: per-wave count histograms of d = key_max - key over the 256
-//   largest key values. All elements of a bin share one key and one weight,
-//   so the top-k threshold, the kept mass and the top-p cut come from scans
-//   over 256 bins. Every element at or above the final cut is then copied,
-//   in index order, into an LDS list; the ties at the cut (the first n
-//   equal-key tokens in index order are kept) and the draw (kept weights in
-//   index order, first running mass > u * W) are resolved on that list.
-// * Rows with neither top-k nor top-p draw over the whole row: per
-//   (wave, round) group masses locate the group, one chunk round is scanned.
-// * A cut below the window, or more candidates than the LDS list holds,
-//   falls back to a generic path over the row in memory: a radix descent
-//   over the full key (8 bits per pass, count and fp64 mass histograms) and
-//   group-mass scans for ties and the draw.
-// Mass sums are fp32 inside a 16-byte chunk and fp64 above (the in-wave tree
-// of a group mass is fp32).
+// bf16 rows (the register kernel):
+// * The row is read from HBM once into registers as 32-bit words (two
+//   tokens). Wave w owns words [w * WPW, (w + 1) * WPW); in round c, slot j
+//   lane l holds word w * WPW + (4c + j) * 64 + l, so every load is a
+//   coalesced 256-byte read and index order is (wave, round, slot, lane,
+//   half). Words past the row read a constant -inf pair instead, so no pass
+//   needs a bounds mask.
+// * As words arrive they are turned in place into pairs of biased 16-bit
+//   keys with packed 16-bit integer ops, and folded into a running maximum;
+//   rows whose top-p runs over the whole row also fold in their mass,
+//   relative to a per-thread reference raised with the running maximum.
+// * A second pass copies every token within 128 key values of the maximum
+//   into a per-wave LDS list, in index order (one saturating packed
+//   subtract, one ballot and one lane count per word slot). The top-k
+//   threshold and the top-p cut come from a count histogram of the list: all
+//   tokens of a bin share one key and one weight. The ties at the cut (the
+//   first n equal-key tokens in index order are kept) and the draw (kept
+//   weights in index order, first running mass > u * W) run on the list.
+// * Rows with neither top-k nor top-p, cuts below the 128-key window and
+//   lists that overflow take the paths below over the row in memory.
+//
+// fp32 rows, and bf16 rows too long for registers (the memory kernel): every
+// pass reads 16-byte chunks from memory (wave w owns a contiguous chunk range,
+// lane l reads chunk w * CPW + 64c + l in round c). Cuts by radix descent over
+// the full key (8 bits per pass, count and fp64 mass histograms); ties and the
+// draw by per-(wave, round) group masses that locate one chunk round.
+//
+// Mass sums are fp32 over at most 8 tokens (a 16-byte chunk, or one round of
+// a thread) or one wave's group, and fp64 above.
 #pragma once
 
 #include "common.hpp"
@@ -73,10 +81,6 @@ struct SampleElem<bf16_t> {
     const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
     return __uint_as_float(b << 16);
   }
-  static PKV_INLINE void set_raw(u32x4& x, int e, const void* p, int64_t i) {
-    const uint32_t r = static_cast<const uint16_t*>(p)[i];
-    x[e >> 1] |= (e & 1) ? (r << 16) : r;
-  }
 };
 
 template <>
@@ -93,16 +97,15 @@ struct SampleElem<float> {
     const uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
     return __uint_as_float(b);
   }
-  static PKV_INLINE void set_raw(u32x4& x, int e, const void* p, int64_t i) {
-    x[e] = static_cast<const uint32_t*>(p)[i];
-  }
 };
 
 constexpr int kSampleThreads = 512;
 constexpr int kSampleWaves = kSampleThreads / kWave;
-constexpr int kSampleWindow = 256;      // key values below the row maximum held in the fast histogram
-constexpr int kSampleMaxRounds = 512;   // chunk rounds per wave with a group-mass slot (bounds the vocabulary)
-constexpr int kSampleCap = 8192;        // candidates the LDS list holds
+constexpr int kSampleWindow = 128;      // register kernel: key values at or below the maximum in the list
+constexpr int kSampleSegment = 1024;    // register kernel: list entries per wave
+constexpr int kSampleCap = kSampleSegment * kSampleWaves;
+constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave with a group-mass slot
+constexpr int kSampleWordsPerRound = 4 * kWave;  // register kernel: words a wave reads per round
 
 // ---------------------------------------------------------------- wave helpers
 
@@ -158,19 +161,50 @@ PKV_INLINE float wave_total_f32(float v) {
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
+// Set bits of m below this lane.
+PKV_INLINE int32_t lanes_below(uint64_t m) {
+  return (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
-// Shared state of one row's workgroup.
+// ---------------------------------------------------------------- packed bf16 keys
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+PKV_INLINE u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
+PKV_INLINE uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Two bf16 values -> two biased 16-bit keys, order-preserving: a positive
+// value b maps to 0x8000 + b, a negative one to 0x8000 - |b|, so -0 and +0
+// share 0x8000 and -inf is 0x0080. Four packed/bitwise ops per pair.
+PKV_INLINE uint32_t bf16x2_keys(uint32_t w) {
+  const i16x2 sgn = __builtin_bit_cast(i16x2, w) >> (int16_t)15;  // 0xffff in negative halves
+  const uint32_t sg = __builtin_bit_cast(uint32_t, sgn);
+  const uint32_t x = w ^ (sg | 0x80008000u);     // positive: b | 0x8000; negative: 0x7fff - |b|
+  return as_u32(as_u16x2(x) - as_u16x2(sg));      // negative halves + 1
+}
+// The bf16 value of a biased key.
+PKV_INLINE float key16_value(uint32_t k) {
+  const uint32_t b = k >= 0x8000u ? (k - 0x8000u) : (0x8000u | (0x8000u - k));
+  return __uint_as_float(b << 16);
+}
+
+// ---------------------------------------------------------------- shared state
+
 struct SampleLds {
-  uint32_t hw[kSampleWaves][kSampleWindow];     // per-wave window counts
-  uint32_t hist[kSampleWindow];                 // window counts
-  float wtab[kSampleWindow];                    // weight of the key at distance d below the maximum
-  float gsum[kSampleWaves * kSampleMaxRounds];  // group masses, group = (wave, round)
-  int32_t cidx[kSampleCap];                     // candidate list: index ...
-  uint8_t cd[kSampleCap];                       // ... and its distance d
-  uint32_t rcnt[256];                           // radix descent: digit counts
-  double rmass[256];                            //                digit masses
+  union {
+    struct {
+      uint32_t g[kSampleCap];    // register kernel list: slot code of the word within its wave ...
+      uint32_t sv[kSampleCap];   // ... and its two saturated key offsets (0 = not in the window)
+    } list;
+    float gsum[kSampleWaves * kSampleMaxRounds];  // memory passes: group masses, group = (wave, round)
+  } big;
+  uint32_t hist[256];    // window counts
+  float wtab[256];       // weight of the key d below the maximum
+  uint32_t rcnt[256];    // radix descent: digit counts
+  double rmass[256];     //                digit masses
+  int32_t seg_n[kSampleWaves];
   double wave_f[kSampleWaves];
-  float wave_v[kSampleWaves];
   int32_t wave_i[kSampleWaves];
   int32_t wave_j[kSampleWaves];
   double scan_f[kSampleWaves];
@@ -180,7 +214,7 @@ struct SampleLds {
   int32_t result;
 };
 
-// Block-wide sum, returned in every thread; starts and ends with a barrier.
+// Block-wide reductions, returned in every thread; they start and end with a barrier.
 PKV_INLINE double block_sum_f64(SampleLds& s, double v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum_f64(v);
@@ -189,6 +223,17 @@ PKV_INLINE double block_sum_f64(SampleLds& s, double v) {
   __syncthreads();
   double t = 0.0;
   for (int w = 0; w < kSampleWaves; ++w) t += s.wave_f[w];
+  __syncthreads();
+  return t;
+}
+PKV_INLINE int32_t block_reduce_i32(SampleLds& s, int32_t v, bool want_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = want_max ? wave_max_i32(v) : wave_min_i32(v);
+  __syncthreads();
+  if (lane == 0) s.wave_j[wave] = v;
+  __syncthreads();
+  int32_t t = s.wave_j[0];
+  for (int w = 1; w < kSampleWaves; ++w) t = want_max ? max(t, s.wave_j[w]) : min(t, s.wave_j[w]);
   __syncthreads();
   return t;
 }
@@ -208,8 +253,8 @@ PKV_INLINE int32_t block_excl_scan_i32(SampleLds& s, int32_t v, int32_t* total) 
   *total = tot;
   return off + incl - v;
 }
-// Block scan in thread order: returns the exclusive prefix, *incl_out the
-// inclusive one (equal to the next thread's exclusive prefix, bit for bit).
+// Returns the exclusive prefix; *incl_out = the inclusive one (equal to the
+// next thread's exclusive prefix, bit for bit).
 PKV_INLINE double block_scan_f64(SampleLds& s, double v, double* incl_out, double* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double excl;
@@ -261,28 +306,15 @@ PKV_INLINE void window_select(SampleLds& s, AF amount, CF count, double goal, in
   __syncthreads();
 }
 
-// The row as 16-byte chunks. REG: MAXR rounds are loaded once into registers;
-// otherwise every pass reads the chunks from memory.
-template <typename T, int MAXR, bool REG>
+// ---------------------------------------------------------------- the row in memory
+
+template <typename T>
 struct SampleRow {
   using E = SampleElem<T>;
   static constexpr int EPC = E::kPerChunk;
   const T* base;
   int V, nchunks, cpw, rounds, wave, lane;
-  u32x4 reg[REG ? MAXR : 1];
 
-  PKV_INLINE int chunk_id(int c) const { return wave * cpw + c * kWave + lane; }
-  PKV_INLINE bool chunk_ok(int c) const { return c * kWave + lane < cpw && chunk_id(c) < nchunks; }
-  PKV_INLINE u32x4 fetch(int c) const {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (!chunk_ok(c)) return x;
-    const int64_t ch = chunk_id(c);
-    if ((ch + 1) * EPC <= V) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + ch);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e)  // the last, partial chunk of a row
-      if (ch * EPC + e < V) E::set_raw(x, e, base, ch * EPC + e);
-    return x;
-  }
   PKV_INLINE void init(const T* b, int vocab, int w, int l) {
     base = b;
     V = vocab;
@@ -291,26 +323,22 @@ struct SampleRow {
     rounds = (cpw + kWave - 1) / kWave;
     wave = w;
     lane = l;
-    if constexpr (REG) {
-#pragma unroll
-      for (int c = 0; c < MAXR; ++c)
-        if (c < rounds) reg[c] = fetch(c);
-    }
   }
-  // f(c, x, ok) for every round c < rounds, in order; the loop is wave-uniform.
+  PKV_INLINE int chunk_id(int c) const { return wave * cpw + c * kWave + lane; }
+  PKV_INLINE bool chunk_ok(int c) const { return c * kWave + lane < cpw && chunk_id(c) < nchunks; }
+  // The 16-byte block of chunk c, read whole: a row's last block may extend
+  // past the vocabulary, but it is 16-byte aligned and starts inside the
+  // row, so it never crosses a page; elements at or past V are never used.
+  PKV_INLINE u32x4 fetch(int c) const {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (chunk_ok(c)) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + chunk_id(c));
+    return x;
+  }
+  // f(c, x, ok) for every round c < rounds, in order (wave-uniform loop).
   template <class F>
   PKV_INLINE void for_rounds(F f) const {
-    if constexpr (REG) {
-#pragma unroll
-      for (int c = 0; c < MAXR; ++c)
-        if (c < rounds) f(c, reg[c], chunk_ok(c));
-    } else {
-      for (int c = 0; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
-    }
+    for (int c = 0; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
   }
-  // The chunk of round c, read again from memory: selecting one register
-  // chunk by a run-time round would put the whole array in scratch.
-  PKV_INLINE u32x4 chunk(int c) const { return fetch(c); }
   // f(i, l) for every element (index, logit) of chunk x of round c.
   template <class F>
   PKV_INLINE void elements(int c, const u32x4& x, bool ok, F f) const {
@@ -358,7 +386,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
       cs += w;
     });
     const float g = wave_total_f32(cs);
-    if (lane == 0) s.gsum[wave * R + c] = g;
+    if (lane == 0) s.big.gsum[wave * R + c] = g;
   });
   const int32_t wlast = wave_max_i32(tlast);
   if (lane == 0) s.wave_i[wave] = wlast;
@@ -369,7 +397,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
     const int G = kSampleWaves * R, per = (G + kWave - 1) / kWave;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     double own = 0.0;
-    for (int g = g0; g < g1; ++g) own += (double)s.gsum[g];
+    for (int g = g0; g < g1; ++g) own += (double)s.big.gsum[g];
     double run;
     const double incl = wave_scan_f64(own, lane, &run);
     const double total = __shfl(incl, 63, 64);
@@ -378,7 +406,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
       int gp = -1;
       double rp = 0.0;
       for (int g = g0; g < g1; ++g) {
-        const double gs = (double)s.gsum[g];
+        const double gs = (double)s.big.gsum[g];
         if (gs > 0.0) {
           gp = g;  // rounding left the target past the sequential sum: the last non-empty group
           rp = target - run;
@@ -397,7 +425,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
   for (int w = 0; w < kSampleWaves; ++w) last = max(last, s.wave_i[w]);
   if (gstar >= 0 && wave == gstar / R) {
     const int c = gstar % R;
-    const u32x4 x = row.chunk(c);
+    const u32x4 x = row.fetch(c);
     const bool ok = row.chunk_ok(c);
     float cs = 0.f;
     int32_t lastv = -1;
@@ -437,14 +465,14 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
 // < goal <= that plus the group's mass (the lowest group if rounding never
 // reaches goal). Returns the key; *above = count or mass strictly above it,
 // *eq = the group's count.
-template <class RowT, int KEYBITS, class PF, class WF>
+template <class RowT, class PF, class WF>
 PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds& s, PF pred, WF weight, bool by_mass, double goal,
                                   double* above_out, uint32_t* eq_out) {
   using E = typename RowT::E;
   uint32_t prefix = 0, mask = 0;
   double above = 0.0;
   uint32_t eq = 0;
-  for (int shift = KEYBITS - 8; shift >= 0; shift -= 8) {
+  for (int shift = E::kKeyBits - 8; shift >= 0; shift -= 8) {
     __syncthreads();
     for (int b = threadIdx.x; b < 256; b += kSampleThreads) {
       s.rcnt[b] = 0;
@@ -496,77 +524,64 @@ PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds& s, PF pred, WF wei
   return prefix;
 }
 
-// Row parameters and the results of the first passes, shared by both paths.
-struct SampleRowState {
-  float lmax, c2, u, p;
-  uint32_t kmax;
-  int32_t k, argmax;
-  bool use_k, use_p;
-  double wall;   // whole-row mass (rows with top-p and no top-k)
-  int dk;        // window bin of the top-k threshold, -1 if below the window
-  uint32_t kk_take, kk_eq;
+// Per-row parameters (wave-uniform).
+struct SampleParams {
+  float c2, u, p;
+  int32_t k;
+  bool greedy, use_k, use_p;
+
+  PKV_INLINE void load(const SampleArgs& a, int row, int V) {
+    const float temp = a.temperature ? a.temperature[row] : 0.f;
+    greedy = !a.temperature || temp <= 1e-6f;
+    k = (!greedy && a.top_k) ? a.top_k[row] : 0;
+    use_k = k > 0 && k < V;
+    if (!use_k) k = V;
+    p = (!greedy && a.top_p) ? a.top_p[row] : 1.f;
+    use_p = p < 1.f;
+    if (use_p) p = fmaxf(p, 1e-6f);
+    c2 = greedy ? 0.f : 1.4426950408889634f / temp;
+    u = greedy ? 0.f : a.uniforms[row];
+  }
 };
 
-// Generic cuts and draw over the row in memory (any cut depth, any number of
-// kept tokens). The window histogram in s.hist / s.wtab is valid.
+// Cuts and draw over the row in memory (any cut depth, any number of kept
+// tokens): radix descents for the top-k threshold and the top-p cut,
+// group-mass scans for the ties at each cut and for the draw.
 template <class RowT>
-PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds& s, const SampleRowState& st) {
+PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds& s, const SampleParams& sp, float lmax) {
   using E = typename RowT::E;
-  const uint32_t kmax = st.kmax;
-  const float lmax = st.lmax, c2 = st.c2;
+  const float c2 = sp.c2;
   auto wt = [&](float l) { return row_weight(l, lmax, c2); };
 
   // top-k: threshold key kk_key; equal keys kept up to index kk_last
-  uint32_t kk_key = 0, kk_take = st.kk_take, kk_eq = st.kk_eq;
-  if (st.use_k) {
-    if (st.dk >= 0) {
-      kk_key = kmax - (uint32_t)st.dk;
-    } else {
-      double ab;
-      kk_key = radix_descend<RowT, E::kKeyBits>(row, s, [](int, float) { return true; },
-                                                [](float) { return 0.f; }, false, (double)st.k, &ab, &kk_eq);
-      kk_take = (uint32_t)st.k - (uint32_t)ab;
+  uint32_t kk_key = 0, kk_eq = 0, kk_take = 0;
+  int32_t kk_last = 0x7fffffff;
+  if (sp.use_k) {
+    double ab;
+    kk_key = radix_descend(row, s, [](int, float) { return true; }, [](float) { return 0.f; }, false,
+                           (double)sp.k, &ab, &kk_eq);
+    kk_take = (uint32_t)sp.k - (uint32_t)ab;
+    if (kk_take < kk_eq) {
+      const double goal = (double)kk_take - 0.5;
+      kk_last = find_crossing(
+          row, s, [&](int, float l) { return E::key(l) == kk_key ? 1.f : 0.f; }, [&](double) { return goal; });
     }
   }
-  int32_t kk_last = 0x7fffffff;
-  if (st.use_k && kk_take < kk_eq) {
-    const double goal = (double)kk_take - 0.5;
-    kk_last = find_crossing(
-        row, s, [&](int, float l) { return E::key(l) == kk_key ? 1.f : 0.f; }, [&](double) { return goal; });
-  }
   auto kept_k = [&](int i, float l) {
-    if (!st.use_k) return true;
+    if (!sp.use_k) return true;
     const uint32_t key = E::key(l);
     return key > kk_key || (key == kk_key && i <= kk_last);
   };
 
-  // kept mass after top-k
-  double Wk = st.wall;
-  if (st.use_k) Wk = row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
-
   // top-p: cut key kp_key; equal keys kept up to index kp_last
   uint32_t kp_key = 0;
   int32_t kp_last = 0x7fffffff;
-  if (st.use_p) {
-    const double target = (double)st.p * Wk;
-    int dstar = -1;
-    double above = 0.0;
-    uint32_t n_at = 0;
-    if (!st.use_k || st.dk >= 0) {  // every kept element's bin is in the window
-      const int dlim = st.use_k ? st.dk : kSampleWindow - 1;
-      window_select(
-          s,
-          [&](int b) {
-            const uint32_t n = b < dlim ? s.hist[b] : (b == dlim ? (st.use_k ? kk_take : s.hist[b]) : 0u);
-            return (double)n * (double)s.wtab[b];
-          },
-          [&](int b) { return (st.use_k && b == st.dk) ? kk_take : s.hist[b]; }, target, &dstar, &above, &n_at);
-    }
-    if (dstar >= 0) {
-      kp_key = kmax - (uint32_t)dstar;
-    } else {
-      kp_key = radix_descend<RowT, E::kKeyBits>(row, s, kept_k, wt, true, target, &above, &n_at);
-    }
+  if (sp.use_p) {
+    const double Wk = row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
+    const double target = (double)sp.p * Wk;
+    double above;
+    uint32_t n_at;
+    kp_key = radix_descend(row, s, kept_k, wt, true, target, &above, &n_at);
     // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
     const double w = (double)wt(E::key_value(kp_key));
     double need = ceil((target - above) / w);
@@ -577,278 +592,374 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds& s, const SampleRow
       kp_last = find_crossing(
           row, s, [&](int i, float l) { return (E::key(l) == kp_key && kept_k(i, l)) ? 1.f : 0.f; },
           [&](double) { return goal; });
-    } else if (st.use_k && kp_key == kk_key) {
+    } else if (sp.use_k && kp_key == kk_key) {
       kp_last = kk_last;
     }
   }
 
   // the draw: kept weights in index order, first running mass > u * W
-  const float u = st.u;
+  const float u = sp.u;
   return find_crossing(
       row, s,
       [&](int i, float l) -> float {
         if (!kept_k(i, l)) return 0.f;
         const uint32_t key = E::key(l);
-        if (st.use_p && !(key > kp_key || (key == kp_key && i <= kp_last))) return 0.f;
+        if (sp.use_p && !(key > kp_key || (key == kp_key && i <= kp_last))) return 0.f;
         return wt(l);
       },
       [&](double total) { return (double)u * total; });
 }
 
-template <typename T, int MAXR, bool REG>
-__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
-  using E = SampleElem<T>;
-  using RowT = SampleRow<T, MAXR, REG>;
-  constexpr int W = kSampleWindow;
+// ---------------------------------------------------------------- memory kernel (fp32; long bf16 rows)
+
+template <typename T>
+__global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a) {
   __shared__ SampleLds s;
   const int row_id = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int V = a.vocab;
-  const T* row_ptr = reinterpret_cast<const T*>(a.logits) + (int64_t)row_id * a.row_stride;
+  SampleParams sp;
+  sp.load(a, row_id, a.vocab);
+  SampleRow<T> row;
+  row.init(reinterpret_cast<const T*>(a.logits) + (int64_t)row_id * a.row_stride, a.vocab, wave, lane);
 
-  // Row parameters (uniform).
-  SampleRowState st;
-  const float temp = a.temperature ? a.temperature[row_id] : 0.f;
-  const bool greedy = !a.temperature || temp <= 1e-6f;
-  st.k = (!greedy && a.top_k) ? a.top_k[row_id] : 0;
-  st.use_k = st.k > 0 && st.k < V;
-  if (!st.use_k) st.k = V;
-  st.p = (!greedy && a.top_p) ? a.top_p[row_id] : 1.f;
-  st.use_p = st.p < 1.f;
-  if (st.use_p) st.p = fmaxf(st.p, 1e-6f);
-  st.c2 = greedy ? 0.f : 1.4426950408889634f / temp;
-  st.u = greedy ? 0.f : a.uniforms[row_id];
-  const bool full_mass = !greedy && st.use_p && !st.use_k;  // top-p over the whole row needs its mass
-  const float c2 = st.c2;
-
-  RowT row;
-  row.init(row_ptr, V, wave, lane);
-
-  // ---- pass 1: maximum, its first index, and (full_mass) the mass relative
-  // to a running maximum
-  float vmax = -INFINITY, mrun = -INFINITY;
+  // maximum and the first index of it (-0 == +0 compare equal)
+  float vmax = -INFINITY;
   int32_t imax = 0x7fffffff;
-  double wrun = 0.0;
-  row.for_rounds([&](int c, const u32x4& x, bool ok) {
-    float cmax = -INFINITY;
-    int32_t carg = 0x7fffffff;
-    row.elements(c, x, ok, [&](int i, float l) {
-      if (l > cmax) {
-        cmax = l;
-        carg = i;
-      }
-    });
-    if (cmax > vmax) {
-      vmax = cmax;
-      imax = carg;
-    }
-    if (full_mass && cmax > -INFINITY) {
-      if (cmax > mrun) {
-        wrun *= (double)fast_exp2((mrun - cmax) * c2);
-        mrun = cmax;
-      }
-      float cs = 0.f;
-      row.elements(c, x, ok, [&](int, float l) { cs += row_weight(l, mrun, c2); });
-      wrun += (double)cs;
+  row.for_each([&](int i, float l) {
+    if (l > vmax) {
+      vmax = l;
+      imax = i;
     }
   });
   float m = wave_max_f32(vmax);
-  if (lane == 0) s.wave_v[wave] = m;
   __syncthreads();
-  m = s.wave_v[0];
-  for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, s.wave_v[w]);
-  st.lmax = m;
-  const int32_t cand = wave_min_i32((vmax == m) ? imax : 0x7fffffff);
-  if (lane == 0) s.wave_i[wave] = cand;
+  if (lane == 0) s.wave_f[wave] = m;
   __syncthreads();
-  int32_t am = s.wave_i[0];
-  for (int w = 1; w < kSampleWaves; ++w) am = min(am, s.wave_i[w]);
-  st.argmax = am == 0x7fffffff ? 0 : am;
-  if (greedy) {
-    if (tid == 0) a.out[row_id] = st.argmax;
+  m = (float)s.wave_f[0];
+  for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, (float)s.wave_f[w]);
+  const int32_t am = block_reduce_i32(s, vmax == m ? imax : 0x7fffffff, false);
+  const int32_t argmax = am == 0x7fffffff ? 0 : am;
+  int32_t idx;
+  if (sp.greedy) {
+    idx = argmax;
+  } else if (!sp.use_k && !sp.use_p) {
+    const float u = sp.u, c2 = sp.c2;
+    idx = find_crossing(row, s, [&](int, float l) { return row_weight(l, m, c2); },
+                        [&](double total) { return (double)u * total; });
+  } else {
+    idx = sample_generic(row, s, sp, m);
+  }
+  if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
+}
+
+// ---------------------------------------------------------------- bf16 register kernel
+
+template <int MAXR>
+__global__ void __launch_bounds__(kSampleThreads) sample_bf16_kernel(SampleArgs a) {
+  constexpr int W = kSampleWindow;
+  __shared__ SampleLds s;
+  const int row_id = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = a.vocab;
+  SampleParams sp;
+  sp.load(a, row_id, V);
+  const float c2 = sp.c2;
+  const bool full_mass = !sp.greedy && sp.use_p && !sp.use_k;  // top-p over the whole row needs its mass
+
+  // word (c, j) of this thread: g = gbase + (4c + j) * 64
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(a.logits) + (int64_t)row_id * (a.row_stride / 2);
+  const int nw = (V + 1) / 2;   // words holding the row
+  const int nfull = V / 2;      // words whose both halves lie in the row
+  const int rounds = (nw + kSampleWaves * kSampleWordsPerRound - 1) / (kSampleWaves * kSampleWordsPerRound);
+  const int wbase = wave * rounds * kSampleWordsPerRound;  // first word of this wave (uniform)
+  const int gbase = wbase + lane;
+
+  // Loads run kAhead rounds ahead of pass 1 (4 per round, 56 in flight per
+  // wave: under the 63 the wait counter can track), so pass 1 overlaps them.
+  // Every load reads a word of the row (indices are clamped): rounds past
+  // `rounds` repeat the last round and are never used, words past the row
+  // are overwritten with -inf before use.
+  constexpr int kAhead = 14;
+  uint32_t r[MAXR][4];
+  auto issue = [&](int c) {
+    const int cc = min(c, rounds - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[c][j] = __builtin_nontemporal_load(wrow + min(gbase + (4 * cc + j) * kWave, nw - 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads in round order, so each round waits only for itself
+  };
+#pragma unroll
+  for (int c = 0; c < kAhead && c < MAXR; ++c) issue(c);
+
+  // ---- pass 1: keys in place, running maximum, and (full_mass) the mass
+  // relative to a per-thread reference that follows the running maximum
+  u16x2 mx = {0, 0};
+  uint32_t refk = 0;          // key of the reference (0: none yet)
+  float refv = -1e30f;        // its value, clamped so that -inf logits give weight 0, never NaN
+  double wsum = 0.0;
+#pragma unroll
+  for (int c = 0; c < MAXR; ++c) {
+    if (c + kAhead < MAXR) issue(c + kAhead);
+    if (c < rounds) {
+      if (wbase + (4 * c + 4) * kWave > nfull) {  // (uniform) this round reaches past the row
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int g = gbase + (4 * c + j) * kWave;
+          if (g >= nfull) r[c][j] = (g == nfull && (V & 1)) ? ((r[c][j] & 0xffffu) | 0xff800000u) : 0xff80ff80u;
+        }
+      }
+      uint32_t raw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        raw[j] = r[c][j];
+        r[c][j] = bf16x2_keys(raw[j]);
+        mx = __builtin_elementwise_max(mx, as_u16x2(r[c][j]));
+      }
+      if (full_mass) {
+        const uint32_t rk = max((uint32_t)mx.x, (uint32_t)mx.y);
+        if (rk > refk) {
+          const float nv = fmaxf(key16_value(rk), -1e30f);
+          wsum *= (double)fast_exp2((refv - nv) * c2);
+          refv = nv;
+          refk = rk;
+        }
+        const float off = -refv * c2;
+        float cs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cs += fast_exp2(fmaf(__uint_as_float(raw[j] << 16), c2, off));
+          cs += fast_exp2(fmaf(__uint_as_float(raw[j] & 0xffff0000u), c2, off));
+        }
+        wsum += (double)cs;
+      }
+    }
+  }
+  const uint32_t tk = max((uint32_t)mx.x, (uint32_t)mx.y);
+  const uint32_t kmax = (uint32_t)block_reduce_i32(s, (int32_t)tk, true);
+  const float lmax = key16_value(kmax);
+
+  // argmax: the first index holding kmax, searched only by threads that hold
+  // it. Positions are kept as 2 * (slot code) + half, slot code =
+  // (4c + j) * 64 + lane, and turned into an index once at the end, so that
+  // no per-word index stays live from the loads.
+  int32_t found = 0x7fffffff;
+  if (tk == kmax) {
+#pragma unroll
+    for (int c = 0; c < MAXR; ++c) {
+      if (c < rounds && found == 0x7fffffff) {
+        const u16x2 m4 = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(r[c][0]), as_u16x2(r[c][1])),
+                                                   __builtin_elementwise_max(as_u16x2(r[c][2]), as_u16x2(r[c][3])));
+        if (m4.x == kmax || m4.y == kmax) {
+#pragma unroll
+          for (int j = 3; j >= 0; --j) {  // the last assignment is the first position
+            const int code = (4 * c + j) * kWave + lane;
+            if ((r[c][j] >> 16) == kmax) found = 2 * code + 1;
+            if ((r[c][j] & 0xffffu) == kmax) found = 2 * code;
+          }
+        }
+      }
+    }
+    found += 2 * wave * rounds * kSampleWordsPerRound;
+  }
+  const int32_t am = block_reduce_i32(s, found, false);
+  const int32_t argmax = am == 0x7fffffff ? 0 : am;
+  if (sp.greedy) {
+    if (tid == 0) a.out[row_id] = argmax;
     return;
   }
-  const float lmax = st.lmax;
-  st.kmax = E::key(lmax);
-  const uint32_t kmax = st.kmax;
-  auto wt = [&](float l) { return row_weight(l, lmax, c2); };
 
-  st.wall = 0.0;
-  if (full_mass)
-    st.wall = block_sum_f64(s, (mrun > -INFINITY) ? wrun * (double)fast_exp2((mrun - lmax) * c2) : 0.0);
-
-  // ---- plain rows: the draw over the whole row
-  if (!st.use_k && !st.use_p) {
-    const float u = st.u;
-    const int32_t idx = find_crossing(row, s, [&](int, float l) { return wt(l); },
+  SampleRow<bf16_t> mrow;  // the row in memory, for the paths the list does not cover
+  mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row_id * a.row_stride, V, wave, lane);
+  if (!sp.use_k && !sp.use_p) {
+    const float u = sp.u;
+    const int32_t idx = find_crossing(mrow, s, [&](int, float l) { return row_weight(l, lmax, c2); },
                                       [&](double total) { return (double)u * total; });
-    if (tid == 0) a.out[row_id] = idx >= 0 ? idx : st.argmax;
+    if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
+    return;
+  }
+  const double wall = full_mass ? block_sum_f64(s, wsum * (double)fast_exp2((refv - lmax) * c2)) : 0.0;
+
+  // ---- pass 2: every token within W keys of the maximum into the wave's
+  // list segment, in index order. s_half = key - th (saturated) is > 0
+  // exactly for those tokens, and d = kmax - key = d0 - s_half.
+  const uint32_t th = kmax > (uint32_t)W ? kmax - (uint32_t)W : 0u;
+  const uint32_t d0 = kmax - th;
+  const u16x2 thpk = as_u16x2(th * 0x10001u);
+  int32_t run = 0;
+  const int seg = wave * kSampleSegment;
+#pragma unroll
+  for (int c = 0; c < MAXR; ++c) {
+    if (c < rounds) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sv = as_u32(__builtin_elementwise_sub_sat(as_u16x2(r[c][j]), thpk));
+        const uint64_t m = __ballot(sv != 0u);
+        if (m) {
+          const int32_t pos = run + lanes_below(m);
+          if (sv != 0u && pos < kSampleSegment) {
+            s.big.list.g[seg + pos] = (uint32_t)((4 * c + j) * kWave + lane);  // slot code; word = wave base + code
+            s.big.list.sv[seg + pos] = sv;
+          }
+          run += __popcll(m);
+        }
+      }
+    }
+  }
+  if (lane == 0) s.seg_n[wave] = run;
+  for (int b = tid; b < 256; b += kSampleThreads) {
+    s.hist[b] = 0;
+    s.wtab[b] = (b < W && (uint32_t)b <= kmax) ? row_weight(key16_value(kmax - (uint32_t)b), lmax, c2) : 0.f;
+  }
+  __syncthreads();
+  int32_t segn[kSampleWaves], n = 0;
+  bool fits = true;
+#pragma unroll
+  for (int w = 0; w < kSampleWaves; ++w) {
+    segn[w] = s.seg_n[w];
+    fits = fits && segn[w] <= kSampleSegment;
+    n += segn[w];
+  }
+
+  // ---- histogram of the list, then the cuts
+  int dcut = -1;
+  uint32_t take = 0;
+  if (fits) {
+#pragma unroll
+    for (int w = 0; w < kSampleWaves; ++w)
+      for (int q = tid; q < segn[w]; q += kSampleThreads) {
+        const uint32_t sv = s.big.list.sv[w * kSampleSegment + q];
+        if (sv & 0xffffu) atomicAdd(&s.hist[d0 - (sv & 0xffffu)], 1u);
+        if (sv >> 16) atomicAdd(&s.hist[d0 - (sv >> 16)], 1u);
+      }
+    __syncthreads();
+    int dk = -1;
+    uint32_t kk_take = 0, kk_eq = 0;
+    if (sp.use_k) {
+      double before;
+      window_select(s, [&](int b) { return (double)s.hist[b]; }, [&](int b) { return s.hist[b]; }, (double)sp.k,
+                    &dk, &before, &kk_eq);
+      if (dk >= 0) kk_take = (uint32_t)sp.k - (uint32_t)before;
+    }
+    dcut = dk;
+    take = kk_take;
+    if (sp.use_p && (!sp.use_k || dk >= 0)) {
+      double Wk = wall;
+      if (sp.use_k) {
+        double t = 0.0;
+        if (tid < W) {
+          const uint32_t nb = tid < dk ? s.hist[tid] : (tid == dk ? kk_take : 0u);
+          t = (double)nb * (double)s.wtab[tid];
+        }
+        Wk = block_sum_f64(s, t);
+      }
+      const double target = (double)sp.p * Wk;
+      const int dlim = sp.use_k ? dk : W - 1;
+      int dstar;
+      double above;
+      uint32_t n_at;
+      window_select(
+          s,
+          [&](int b) {
+            const uint32_t nb = b < dlim ? s.hist[b] : (b == dlim ? (sp.use_k ? kk_take : s.hist[b]) : 0u);
+            return (double)nb * (double)s.wtab[b];
+          },
+          [&](int b) { return (sp.use_k && b == dk) ? kk_take : s.hist[b]; }, target, &dstar, &above, &n_at);
+      dcut = dstar;
+      if (dstar >= 0) {
+        // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
+        double need = ceil((target - above) / (double)s.wtab[dstar]);
+        if (!(need >= 1.0)) need = 1.0;
+        take = need >= (double)n_at ? n_at : (uint32_t)need;
+      }
+    }
+  }
+
+  if (dcut >= 0) {
+    // ---- ties at the cut and the draw, on the list in index order. Thread
+    // t takes list positions [q0, q1) of the concatenated segments.
+    const int per = (n + kSampleThreads - 1) / kSampleThreads;
+    const int q0 = min(n, tid * per), q1 = min(n, q0 + per);
+    const int wwords = rounds * kSampleWordsPerRound;  // words per wave
+    auto word_of = [&](int e) { return (e / kSampleSegment) * wwords + (int)s.big.list.g[e]; };
+    auto slot_of = [&](int q) {  // list slot of position q (constant indices into segn)
+      int w = 0, base = 0;
+#pragma unroll
+      for (int ww = 0; ww < kSampleWaves - 1; ++ww)
+        if (w == ww && q - base >= segn[ww]) {
+          base += segn[ww];
+          w = ww + 1;
+        }
+      return w * kSampleSegment + (q - base);
+    };
+    int32_t nat = 0;
+    for (int q = q0; q < q1; ++q) {
+      const uint32_t sv = s.big.list.sv[slot_of(q)];
+      nat += ((sv & 0xffffu) && d0 - (sv & 0xffffu) == (uint32_t)dcut) +
+             ((sv >> 16) && d0 - (sv >> 16) == (uint32_t)dcut);
+    }
+    int32_t tot_at;
+    const int32_t rank0 = block_excl_scan_i32(s, nat, &tot_at);  // rank of this thread's first token at the cut
+    // weight of half h of a list entry, advancing the running rank at the cut
+    auto kept_w = [&](uint32_t sv, int h, int32_t& rank) -> float {
+      const uint32_t sh = h ? (sv >> 16) : (sv & 0xffffu);
+      if (!sh) return 0.f;
+      const uint32_t d = d0 - sh;
+      if ((int)d > dcut) return 0.f;
+      if ((int)d == dcut && (uint32_t)(rank++) >= take) return 0.f;
+      return s.wtab[d];
+    };
+    double own = 0.0;
+    int32_t last_kept = -1;
+    {
+      int32_t rank = rank0;
+      for (int q = q0; q < q1; ++q) {
+        const int e = slot_of(q);
+        const uint32_t sv = s.big.list.sv[e];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float w = kept_w(sv, h, rank);
+          if (w > 0.f) {
+            own += (double)w;
+            last_kept = (int32_t)(2 * word_of(e) + h);
+          }
+        }
+      }
+    }
+    double total, incl;
+    const double excl = block_scan_f64(s, own, &incl, &total);
+    const double target = (double)sp.u * total;
+    const int32_t lk = block_reduce_i32(s, last_kept, true);  // list order is index order
+    if (tid == 0) s.result = -1;
+    __syncthreads();
+    if (own > 0.0 && excl <= target && target < incl) {
+      int32_t rank = rank0, res = last_kept;
+      double runm = excl;
+      bool done = false;
+      for (int q = q0; q < q1 && !done; ++q) {
+        const int e = slot_of(q);
+        const uint32_t sv = s.big.list.sv[e];
+        for (int h = 0; h < 2 && !done; ++h) {
+          const float w = kept_w(sv, h, rank);
+          if (w > 0.f) {
+            runm += (double)w;
+            if (runm > target) {
+              res = (int32_t)(2 * word_of(e) + h);
+              done = true;
+            }
+          }
+        }
+      }
+      s.result = res;
+    }
+    __syncthreads();
+    const int32_t res = s.result >= 0 ? s.result : lk;
+    if (tid == 0) a.out[row_id] = res >= 0 ? res : argmax;
     return;
   }
 
-  // ---- pass 2: per-wave window histograms of d = kmax - key
-  __syncthreads();
-  for (int b = tid; b < kSampleWaves * W; b += kSampleThreads) (&s.hw[0][0])[b] = 0;
-  for (int b = tid; b < W; b += kSampleThreads)
-    s.wtab[b] = kmax >= (uint32_t)b ? wt(E::key_value(kmax - (uint32_t)b)) : 0.f;
-  __syncthreads();
-  row.for_each([&](int, float l) {
-    const uint32_t d = kmax - E::key(l);
-    if (d < (uint32_t)W) atomicAdd(&s.hw[wave][d], 1u);
-  });
-  __syncthreads();
-  for (int b = tid; b < W; b += kSampleThreads) {
-    uint32_t n = 0;
-    for (int w = 0; w < kSampleWaves; ++w) n += s.hw[w][b];
-    s.hist[b] = n;
-  }
-  __syncthreads();
-
-  // ---- top-k threshold from the window
-  st.dk = -1;
-  st.kk_take = 0;
-  st.kk_eq = 0;
-  bool fast = true;
-  if (st.use_k) {
-    double before;
-    window_select(s, [&](int b) { return (double)s.hist[b]; }, [&](int b) { return s.hist[b]; }, (double)st.k,
-                  &st.dk, &before, &st.kk_eq);
-    if (st.dk >= 0)
-      st.kk_take = (uint32_t)st.k - (uint32_t)before;
-    else
-      fast = false;
-  }
-
-  // ---- top-p cut from the window
-  int dcut = st.dk;
-  uint32_t take = st.kk_take;
-  if (fast && st.use_p) {
-    double Wk = st.wall;
-    if (st.use_k) {
-      double t = 0.0;
-      if (tid < W) {
-        const uint32_t n = tid < st.dk ? s.hist[tid] : (tid == st.dk ? st.kk_take : 0u);
-        t = (double)n * (double)s.wtab[tid];
-      }
-      Wk = block_sum_f64(s, t);
-    }
-    const double target = (double)st.p * Wk;
-    const int dlim = st.use_k ? st.dk : W - 1;
-    int dstar;
-    double above;
-    uint32_t n_at;
-    window_select(
-        s,
-        [&](int b) {
-          const uint32_t n = b < dlim ? s.hist[b] : (b == dlim ? (st.use_k ? st.kk_take : s.hist[b]) : 0u);
-          return (double)n * (double)s.wtab[b];
-        },
-        [&](int b) { return (st.use_k && b == st.dk) ? st.kk_take : s.hist[b]; }, target, &dstar, &above, &n_at);
-    if (dstar < 0) {
-      fast = false;
-    } else {
-      const double w = (double)s.wtab[dstar];
-      double need = ceil((target - above) / w);
-      if (!(need >= 1.0)) need = 1.0;
-      dcut = dstar;
-      take = need >= (double)n_at ? n_at : (uint32_t)need;
-    }
-  }
-
-  // ---- candidates: every element with d <= dcut, copied in index order
-  if (fast) {
-    int32_t cw = 0;
-    for (int b = lane; b <= dcut; b += kWave) cw += (int32_t)s.hw[wave][b];
-    cw = __shfl(wave_incl_scan_i32(cw, lane), 63, 64);  // this wave's candidates
-    int32_t ncand;
-    const int32_t wbase = __shfl(block_excl_scan_i32(s, lane == 0 ? cw : 0, &ncand), 0, 64);
-    if (ncand > kSampleCap) fast = false;
-
-    if (fast) {
-      int32_t run = wbase;
-      row.for_rounds([&](int c, const u32x4& x, bool ok) {
-        const int i0 = row.chunk_id(c) * E::kPerChunk;
-        uint32_t flags = 0;
-#pragma unroll
-        for (int e = 0; e < E::kPerChunk; ++e) {
-          const bool in = ok && i0 + e < V && (kmax - E::key(E::value(x, e))) <= (uint32_t)dcut;
-          flags |= (uint32_t)in << e;
-        }
-        if (__ballot(flags != 0)) {
-          const int32_t mine = __popc(flags);
-          const int32_t incl = wave_incl_scan_i32(mine, lane);
-          int32_t pos = run + incl - mine;
-#pragma unroll
-          for (int e = 0; e < E::kPerChunk; ++e) {
-            if (flags & (1u << e)) {
-              s.cidx[pos] = i0 + e;
-              s.cd[pos] = (uint8_t)(kmax - E::key(E::value(x, e)));
-              ++pos;
-            }
-          }
-          run += __shfl(incl, 63, 64);
-        }
-      });
-      __syncthreads();
-
-      // ---- ties at the cut and the draw, on the list
-      const int per = (ncand + kSampleThreads - 1) / kSampleThreads;
-      const int j0 = min(ncand, tid * per), j1 = min(ncand, j0 + per);
-      int32_t at = 0;
-      for (int j = j0; j < j1; ++j) at += s.cd[j] == dcut;
-      int32_t tot_at;
-      const int32_t rank0 = block_excl_scan_i32(s, at, &tot_at);  // rank of this thread's first entry at the cut
-      double own = 0.0;
-      int32_t last_kept = -1;
-      int32_t rank = rank0;
-      for (int j = j0; j < j1; ++j) {
-        const int d = s.cd[j];
-        bool kept = d < dcut;
-        if (d == dcut) kept = (uint32_t)(rank++) < take;
-        if (kept) {
-          own += (double)s.wtab[d];
-          last_kept = j;
-        }
-      }
-      double total, incl;
-      const double excl = block_scan_f64(s, own, &incl, &total);
-      const double target = (double)st.u * total;
-      const int32_t lk = wave_max_i32(last_kept);
-      if (lane == 0) s.wave_i[wave] = lk;
-      if (tid == 0) s.result = -1;
-      __syncthreads();
-      if (own > 0.0 && excl <= target && target < incl) {
-        rank = rank0;
-        double runm = excl;
-        int32_t found = last_kept;
-        for (int j = j0; j < j1; ++j) {
-          const int d = s.cd[j];
-          bool kept = d < dcut;
-          if (d == dcut) kept = (uint32_t)(rank++) < take;
-          if (kept) {
-            runm += (double)s.wtab[d];
-            if (runm > target) {
-              found = j;
-              break;
-            }
-          }
-        }
-        s.result = found;
-      }
-      __syncthreads();
-      int32_t j = s.result;
-      if (j < 0)
-        for (int w = 0; w < kSampleWaves; ++w) j = max(j, s.wave_i[w]);
-      if (tid == 0) a.out[row_id] = j >= 0 ? s.cidx[j] : st.argmax;
-      return;
-    }
-  }
-
-  // ---- generic path over the row in memory
-  SampleRow<T, 1, false> grow;
-  grow.init(row_ptr, V, wave, lane);
-  const int32_t idx = sample_generic(grow, s, st);
-  if (tid == 0) a.out[row_id] = idx >= 0 ? idx : st.argmax;
+  // ---- the cut lies below the window, or the list overflowed
+  const int32_t idx = sample_generic(mrow, s, sp, lmax);
+  if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
 }
 
 }  // namespace pkv

@@ -175,3 +175,29 @@ def test_mixed_batch_greedy_rows_exact():
         got, _, _ = _run(logits, "bf16", T, K, P, u, f"mixed-u{u_val}")
         lf = oracle.widen(logits, "bf16")
         assert np.array_equal(got[greedy], np.argmax(lf[greedy], axis=1))
+
+
+@pytest.mark.parametrize("V", [4097, 32768, 32769, 163840, 163841])
+def test_vocab_boundaries_and_masked_tokens(V):
+    """Vocabularies at and just past the kernels' register-round limits (odd
+    sizes leave half a word past the row); maxima in the last token; rows
+    where every third token is masked to -inf."""
+    rng = _rng(f"edge{V}")
+    bs = 8
+    x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+    x[0, -1] = 50.0
+    x[1, -2:] = 50.0
+    x[2:5, ::3] = -np.inf
+    T = np.array([0.0, 0.0, 0.8, 1.0, 0.5, 0.9, 0.9, 1.2], np.float32)
+    K = np.array([0, 0, 0, 40, 5, 30, 0, 0], np.int32)
+    P = np.array([1.0, 1.0, 0.9, 1.0, 0.5, 0.9, 0.95, 1.0], np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    xb = _bf16(np.pad(x, ((0, 0), (0, (-V) % 8))))     # rows padded to 16 bytes, the kernel sees V tokens
+    print(f"sample case edge-V{V}", flush=True)
+    tok = pkv.sample(to_dev(xb, "bf16")[:, :V], to_dev(T), to_dev(K), to_dev(P), to_dev(u))
+    torch.cuda.synchronize()
+    got = to_host(tok)
+    want, flagged = oracle.sample(oracle.widen(xb, "bf16")[:, :V], T, K, P, u)
+    bad = np.nonzero((got != want) & ~flagged)[0]
+    assert bad.size == 0, (V, bad.tolist(), got[bad].tolist(), want[bad].tolist())
+    assert got[0] == V - 1 and got[1] == V - 2
