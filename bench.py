@@ -109,13 +109,14 @@ def main():
     d_P = None if P is None else torch.from_numpy(P).to(dev)
     d_u = torch.from_numpy(draw_uniforms(cfg)).to(dev)
     tokens = torch.empty(bs, dtype=torch.int32, device=dev)
+    s_ws = torch.empty(pkv.sample_workspace_size(bs, cfg.vocab), dtype=torch.uint8, device=dev)
 
     def step(i):
         layer = i % LAYERS_FILLED
         kp, vp = pool[0, layer], pool[1, layer]
         pkv.store_kv(kp, vp, d_loc, new_k, new_v)
         pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
-        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens)
+        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
 
     # ---------------------------------------------------------------- timed region
     for i in range(args.warmup):
@@ -142,7 +143,7 @@ def main():
         ev[i][1].record()
         pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
         ev[i][2].record()
-        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens)
+        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
         ev[i][3].record()
     torch.cuda.synchronize()
     ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(n)])

@@ -12,28 +12,26 @@
 // and top-k are exact and ties go to the lower index; weights are
 // w(l) = exp2((l - l_max) * log2(e) / T), so equal logits weigh the same.
 //
-// bf16 rows (the register kernel):
-// * The row is read from HBM once into registers as 32-bit words (two
-//   tokens). Wave w owns words [w * WPW, (w + 1) * WPW); in round c, slot j
-//   lane l holds word w * WPW + (4c + j) * 64 + l, so every load is a
-//   coalesced 256-byte read and index order is (wave, round, slot, lane,
-//   half). Words past the row read a constant -inf pair instead, so no pass
-//   needs a bounds mask.
-// * As words arrive they are turned in place into pairs of biased 16-bit
-//   keys with packed 16-bit integer ops, and folded into a running maximum;
-//   rows whose top-p runs over the whole row also fold in their mass,
-//   relative to a per-thread reference raised with the running maximum.
-// * A second pass copies every token within 128 key values of the maximum
-//   into a per-wave LDS list, in index order (one saturating packed
-//   subtract, one ballot and one lane count per word slot). The top-k
-//   threshold and the top-p cut come from a count histogram of the list: all
-//   tokens of a bin share one key and one weight. The ties at the cut (the
-//   first n equal-key tokens in index order are kept) and the draw (kept
-//   weights in index order, first running mass > u * W) run on the list.
-// * Rows with neither top-k nor top-p, cuts below the 128-key window and
-//   lists that overflow take the paths below over the row in memory.
+// bf16 rows (slice kernel + finish kernel):
+// * Each row is cut into slices of 8192 tokens, one workgroup per slice
+//   (about 19 per row on a 151936-token vocabulary, so the chip is full even
+//   for small batches). A slice reads its tokens once, turns them into
+//   order-preserving biased 16-bit keys with packed 16-bit integer ops (-0
+//   and +0 share a key) and hands over its maximum, the first index of it,
+//   its mass (rows whose draw or top-p runs over the whole row) and, in
+//   index order, every token within 128 key values of its maximum.
+// * The finish kernel (one workgroup per row) takes the row maximum, keeps
+//   the handed-over tokens within 128 keys of it (a superset is handed over,
+//   since no slice maximum exceeds the row's) in an LDS list in index order,
+//   and finds the top-k threshold and the top-p cut from a count histogram of
+//   the list: all tokens of a bin share one key and one weight. The ties at
+//   the cut (the first n equal-key tokens in index order are kept) and the
+//   draw (kept weights in index order, first running mass > u * W) run on
+//   the list. Rows with neither top-k nor top-p locate their slice by the
+//   slices' masses and scan it. Cuts below the window and lists that
+//   overflow take the generic path below over the row in memory.
 //
-// fp32 rows, and bf16 rows too long for registers (the memory kernel): every
+// fp32 rows (the memory kernel) and the generic path: every
 // pass reads 16-byte chunks from memory (wave w owns a contiguous chunk range,
 // lane l reads chunk w * CPW + 64c + l in round c). Cuts by radix descent over
 // the full key (8 bits per pass, count and fp64 mass histograms); ties and the
@@ -101,11 +99,8 @@ struct SampleElem<float> {
 
 constexpr int kSampleThreads = 512;
 constexpr int kSampleWaves = kSampleThreads / kWave;
-constexpr int kSampleWindow = 128;      // register kernel: key values at or below the maximum in the list
-constexpr int kSampleSegment = 1024;    // register kernel: list entries per wave
-constexpr int kSampleCap = kSampleSegment * kSampleWaves;
+constexpr int kSampleWindow = 128;      // bf16: key values at or below the maximum in the window list
 constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave with a group-mass slot
-constexpr int kSampleWordsPerRound = 4 * kWave;  // register kernel: words a wave reads per round
 
 // ---------------------------------------------------------------- wave helpers
 
@@ -122,6 +117,11 @@ PKV_INLINE float wave_max_f32(float v) {
 PKV_INLINE int32_t wave_min_i32(int32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+PKV_INLINE int32_t wave_sum_i32(int32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 PKV_INLINE int32_t wave_max_i32(int32_t v) {
@@ -192,13 +192,7 @@ PKV_INLINE float key16_value(uint32_t k) {
 // ---------------------------------------------------------------- shared state
 
 struct SampleLds {
-  union {
-    struct {
-      uint32_t g[kSampleCap];    // register kernel list: slot code of the word within its wave ...
-      uint32_t sv[kSampleCap];   // ... and its two saturated key offsets (0 = not in the window)
-    } list;
-    float gsum[kSampleWaves * kSampleMaxRounds];  // memory passes: group masses, group = (wave, round)
-  } big;
+  float gsum[kSampleWaves * kSampleMaxRounds];  // memory passes: group masses, group = (wave, round)
   uint32_t hist[256];    // window counts
   float wtab[256];       // weight of the key d below the maximum
   uint32_t rcnt[256];    // radix descent: digit counts
@@ -386,7 +380,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
       cs += w;
     });
     const float g = wave_total_f32(cs);
-    if (lane == 0) s.big.gsum[wave * R + c] = g;
+    if (lane == 0) s.gsum[wave * R + c] = g;
   });
   const int32_t wlast = wave_max_i32(tlast);
   if (lane == 0) s.wave_i[wave] = wlast;
@@ -397,7 +391,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
     const int G = kSampleWaves * R, per = (G + kWave - 1) / kWave;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     double own = 0.0;
-    for (int g = g0; g < g1; ++g) own += (double)s.big.gsum[g];
+    for (int g = g0; g < g1; ++g) own += (double)s.gsum[g];
     double run;
     const double incl = wave_scan_f64(own, lane, &run);
     const double total = __shfl(incl, 63, 64);
@@ -406,7 +400,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
       int gp = -1;
       double rp = 0.0;
       for (int g = g0; g < g1; ++g) {
-        const double gs = (double)s.big.gsum[g];
+        const double gs = (double)s.gsum[g];
         if (gs > 0.0) {
           gp = g;  // rounding left the target past the sequential sum: the last non-empty group
           rp = target - run;
@@ -652,300 +646,583 @@ __global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a
   if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
 }
 
-// ---------------------------------------------------------------- bf16 register kernel
+// ---------------------------------------------------------------- bf16: slice kernel + finish kernel
 
-template <int MAXR>
-__global__ void __launch_bounds__(kSampleThreads) sample_bf16_kernel(SampleArgs a) {
+constexpr int kSliceThreads = 256;
+constexpr int kSliceRounds = 4;                                 // 16-byte chunks per thread
+constexpr int kSliceTokens = kSliceThreads * kSliceRounds * 8;  // 8192 tokens per slice
+constexpr int kSliceCap = 1024;                                 // window tokens a slice can hand over
+constexpr int kFinishCap = 8192;                                // window tokens a row can hold in LDS
+
+// What a slice hands to the finish kernel.
+struct SliceRec {
+  int32_t kmax;     // largest biased key of the slice
+  int32_t argmax;   // first row index holding it
+  int32_t count;    // tokens within the window of the slice maximum (may exceed kSliceCap)
+  int32_t pad;
+  double mass;      // sum of exp2((l - l_slice_max) * c2) over the slice (rows that need it)
+};
+
+__host__ __device__ inline int sample_slices(int V) { return (V + kSliceTokens - 1) / kSliceTokens; }
+
+// Slice kernel: workgroup b handles slice b % S of row b / S. It reads its
+// 8192 tokens once (thread t holds chunks t, t + 256, t + 512, t + 768, so
+// index order within the slice is (round, thread, token)), turns them into
+// biased 16-bit keys, and writes its maximum, the first index of it, its
+// mass (rows whose draw or top-p runs over the whole row) and, in index
+// order, every token within kSampleWindow keys of its maximum as
+// (row index, key). The window of the row maximum is inside the union of
+// these windows, since no slice maximum exceeds the row maximum. A handed-over
+// token is one word: (offset in the slice) << 16 | key; the list is built in
+// LDS and written out with 16-byte stores.
+__global__ void __launch_bounds__(kSliceThreads, 8) sample_slice_kernel(SampleArgs a, SliceRec* recs,
+                                                                        uint32_t* ents) {
   constexpr int W = kSampleWindow;
-  __shared__ SampleLds s;
-  const int row_id = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int V = a.vocab;
+  __shared__ uint32_t sh_u[kSliceThreads / kWave];
+  __shared__ int32_t sh_i[kSliceThreads / kWave];
+  __shared__ double sh_d[kSliceThreads / kWave];
+  __shared__ uint32_t sh_sc[2][kSliceThreads / kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t sh_list[kSliceCap];
+  const int V = a.vocab, S = sample_slices(V);
+  const int row = blockIdx.x / S, slice = blockIdx.x % S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
-  sp.load(a, row_id, V);
-  const float c2 = sp.c2;
-  const bool full_mass = !sp.greedy && sp.use_p && !sp.use_k;  // top-p over the whole row needs its mass
+  sp.load(a, row, V);
+  const bool need_mass = !sp.greedy && !sp.use_k;            // plain rows and top-p over the whole row
+  const bool need_list = !sp.greedy && (sp.use_k || sp.use_p);
+  const int t0 = slice * kSliceTokens;
+  const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
+                                                     (int64_t)row * a.row_stride);
+  const int last_chunk = (V - 1) / 8;
 
-  // word (c, j) of this thread: g = gbase + (4c + j) * 64
-  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(a.logits) + (int64_t)row_id * (a.row_stride / 2);
-  const int nw = (V + 1) / 2;   // words holding the row
-  const int nfull = V / 2;      // words whose both halves lie in the row
-  const int rounds = (nw + kSampleWaves * kSampleWordsPerRound - 1) / (kSampleWaves * kSampleWordsPerRound);
-  const int wbase = wave * rounds * kSampleWordsPerRound;  // first word of this wave (uniform)
-  const int gbase = wbase + lane;
-
-  // Loads run kAhead rounds ahead of pass 1 (4 per round, 56 in flight per
-  // wave: under the 63 the wait counter can track), so pass 1 overlaps them.
-  // Every load reads a word of the row (indices are clamped): rounds past
-  // `rounds` repeat the last round and are never used, words past the row
-  // are overwritten with -inf before use.
-  constexpr int kAhead = 14;
-  uint32_t r[MAXR][4];
-  auto issue = [&](int c) {
-    const int cc = min(c, rounds - 1);
+  // Load (indices clamped to the row's last chunk: every read stays inside
+  // the row), then mask the tokens at or past V to -inf. Only the raw words
+  // stay in registers; keys are recomputed where needed (three ops a pair).
+  u32x4 raw[kSliceRounds];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[c][j] = __builtin_nontemporal_load(wrow + min(gbase + (4 * cc + j) * kWave, nw - 1));
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads in round order, so each round waits only for itself
-  };
-#pragma unroll
-  for (int c = 0; c < kAhead && c < MAXR; ++c) issue(c);
-
-  // ---- pass 1: keys in place, running maximum, and (full_mass) the mass
-  // relative to a per-thread reference that follows the running maximum
+  for (int i = 0; i < kSliceRounds; ++i) {
+    const int ch = t0 / 8 + i * kSliceThreads + tid;
+    raw[i] = __builtin_nontemporal_load(crow + min(ch, last_chunk));
+  }
   u16x2 mx = {0, 0};
-  uint32_t refk = 0;          // key of the reference (0: none yet)
-  float refv = -1e30f;        // its value, clamped so that -inf logits give weight 0, never NaN
-  double wsum = 0.0;
 #pragma unroll
-  for (int c = 0; c < MAXR; ++c) {
-    if (c + kAhead < MAXR) issue(c + kAhead);
-    if (c < rounds) {
-      if (wbase + (4 * c + 4) * kWave > nfull) {  // (uniform) this round reaches past the row
+  for (int i = 0; i < kSliceRounds; ++i) {
+    const int tok = t0 + 8 * (i * kSliceThreads + tid);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int g = gbase + (4 * c + j) * kWave;
-          if (g >= nfull) r[c][j] = (g == nfull && (V & 1)) ? ((r[c][j] & 0xffffu) | 0xff800000u) : 0xff80ff80u;
-        }
-      }
-      uint32_t raw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        raw[j] = r[c][j];
-        r[c][j] = bf16x2_keys(raw[j]);
-        mx = __builtin_elementwise_max(mx, as_u16x2(r[c][j]));
-      }
-      if (full_mass) {
-        const uint32_t rk = max((uint32_t)mx.x, (uint32_t)mx.y);
-        if (rk > refk) {
-          const float nv = fmaxf(key16_value(rk), -1e30f);
-          wsum *= (double)fast_exp2((refv - nv) * c2);
-          refv = nv;
-          refk = rk;
-        }
-        const float off = -refv * c2;
-        float cs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          cs += fast_exp2(fmaf(__uint_as_float(raw[j] << 16), c2, off));
-          cs += fast_exp2(fmaf(__uint_as_float(raw[j] & 0xffff0000u), c2, off));
-        }
-        wsum += (double)cs;
-      }
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = raw[i][j];
+      if (tok + 2 * j >= V) w = 0xff80ff80u;
+      else if (tok + 2 * j + 1 >= V) w = (w & 0xffffu) | 0xff800000u;
+      raw[i][j] = w;
+      mx = __builtin_elementwise_max(mx, as_u16x2(bf16x2_keys(w)));
     }
   }
   const uint32_t tk = max((uint32_t)mx.x, (uint32_t)mx.y);
-  const uint32_t kmax = (uint32_t)block_reduce_i32(s, (int32_t)tk, true);
-  const float lmax = key16_value(kmax);
-
-  // argmax: the first index holding kmax, searched only by threads that hold
-  // it. Positions are kept as 2 * (slot code) + half, slot code =
-  // (4c + j) * 64 + lane, and turned into an index once at the end, so that
-  // no per-word index stays live from the loads.
+  // mass relative to this thread's maximum (rescaled to the slice maximum below)
+  double mass = 0.0;
+  if (need_mass) {
+    const float c2 = sp.c2, off = -fmaxf(key16_value(tk), -1e30f) * c2;
+#pragma unroll
+    for (int i = 0; i < kSliceRounds; ++i) {
+      float cs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cs += fast_exp2(fmaf(__uint_as_float(raw[i][j] << 16), c2, off));
+        cs += fast_exp2(fmaf(__uint_as_float(raw[i][j] & 0xffff0000u), c2, off));
+      }
+      mass += (double)cs;
+    }
+  }
+  // slice maximum
+  const uint32_t wk = (uint32_t)wave_max_i32((int32_t)tk);
+  if (lane == 0) sh_u[wave] = wk;
+  __syncthreads();
+  uint32_t kmax = sh_u[0];
+#pragma unroll
+  for (int w = 1; w < kSliceThreads / kWave; ++w) kmax = max(kmax, sh_u[w]);
+  if (need_mass) {
+    mass = wave_sum_f64(mass * (double)fast_exp2((fmaxf(key16_value(tk), -1e30f) -
+                                                   fmaxf(key16_value(kmax), -1e30f)) * sp.c2));
+    if (lane == 0) sh_d[wave] = mass;
+  }
+  // first index holding it
   int32_t found = 0x7fffffff;
   if (tk == kmax) {
 #pragma unroll
-    for (int c = 0; c < MAXR; ++c) {
-      if (c < rounds && found == 0x7fffffff) {
-        const u16x2 m4 = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(r[c][0]), as_u16x2(r[c][1])),
-                                                   __builtin_elementwise_max(as_u16x2(r[c][2]), as_u16x2(r[c][3])));
-        if (m4.x == kmax || m4.y == kmax) {
+    for (int i = kSliceRounds - 1; i >= 0; --i)
 #pragma unroll
-          for (int j = 3; j >= 0; --j) {  // the last assignment is the first position
-            const int code = (4 * c + j) * kWave + lane;
-            if ((r[c][j] >> 16) == kmax) found = 2 * code + 1;
-            if ((r[c][j] & 0xffffu) == kmax) found = 2 * code;
-          }
-        }
+      for (int j = 3; j >= 0; --j) {
+        const int tok = t0 + 8 * (i * kSliceThreads + tid) + 2 * j;
+        const uint32_t k = bf16x2_keys(raw[i][j]);
+        if ((k >> 16) == kmax) found = tok + 1;
+        if ((k & 0xffffu) == kmax) found = tok;
       }
-    }
-    found += 2 * wave * rounds * kSampleWordsPerRound;
   }
-  const int32_t am = block_reduce_i32(s, found, false);
-  const int32_t argmax = am == 0x7fffffff ? 0 : am;
-  if (sp.greedy) {
-    if (tid == 0) a.out[row_id] = argmax;
-    return;
-  }
-
-  SampleRow<bf16_t> mrow;  // the row in memory, for the paths the list does not cover
-  mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row_id * a.row_stride, V, wave, lane);
-  if (!sp.use_k && !sp.use_p) {
-    const float u = sp.u;
-    const int32_t idx = find_crossing(mrow, s, [&](int, float l) { return row_weight(l, lmax, c2); },
-                                      [&](double total) { return (double)u * total; });
-    if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
-    return;
-  }
-  const double wall = full_mass ? block_sum_f64(s, wsum * (double)fast_exp2((refv - lmax) * c2)) : 0.0;
-
-  // ---- pass 2: every token within W keys of the maximum into the wave's
-  // list segment, in index order. s_half = key - th (saturated) is > 0
-  // exactly for those tokens, and d = kmax - key = d0 - s_half.
-  const uint32_t th = kmax > (uint32_t)W ? kmax - (uint32_t)W : 0u;
-  const uint32_t d0 = kmax - th;
-  const u16x2 thpk = as_u16x2(th * 0x10001u);
-  int32_t run = 0;
-  const int seg = wave * kSampleSegment;
+  found = wave_min_i32(found);
+  if (lane == 0) sh_i[wave] = found;
+  // window tokens: key > th, i.e. the saturated key - th is nonzero
+  int32_t count = 0;
+  if (need_list) {
+    const uint32_t th = kmax > (uint32_t)W ? kmax - (uint32_t)W : 0u;
+    const u16x2 thpk = as_u16x2(th * 0x10001u);
+    uint32_t n[kSliceRounds];
 #pragma unroll
-  for (int c = 0; c < MAXR; ++c) {
-    if (c < rounds) {
+    for (int i = 0; i < kSliceRounds; ++i) {
+      n[i] = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t sv = as_u32(__builtin_elementwise_sub_sat(as_u16x2(r[c][j]), thpk));
-        const uint64_t m = __ballot(sv != 0u);
-        if (m) {
-          const int32_t pos = run + lanes_below(m);
-          if (sv != 0u && pos < kSampleSegment) {
-            s.big.list.g[seg + pos] = (uint32_t)((4 * c + j) * kWave + lane);  // slot code; word = wave base + code
-            s.big.list.sv[seg + pos] = sv;
-          }
-          run += __popcll(m);
-        }
+        const u16x2 sv = __builtin_elementwise_sub_sat(as_u16x2(bf16x2_keys(raw[i][j])), thpk);
+        n[i] += (sv.x != 0) + (sv.y != 0);
       }
     }
+    // positions in (round, thread) order: two 16-bit-lane scans over the block
+    const uint32_t p01 = n[0] | (n[1] << 16), p23 = n[2] | (n[3] << 16);
+    const uint32_t i01 = (uint32_t)wave_incl_scan_i32((int32_t)p01, lane);
+    const uint32_t i23 = (uint32_t)wave_incl_scan_i32((int32_t)p23, lane);
+    if (lane == 63) {
+      sh_sc[0][wave] = i01;
+      sh_sc[1][wave] = i23;
+    }
+    __syncthreads();
+    uint32_t o01 = 0, o23 = 0, t01 = 0, t23 = 0;
+#pragma unroll
+    for (int w = 0; w < kSliceThreads / kWave; ++w) {
+      if (w < wave) {
+        o01 += sh_sc[0][w];
+        o23 += sh_sc[1][w];
+      }
+      t01 += sh_sc[0][w];
+      t23 += sh_sc[1][w];
+    }
+    const uint32_t e01 = o01 + i01 - p01, e23 = o23 + i23 - p23;  // exclusive, per 16-bit lane
+    const uint32_t tot[4] = {t01 & 0xffffu, t01 >> 16, t23 & 0xffffu, t23 >> 16};
+    uint32_t pos[4] = {e01 & 0xffffu, (e01 >> 16) + tot[0], (e23 & 0xffffu) + tot[0] + tot[1],
+                       (e23 >> 16) + tot[0] + tot[1] + tot[2]};
+    count = (int32_t)(tot[0] + tot[1] + tot[2] + tot[3]);
+#pragma unroll
+    for (int i = 0; i < kSliceRounds; ++i) {
+      if (n[i]) {
+        const uint32_t off = 8 * (i * kSliceThreads + tid);  // token offset within the slice
+        uint32_t p = pos[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t kw = bf16x2_keys(raw[i][j]);
+            const uint32_t k = h ? (kw >> 16) : (kw & 0xffffu);
+            if (k > th) {
+              if (p < (uint32_t)kSliceCap) sh_list[p] = ((off + 2 * j + h) << 16) | k;
+              ++p;
+            }
+          }
+      }
+    }
+    __syncthreads();
+    const int nw = (min(count, kSliceCap) + 3) / 4;  // 16-byte stores
+    u32x4* out = reinterpret_cast<u32x4*>(ents + (int64_t)blockIdx.x * kSliceCap);
+    for (int q = tid; q < nw; q += kSliceThreads) out[q] = reinterpret_cast<const u32x4*>(sh_list)[q];
   }
-  if (lane == 0) s.seg_n[wave] = run;
+  __syncthreads();
+  if (tid == 0) {
+    SliceRec r;
+    r.kmax = (int32_t)kmax;
+    int32_t am = sh_i[0];
+    for (int w = 1; w < kSliceThreads / kWave; ++w) am = min(am, sh_i[w]);
+    r.argmax = am;
+    r.count = count;
+    r.pad = 0;
+    double m = 0.0;
+    if (need_mass)
+      for (int w = 0; w < kSliceThreads / kWave; ++w) m += sh_d[w];
+    r.mass = m;
+    recs[blockIdx.x] = r;
+  }
+}
+
+// Exclusive block scan of v (thread order) that also returns the block
+// maximum of m, with the same three barriers; *incl_out equals the next
+// thread's exclusive prefix bit for bit.
+PKV_INLINE double block_scan_f64_max(SampleLds& s, double v, int32_t m, double* incl_out, double* total,
+                                     int32_t* mmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double excl;
+  const double incl = wave_scan_f64(v, lane, &excl);
+  m = wave_max_i32(m);
+  __syncthreads();
+  if (lane == 63) {
+    s.scan_f[wave] = incl;
+    s.wave_j[wave] = m;
+  }
+  __syncthreads();
+  double off = 0.0, tot = 0.0;
+  int32_t mx = s.wave_j[0];
+  for (int w = 0; w < kSampleWaves; ++w) {
+    if (w < wave) off += s.scan_f[w];
+    tot += s.scan_f[w];
+    mx = max(mx, s.wave_j[w]);
+  }
+  __syncthreads();
+  *total = tot;
+  *mmax = mx;
+  *incl_out = off + incl;
+  return off + excl;
+}
+
+// First of W <= 128 bins (ascending) whose running amount reaches goal, by
+// one wave (two bins per lane): *bin = -1 if none, *before = the amount
+// strictly before it, *cnt = count(bin). No barriers.
+template <class AF, class CF>
+PKV_INLINE void wave_select128(AF amount, CF count, double goal, int* bin, double* before, uint32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  const double a0 = amount(2 * lane), a1 = amount(2 * lane + 1);
+  double excl;
+  const double incl = wave_scan_f64(a0 + a1, lane, &excl);
+  int b = -1;
+  double bef = 0.0;
+  if (a0 + a1 > 0.0 && excl < goal && goal <= incl) {  // at most one lane
+    if (a0 > 0.0 && goal <= excl + a0) {
+      b = 2 * lane;
+      bef = excl;
+    } else {
+      b = 2 * lane + 1;
+      bef = excl + a0;
+    }
+  }
+  const uint64_t who = __ballot(b >= 0);
+  if (!who) {
+    *bin = -1;
+    *before = 0.0;
+    *cnt = 0;
+    return;
+  }
+  const int l0 = __ffsll((unsigned long long)who) - 1;
+  *bin = __shfl(b, l0, 64);
+  *before = __shfl(bef, l0, 64);
+  const uint32_t c = b >= 0 ? count(b) : 0u;
+  *cnt = (uint32_t)__shfl((int32_t)c, l0, 64);
+}
+
+// Finish kernel: one workgroup per row merges the slices' results.
+__global__ void __launch_bounds__(kSampleThreads) sample_finish_kernel(SampleArgs a, const SliceRec* recs,
+                                                                       const uint32_t* ents) {
+  constexpr int W = kSampleWindow;
+  static_assert(W <= 128, "wave_select128 covers 128 bins");
+  __shared__ SampleLds s;
+  __shared__ int32_t f_idx[kFinishCap];
+  __shared__ uint8_t f_d[kFinishCap];
+  __shared__ int32_t f_cnt[256 + 1];
+  __shared__ int32_t h_i[8];
+  __shared__ double h_f[2];
+  const int V = a.vocab, S = sample_slices(V);
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  SampleParams sp;
+  sp.load(a, row, V);
+  const float c2 = sp.c2;
+  const SliceRec* rr = recs + (int64_t)row * S;
+  const bool plain = !sp.greedy && !sp.use_k && !sp.use_p;
+
+  // ---- wave 0: everything about the slices (at most 256; lane l holds slices l, l + 64, ...)
+  if (wave == 0) {
+    SliceRec rec[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u * kWave + lane < S) rec[u] = rr[u * kWave + lane];  // one round of loads
+    int32_t mk = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u * kWave + lane < S) mk = max(mk, rec[u].kmax);
+    mk = wave_max_i32(mk);  // row maximum
+    int32_t am = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u * kWave + lane < S && rec[u].kmax == mk) am = min(am, rec[u].argmax);
+    am = wave_min_i32(am);  // its first index: slices are in index order
+    int32_t T = 0, ovf = 0, psl = -1;
+    double wall = 0.0, rem = INFINITY;
+    if (!sp.greedy) {
+      const float lmax = key16_value((uint32_t)mk);
+      double sm[4];  // slice masses in units of the row maximum
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sm[u] = u * kWave + lane < S && !sp.use_k
+                    ? rec[u].mass * (double)fast_exp2((fmaxf(key16_value((uint32_t)rec[u].kmax), -1e30f) - lmax) * c2)
+                    : 0.0;
+      if (!sp.use_k) wall = wave_sum_f64(sm[0] + sm[1] + sm[2] + sm[3]);
+      if (plain) {  // the slice where the running mass passes u * W
+        const double target = (double)sp.u * wall;
+        double off = 0.0;
+        int32_t last = -1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (psl < 0 && u * kWave < S) {
+            double ex;
+            const double in = wave_scan_f64(sm[u], lane, &ex);
+            const uint64_t who = __ballot(sm[u] > 0.0 && off + ex <= target && target < off + in);
+            if (who) {
+              const int l0 = __ffsll((unsigned long long)who) - 1;
+              psl = u * kWave + l0;
+              rem = target - (off + __shfl(ex, l0, 64));
+            }
+            last = max(last, wave_max_i32(sm[u] > 0.0 ? u * kWave + lane : -1));
+            off += __shfl(in, 63, 64);
+          }
+        }
+        if (psl < 0) psl = max(last, 0);  // rounding left the target past every slice: the last one with mass
+      } else {  // flattened window tokens of the slices whose maximum reaches the threshold
+        const uint32_t thr = (uint32_t)mk >= (uint32_t)(W - 1) ? (uint32_t)mk - (uint32_t)(W - 1) : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (u * kWave < S) {
+            const int sl = u * kWave + lane;
+            int32_t c = 0;
+            if (sl < S && (uint32_t)rec[u].kmax >= thr) {
+              c = min(rec[u].count, kSliceCap);
+              ovf |= rec[u].count > kSliceCap;
+            }
+            const int32_t in = wave_incl_scan_i32(c, lane);
+            if (sl < S) f_cnt[sl] = T + in - c;
+            T += __shfl(in, 63, 64);
+          }
+        }
+        ovf = wave_max_i32(ovf);
+        if (lane == 0) f_cnt[S] = T;
+      }
+    }
+    if (lane == 0) {
+      h_i[0] = mk;
+      h_i[1] = am;
+      h_i[2] = T;
+      h_i[3] = ovf;
+      h_i[4] = psl;
+      h_f[0] = wall;
+      h_f[1] = rem;
+    }
+  }
+  __syncthreads();
+  const uint32_t kmax = (uint32_t)h_i[0];
+  const int32_t argmax = h_i[1] == 0x7fffffff ? 0 : h_i[1];
+  if (sp.greedy) {
+    if (tid == 0) a.out[row] = argmax;
+    return;
+  }
+  const float lmax = key16_value(kmax);
+  const double wall = h_f[0];
+  SampleRow<bf16_t> mrow;  // the row in memory, for the paths the window does not cover
+  mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
+
+  if (plain) {
+    // ---- plain rows: the token inside the chosen slice; thread t scans tokens [16t, 16t + 16)
+    const int sl = h_i[4];
+    const double rem = h_f[1];
+    const bf16_t* tp = reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride +
+                       (int64_t)sl * kSliceTokens + 16 * tid;
+    const int base = sl * kSliceTokens + 16 * tid;
+    float w[16];
+    double own = 0.0;
+    int32_t lastp = -1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (base + 8 * q < V) x = *reinterpret_cast<const u32x4*>(tp + 8 * q);
+      float cs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = base + 8 * q + e;
+        w[8 * q + e] = i < V ? row_weight(SampleElem<bf16_t>::value(x, e), lmax, c2) : 0.f;
+        if (w[8 * q + e] > 0.f) lastp = i;
+        cs += w[8 * q + e];
+      }
+      own += (double)cs;
+    }
+    double in2, tot2;
+    int32_t lk;
+    const double ex2 = block_scan_f64_max(s, own, lastp, &in2, &tot2, &lk);
+    if (tid == 0) s.result = -1;
+    __syncthreads();
+    if (own > 0.0 && ex2 <= rem && rem < in2) {
+      double run = ex2;
+      int32_t res = lastp;
+      bool done = false;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!done && w[e] > 0.f) {
+          run += (double)w[e];
+          if (run > rem) {
+            res = base + e;
+            done = true;
+          }
+        }
+      s.result = res;
+    }
+    __syncthreads();
+    const int32_t r = s.result >= 0 ? s.result : lk;
+    if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
+    return;
+  }
+
+  // ---- rows with top-k or top-p: the window of the row maximum (keys >= thr, d = kmax - key < W)
+  const uint32_t thr = kmax >= (uint32_t)(W - 1) ? kmax - (uint32_t)(W - 1) : 0u;
+  const int32_t T = h_i[2];
+  // Thread t takes flattened positions [g0, g1) (slice by slice, index order).
+  const int gper = (T + kSampleThreads - 1) / kSampleThreads;
+  const int g0 = min(T, tid * gper), g1 = min(T, g0 + gper);
+  int sl0 = 0;  // the slice holding g0: the last slice that starts at or before it
+  for (int lo = 0, hi = S - 1; lo <= hi;) {
+    const int mid = (lo + hi) >> 1;
+    if (f_cnt[mid] <= g0) {
+      sl0 = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  // Batches of kB positions; the first batch stays in registers for the
+  // second pass (one batch covers rows of up to 512 * kB handed-over tokens).
+  constexpr int kB = 16;
+  auto load_batch = [&](int q0, int& sl, uint32_t* idx, uint32_t* key) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int q = q0 + u;
+      idx[u] = 0;
+      key[u] = 0;
+      if (q < g1) {
+        while (f_cnt[sl + 1] <= q) ++sl;
+        const uint32_t e = ents[((int64_t)row * S + sl) * kSliceCap + (q - f_cnt[sl])];
+        idx[u] = (uint32_t)sl * kSliceTokens + (e >> 16);
+        key[u] = e & 0xffffu;  // 0 (below every real key) past g1
+      }
+    }
+  };
+  uint32_t bidx[kB], bkey[kB];
+  int sl_next = sl0;
+  load_batch(g0, sl_next, bidx, bkey);
+  int32_t npass = 0;
+#pragma unroll
+  for (int u = 0; u < kB; ++u) npass += bkey[u] >= thr && bkey[u] != 0;
+  {
+    int sl = sl_next;
+    for (int q0 = g0 + kB; q0 < g1; q0 += kB) {
+      uint32_t ti[kB], tk[kB];
+      load_batch(q0, sl, ti, tk);
+#pragma unroll
+      for (int u = 0; u < kB; ++u) npass += tk[u] >= thr && tk[u] != 0;
+    }
+  }
+  int32_t n;
+  const int32_t pbase = block_excl_scan_i32(s, npass, &n);
+  const bool ok = h_i[3] == 0 && n <= kFinishCap;
+  if (ok) {
+    int32_t p = pbase;
+    auto put = [&](const uint32_t* ti, const uint32_t* tk) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (tk[u] >= thr && tk[u] != 0) {
+          f_idx[p] = (int32_t)ti[u];
+          f_d[p] = (uint8_t)(kmax - tk[u]);
+          ++p;
+        }
+    };
+    put(bidx, bkey);
+    int sl = sl_next;
+    for (int q0 = g0 + kB; q0 < g1; q0 += kB) {
+      uint32_t ti[kB], tk[kB];
+      load_batch(q0, sl, ti, tk);
+      put(ti, tk);
+    }
+  }
   for (int b = tid; b < 256; b += kSampleThreads) {
     s.hist[b] = 0;
     s.wtab[b] = (b < W && (uint32_t)b <= kmax) ? row_weight(key16_value(kmax - (uint32_t)b), lmax, c2) : 0.f;
   }
   __syncthreads();
-  int32_t segn[kSampleWaves], n = 0;
-  bool fits = true;
-#pragma unroll
-  for (int w = 0; w < kSampleWaves; ++w) {
-    segn[w] = s.seg_n[w];
-    fits = fits && segn[w] <= kSampleSegment;
-    n += segn[w];
-  }
+  if (ok)
+    for (int q = tid; q < n; q += kSampleThreads) atomicAdd(&s.hist[f_d[q]], 1u);
+  __syncthreads();
 
-  // ---- histogram of the list, then the cuts
-  int dcut = -1;
-  uint32_t take = 0;
-  if (fits) {
-#pragma unroll
-    for (int w = 0; w < kSampleWaves; ++w)
-      for (int q = tid; q < segn[w]; q += kSampleThreads) {
-        const uint32_t sv = s.big.list.sv[w * kSampleSegment + q];
-        if (sv & 0xffffu) atomicAdd(&s.hist[d0 - (sv & 0xffffu)], 1u);
-        if (sv >> 16) atomicAdd(&s.hist[d0 - (sv >> 16)], 1u);
-      }
-    __syncthreads();
-    int dk = -1;
-    uint32_t kk_take = 0, kk_eq = 0;
-    if (sp.use_k) {
-      double before;
-      window_select(s, [&](int b) { return (double)s.hist[b]; }, [&](int b) { return s.hist[b]; }, (double)sp.k,
-                    &dk, &before, &kk_eq);
-      if (dk >= 0) kk_take = (uint32_t)sp.k - (uint32_t)before;
-    }
-    dcut = dk;
-    take = kk_take;
-    if (sp.use_p && (!sp.use_k || dk >= 0)) {
-      double Wk = wall;
+  // ---- cuts, by wave 0
+  if (wave == 0) {
+    int dcut = -1;
+    uint32_t take = 0;
+    if (ok) {
+      auto hc = [&](int b) { return b < W ? s.hist[b] : 0u; };
+      int dk = -1;
+      uint32_t kk_take = 0, kk_eq = 0;
       if (sp.use_k) {
-        double t = 0.0;
-        if (tid < W) {
-          const uint32_t nb = tid < dk ? s.hist[tid] : (tid == dk ? kk_take : 0u);
-          t = (double)nb * (double)s.wtab[tid];
+        double before;
+        wave_select128([&](int b) { return (double)hc(b); }, hc, (double)sp.k, &dk, &before, &kk_eq);
+        if (dk >= 0) kk_take = (uint32_t)sp.k - (uint32_t)before;
+      }
+      dcut = dk;
+      take = kk_take;
+      if (sp.use_p && (!sp.use_k || dk >= 0)) {
+        const int dlim = sp.use_k ? dk : W - 1;
+        auto nb = [&](int b) { return b < dlim ? hc(b) : (b == dlim ? (sp.use_k ? kk_take : hc(b)) : 0u); };
+        double Wk = wall;
+        if (sp.use_k) Wk = wave_sum_f64((double)nb(2 * lane) * (double)s.wtab[2 * lane] +
+                                        (double)nb(2 * lane + 1) * (double)s.wtab[2 * lane + 1]);
+        const double target = (double)sp.p * Wk;
+        int dstar;
+        double above;
+        uint32_t n_at;
+        wave_select128([&](int b) { return (double)nb(b) * (double)s.wtab[b]; }, nb, target, &dstar, &above,
+                       &n_at);
+        dcut = dstar;
+        if (dstar >= 0) {
+          // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
+          double need = ceil((target - above) / (double)s.wtab[dstar]);
+          if (!(need >= 1.0)) need = 1.0;
+          take = need >= (double)n_at ? n_at : (uint32_t)need;
         }
-        Wk = block_sum_f64(s, t);
       }
-      const double target = (double)sp.p * Wk;
-      const int dlim = sp.use_k ? dk : W - 1;
-      int dstar;
-      double above;
-      uint32_t n_at;
-      window_select(
-          s,
-          [&](int b) {
-            const uint32_t nb = b < dlim ? s.hist[b] : (b == dlim ? (sp.use_k ? kk_take : s.hist[b]) : 0u);
-            return (double)nb * (double)s.wtab[b];
-          },
-          [&](int b) { return (sp.use_k && b == dk) ? kk_take : s.hist[b]; }, target, &dstar, &above, &n_at);
-      dcut = dstar;
-      if (dstar >= 0) {
-        // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
-        double need = ceil((target - above) / (double)s.wtab[dstar]);
-        if (!(need >= 1.0)) need = 1.0;
-        take = need >= (double)n_at ? n_at : (uint32_t)need;
-      }
+    }
+    if (lane == 0) {
+      h_i[5] = dcut;
+      h_i[6] = (int32_t)take;
     }
   }
+  __syncthreads();
+  const int dcut = h_i[5];
+  const uint32_t take = (uint32_t)h_i[6];
 
   if (dcut >= 0) {
-    // ---- ties at the cut and the draw, on the list in index order. Thread
-    // t takes list positions [q0, q1) of the concatenated segments.
+    // ---- ties at the cut and the draw, on the list: thread t takes [q0, q1)
     const int per = (n + kSampleThreads - 1) / kSampleThreads;
     const int q0 = min(n, tid * per), q1 = min(n, q0 + per);
-    const int wwords = rounds * kSampleWordsPerRound;  // words per wave
-    auto word_of = [&](int e) { return (e / kSampleSegment) * wwords + (int)s.big.list.g[e]; };
-    auto slot_of = [&](int q) {  // list slot of position q (constant indices into segn)
-      int w = 0, base = 0;
-#pragma unroll
-      for (int ww = 0; ww < kSampleWaves - 1; ++ww)
-        if (w == ww && q - base >= segn[ww]) {
-          base += segn[ww];
-          w = ww + 1;
-        }
-      return w * kSampleSegment + (q - base);
-    };
     int32_t nat = 0;
-    for (int q = q0; q < q1; ++q) {
-      const uint32_t sv = s.big.list.sv[slot_of(q)];
-      nat += ((sv & 0xffffu) && d0 - (sv & 0xffffu) == (uint32_t)dcut) +
-             ((sv >> 16) && d0 - (sv >> 16) == (uint32_t)dcut);
-    }
+    for (int q = q0; q < q1; ++q) nat += f_d[q] == dcut;
     int32_t tot_at;
     const int32_t rank0 = block_excl_scan_i32(s, nat, &tot_at);  // rank of this thread's first token at the cut
-    // weight of half h of a list entry, advancing the running rank at the cut
-    auto kept_w = [&](uint32_t sv, int h, int32_t& rank) -> float {
-      const uint32_t sh = h ? (sv >> 16) : (sv & 0xffffu);
-      if (!sh) return 0.f;
-      const uint32_t d = d0 - sh;
-      if ((int)d > dcut) return 0.f;
-      if ((int)d == dcut && (uint32_t)(rank++) >= take) return 0.f;
-      return s.wtab[d];
-    };
     double own = 0.0;
     int32_t last_kept = -1;
     {
       int32_t rank = rank0;
       for (int q = q0; q < q1; ++q) {
-        const int e = slot_of(q);
-        const uint32_t sv = s.big.list.sv[e];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float w = kept_w(sv, h, rank);
-          if (w > 0.f) {
-            own += (double)w;
-            last_kept = (int32_t)(2 * word_of(e) + h);
-          }
+        const int d = f_d[q];
+        const bool kept = d < dcut || (d == dcut && (uint32_t)(rank++) < take);
+        if (kept) {
+          own += (double)s.wtab[d];
+          last_kept = f_idx[q];
         }
       }
     }
-    double total, incl;
-    const double excl = block_scan_f64(s, own, &incl, &total);
-    const double target = (double)sp.u * total;
-    const int32_t lk = block_reduce_i32(s, last_kept, true);  // list order is index order
+    double tot, incl;
+    int32_t lk;  // list order is index order: the largest kept index is the last kept token
+    const double excl = block_scan_f64_max(s, own, last_kept, &incl, &tot, &lk);
+    const double target = (double)sp.u * tot;
     if (tid == 0) s.result = -1;
     __syncthreads();
     if (own > 0.0 && excl <= target && target < incl) {
       int32_t rank = rank0, res = last_kept;
-      double runm = excl;
-      bool done = false;
-      for (int q = q0; q < q1 && !done; ++q) {
-        const int e = slot_of(q);
-        const uint32_t sv = s.big.list.sv[e];
-        for (int h = 0; h < 2 && !done; ++h) {
-          const float w = kept_w(sv, h, rank);
-          if (w > 0.f) {
-            runm += (double)w;
-            if (runm > target) {
-              res = (int32_t)(2 * word_of(e) + h);
-              done = true;
-            }
+      double run = excl;
+      for (int q = q0; q < q1; ++q) {
+        const int d = f_d[q];
+        const bool kept = d < dcut || (d == dcut && (uint32_t)(rank++) < take);
+        if (kept) {
+          run += (double)s.wtab[d];
+          if (run > target) {
+            res = f_idx[q];
+            break;
           }
         }
       }
@@ -953,13 +1230,13 @@ __global__ void __launch_bounds__(kSampleThreads) sample_bf16_kernel(SampleArgs 
     }
     __syncthreads();
     const int32_t res = s.result >= 0 ? s.result : lk;
-    if (tid == 0) a.out[row_id] = res >= 0 ? res : argmax;
+    if (tid == 0) a.out[row] = res >= 0 ? res : argmax;
     return;
   }
 
-  // ---- the cut lies below the window, or the list overflowed
+  // ---- the cut lies below the window, or a list overflowed
   const int32_t idx = sample_generic(mrow, s, sp, lmax);
-  if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
+  if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
 }
 
 }  // namespace pkv

@@ -148,14 +148,15 @@ def test_decode_workspace_size_grows_with_batch(L):
 
 
 def _sample(L, logits=0x100000, dt=1, bs=4, V=1024, stride=1024, T=0x200000, K=None, P=None, u=0x300000,
-            out=0x400000):
-    return L.pkv_sample(logits, dt, bs, V, stride, T, K, P, u, out, None, 0, None)
+            out=0x400000, ws=0x500000, ws_bytes=1 << 30):
+    return L.pkv_sample(logits, dt, bs, V, stride, T, K, P, u, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(logits=None), -1), (dict(dt=7), -2), (dict(V=0), -3), (dict(bs=-1), -3), (dict(stride=1000), -3),
     (dict(stride=1028), -5), (dict(logits=0x100004), -5), (dict(out=None), -1), (dict(u=None), -1),
     (dict(V=2097153, stride=2097160), -3), (dict(dt=0, V=1048577, stride=1048580), -3),
+    (dict(ws=None), -6), (dict(ws_bytes=1024), -6), (dict(ws=0x500008), -5),
 ])
 def test_sample_argument_errors(L, kw, status):
     assert _sample(L, **kw) == status
@@ -164,6 +165,12 @@ def test_sample_argument_errors(L, kw, status):
 
 def test_sample_zero_rows_is_noop(L):
     assert _sample(L, bs=0) == 0
+
+
+def test_sample_workspace_size(L):
+    """bf16 rows need slice records and window lists; the size grows with the batch."""
+    a, b = L.pkv_sample_workspace_size(1, 151936), L.pkv_sample_workspace_size(256, 151936)
+    assert 0 < a < b and L.pkv_sample_workspace_size(0, 151936) == 0
 
 
 def _extend(L, pool, bs=2, hq=16, q=0x60000, o=0x70000, pt=0x80000, cl=0x88000, dl=0x90000, total_q=10,
