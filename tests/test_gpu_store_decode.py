@@ -196,3 +196,54 @@ def test_decode_single_key_returns_v():
         slot = c["table"][r, 0]
         for h in range(16):
             assert np.array_equal(got[r, h], c["kv"][1][slot, h // 2])
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_decode_full_size_sampled(cid):
+    """Decode at the full sizes of the 256-request batch (config 3, page_size 1)
+    and of the 240 decode rows of the mixed batch (config 5, page_size 16,
+    contexts up to 32768, rows picked through table_idx), in the launch
+    configuration the benchmark times. The pool is filled on the device with
+    torch draws (the inputs); store_kv writes each request's new row first;
+    the oracle checks 16 seeded requests, rebuilt from the pool rows read back
+    before the store plus the new rows."""
+    from workloads import default_num_pages, draw_lengths, draw_page_table, draw_q
+    cfg = config(cid)
+    C, S = draw_lengths(cfg)
+    nump = default_num_pages(cfg, S)
+    table = draw_page_table(cfg, S, nump)
+    q_all = draw_q(cfg, C, S)
+    E = (S - C).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(E)])
+    dec = np.nonzero(E == 1)[0].astype(np.int32)
+    q = q_all[cu[dec]]
+    Cd, Sd = C[dec], S[dec]
+    num_slots = (nump + 1) * cfg.page_size
+    print(f"decode full-size case {cfg.name}: {len(dec)} rows, sum S {int(Sd.sum())}, slots {num_slots}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(1000 + cid)
+    kp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    nk = torch.randn((len(dec), 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    nv = torch.randn((len(dec), 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    out_loc = table[dec, Cd].astype(np.int32)
+    rng = np.random.default_rng(cid)
+    pick = np.sort(rng.choice(len(dec), 16, replace=False))
+    prefix = {}
+    for i in pick:
+        slots = torch.from_numpy(table[dec[i], :Cd[i]].astype(np.int64)).cuda()
+        prefix[i] = (to_host(kp.index_select(0, slots)), to_host(vp.index_select(0, slots)))
+    pkv.store_kv(kp, vp, to_dev(out_loc), nk, nv, page_size=cfg.page_size)
+    o = pkv.paged_attention_decode(to_dev(q, "bf16"), kp, vp, to_dev(table), to_dev(Cd), to_dev(Sd),
+                                   table_idx=to_dev(dec), max_total_kv=int(Sd.sum()), page_size=cfg.page_size)
+    torch.cuda.synchronize()
+    got, hk, hv = to_host(o), to_host(nk), to_host(nv)
+    from oracle.attention import attention_request
+    refs, gots = [], []
+    for i in pick:
+        K = oracle.widen(np.concatenate([prefix[i][0], hk[i:i + 1]]), "bf16")
+        V = oracle.widen(np.concatenate([prefix[i][1], hv[i:i + 1]]), "bf16")
+        refs.append(attention_request(oracle.widen(q[i:i + 1], "bf16"), K, V, int(Cd[i]))[0])
+        gots.append(got[i])
+    mx, rel = check_attention(np.stack(gots), np.stack(refs), "bf16", f"{cfg.name} sampled")
+    print(f"  16 requests: max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0
