@@ -8,11 +8,15 @@
 // through the token-granular page table. GQA: query head h uses KV head
 // h / (HQ / HKV). Scale sm_scale, fp32 online softmax.
 //
-// Work: one workgroup (4 waves) per (request, KV head, pair of query heads
-// sharing it, block of 64 query positions); wave w owns positions
+// Work: one workgroup (8 waves) per (request, KV head, pair of query heads
+// sharing it, block of 128 query positions); wave w owns positions
 // [16w, 16w + 16) of the block for both query heads. Key blocks of 64 are
 // gathered row by row (256 B per head per token) into LDS, so every K/V
-// element fetched from HBM serves 64 positions x 2 heads.
+// element fetched serves 128 positions x 2 heads (256 FLOP per byte).
+// The grid is one-dimensional: the KV head is the fastest index (so with 8
+// KV heads each XCD serves one head), then the query blocks of one request
+// from the longest down, then the request -- so the workgroups that run at
+// the same time on an XCD share one request's K/V rows in its L2.
 //
 // MFMA layout (v_mfma_f32_16x16x32_bf16): the kernel computes S^T = K . Q^T,
 // so each lane's four accumulators belong to ONE query (lane % 16) and four
@@ -56,7 +60,8 @@ struct ExtendArgs {
   uint32_t* faults;
 };
 
-constexpr int kExtBlockQ = 64;   // query positions per workgroup
+constexpr int kExtBlockQ = 128;  // query positions per workgroup
+constexpr int kExtThreads = 512; // 8 waves
 constexpr int kExtBlockK = 64;   // keys per LDS tile
 constexpr int kKPad = 136;       // K tile row: 128 dims + 8 pad (272 B)
 constexpr int kVPad = 72;        // V^T tile row: 64 keys + 8 pad (144 B)
@@ -76,21 +81,24 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // [a.hi,
 }
 
 template <int NH>
-__global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kExtBlockK][kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHeadDim][kVPad];
+__global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
+  // Two tile buffers: tile kb is computed from buffer kb & 1 while tile kb + 1
+  // is written to the other one (one barrier per tile).
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kExtBlockK][kKPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim][kVPad];
   __shared__ int32_t sh_qstart;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;   // MFMA row-in-tile and k-group of this lane
 
-  const int nqb = gridDim.y;
-  const int qb = nqb - 1 - (int)blockIdx.y;   // longest blocks first
-  const int x = blockIdx.x;
-  const int hp = x % a.head_pairs;
-  const int g = (x / a.head_pairs) % a.kv_heads;
-  const int r = x / (a.head_pairs * a.kv_heads);
+  const int nqb = (a.max_extend + kExtBlockQ - 1) / kExtBlockQ;
+  const int id = blockIdx.x;
+  const int g = id % a.kv_heads;
+  const int rest = id / a.kv_heads;
+  const int qb = nqb - 1 - rest % nqb;         // longest blocks of a request first
+  const int hp = (rest / nqb) % a.head_pairs;
+  const int r = rest / (nqb * a.head_pairs);
 
   const int32_t C = a.cached_len[r], S = a.device_len[r];
   const int32_t row = a.table_idx ? a.table_idx[r] : r;
@@ -106,17 +114,18 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
   // Query row offset of this request: sum of the earlier requests' extend lengths.
   {
     int64_t part = 0;
-    for (int i = tid; i < r; i += 256) {
+    for (int i = tid; i < r; i += kExtThreads) {
       const int32_t ci = a.cached_len[i], si = a.device_len[i];
       part += (si > ci) ? (si - ci) : 0;
     }
-    __shared__ int64_t red[4];
+    __shared__ int64_t red[kExtThreads / kWave];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
     if (lane == 0) red[wave] = part;
     __syncthreads();
     if (tid == 0) {
-      const int64_t qs = red[0] + red[1] + red[2] + red[3];
+      int64_t qs = 0;
+      for (int w = 0; w < kExtThreads / kWave; ++w) qs += red[w];
       sh_qstart = (qs + E <= a.total_q) ? (int32_t)qs : -1;
     }
     __syncthreads();
@@ -168,20 +177,28 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
   const int n_keys = C + t_last + 1;
   const int nkb = (n_keys + kExtBlockK - 1) / kExtBlockK;
 
-  // Tile loader: thread -> 4 consecutive keys (kq*4 ..) x 8 dims (dg*8 ..).
+  // Tile loader: thread -> 2 consecutive keys (kq*2 ..) x 8 dims (dg*8 ..).
+  // Page-table entries are fetched one tile ahead of the K/V rows they
+  // address, and K/V rows one tile ahead of their use, so neither latency
+  // sits between two tiles of MFMA work.
   const int kq = tid >> 4, dg = tid & 15;
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int kb) {
+  constexpr int KPT = kExtBlockK * 16 / kExtThreads;  // keys per thread
+  int32_t slot_next[KPT];
+  auto load_slots = [&](int kb) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = kb * kExtBlockK + kq * 4 + e;
-      int32_t slot = -1;
-      if (j < n_keys) {
-        slot = pt[j];
-        if (slot < 0 || (int64_t)slot >= a.num_slots) {
-          raise_fault(a.faults, 0x4u);
-          slot = -1;
-        }
+    for (int e = 0; e < KPT; ++e) {
+      const int j = kb * kExtBlockK + kq * KPT + e;
+      slot_next[e] = (kb < nkb && j < n_keys) ? pt[j] : -1;
+    }
+  };
+  u32x4 kreg[KPT], vreg[KPT];
+  auto load_tile = [&]() {  // rows of the slots in slot_next
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      int32_t slot = slot_next[e];
+      if (slot != -1 && (slot < 0 || (int64_t)slot >= a.num_slots)) {
+        raise_fault(a.faults, 0x4u);
+        slot = -1;
       }
       if (slot >= 0) {
         const int64_t off = (int64_t)slot * a.pool_row + (int64_t)g * kHeadDim + dg * 8;
@@ -193,31 +210,29 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(&Ks[kq * 4 + e][dg * 8]) = kreg[e];
-    const int p0 = vt_pos(kq * 4);
+    for (int e = 0; e < KPT; ++e) *reinterpret_cast<u32x4*>(&Ks[buf][kq * KPT + e][dg * 8]) = kreg[e];
+    static_assert(KPT == 2, "V^T stores pack two keys");
+    const int p0 = vt_pos(kq * 2);  // keys 2m, 2m + 1 sit side by side in a V^T row
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // dims dg*8 + 2w (lo halves) and + 2w + 1 (hi halves)
-      uint2 lo, hi;
-      lo.x = pack_lo(vreg[0][w], vreg[1][w]);
-      lo.y = pack_lo(vreg[2][w], vreg[3][w]);
-      hi.x = pack_hi(vreg[0][w], vreg[1][w]);
-      hi.y = pack_hi(vreg[2][w], vreg[3][w]);
-      *reinterpret_cast<uint2*>(&Vt[dg * 8 + 2 * w][p0]) = lo;
-      *reinterpret_cast<uint2*>(&Vt[dg * 8 + 2 * w + 1][p0]) = hi;
+      *reinterpret_cast<uint32_t*>(&Vt[buf][dg * 8 + 2 * w][p0]) = pack_lo(vreg[0][w], vreg[1][w]);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][dg * 8 + 2 * w + 1][p0]) = pack_hi(vreg[0][w], vreg[1][w]);
     }
   };
 
   const float sc = a.scale_log2;
   const int t_min_wave = qb * kExtBlockQ + wave * 16;
-  load_tile(0);
+  load_slots(0);
+  load_tile();        // tile 0
+  load_slots(1);
+  store_tile(0);
+  load_tile();        // tile 1
+  load_slots(2);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (kb + 1 < nkb) load_tile(kb + 1);  // in flight while this tile is computed
-
+    const int buf = kb & 1;
     // S^T = K . Q^T for 4 key tiles of 16.
     f32x4_v s[NH][4];
 #pragma unroll
@@ -229,7 +244,7 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_v ka =
-            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Ks[kt * 16 + lq][ks * 32 + lg * 8]));
+            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Ks[buf][kt * 16 + lq][ks * 32 + lg * 8]));
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
           s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
@@ -282,11 +297,20 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendArgs a) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const bf16x8_v va =
-            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Vt[dt * 16 + lq][k2 * 32 + lg * 8]));
+            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Vt[buf][dt * 16 + lq][k2 * 32 + lg * 8]));
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
           oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
       }
+
+    // Tile kb + 1 (loaded during this tile) into the other buffer; rows of
+    // tile kb + 2 and the slots of tile kb + 3 go out.
+    if (kb + 1 < nkb) {
+      store_tile(buf ^ 1);
+      load_tile();
+      load_slots(kb + 3);
+    }
+    __syncthreads();
   }
 
   // Normalise and write: lane holds dims dt*16 + 4*lg + i of query t.

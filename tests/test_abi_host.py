@@ -182,7 +182,7 @@ def _extend(L, pool, bs=2, hq=16, q=0x60000, o=0x70000, pt=0x80000, cl=0x88000, 
 @pytest.mark.parametrize("pool,kw,status", [
     (dict(dtype=0), {}, -2), (dict(), dict(hq=12), -3), (dict(), dict(q=None), -1), (dict(), dict(o=0x70002), -5),
     (dict(), dict(cl=None), -1), (dict(), dict(max_e=0), -4), (dict(), dict(rows=0), -3),
-    (dict(), dict(max_e=64 * 65536), -3),
+    (dict(), dict(bs=1 << 28, max_e=8), -3),
 ])
 def test_extend_argument_errors(L, pool, kw, status):
     assert _extend(L, _pool(**pool), **kw) == status
