@@ -24,6 +24,7 @@ Prints ONE JSON line (see the keys below).
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,7 +46,53 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3])
     ap.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--skip-extend", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="before warm-up, run plain 1 GiB device copies (untimed) whose counter "
+                         "readings calibrate FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode256_traffic.md")
+DECODE_SOURCES = ["paged_kv_attention_scatter_amd/csrc/decode.hpp", "paged_kv_attention_scatter_amd/csrc/pkv.hip",
+                  "paged_kv_attention_scatter_amd/csrc/common.hpp"]
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when that summary was taken on a different version of the decode sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    src = re.search(r"^decode_source_hash:\s*(\S+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_call:\s*(\d+)", text, re.M)
+    if not src or not val or src.group(1) != decode_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def copy_calibration(torch, dev):
+    """Plain device copies of known size (1 GiB read + 1 GiB written each):
+    the blit behind Tensor.copy_ and an elementwise kernel."""
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x (copy_ + neg) of {n * 2} bytes")
+    del src, dst
 
 
 def log(msg):
@@ -68,6 +115,8 @@ def main():
     cfg = config(args.config)
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 + cfg.cid)
+    if args.copy_calib:
+        copy_calibration(torch, dev)
 
     # ---------------------------------------------------------------- pool sized for 28 layers
     free, total = torch.cuda.mem_get_info()
@@ -174,7 +223,7 @@ def main():
                    "bs": bs, "sum_device_len": total_kv, "num_pages": num_pages, "page_size": 1},
         "roofline": {"bound": "hbm", "kernel": "decode attention (split-K + combine, one call)",
                      "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": kv_bytes, "avg_launch_us": round(decode_ms * 1e3, 2),
                      "p10_p50_p90_us": [round(x * 1e3, 2) for x in decode_p]},
         "components": {
