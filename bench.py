@@ -158,7 +158,7 @@ def main():
     d_P = None if P is None else torch.from_numpy(P).to(dev)
     d_u = torch.from_numpy(draw_uniforms(cfg)).to(dev)
     tokens = torch.empty(bs, dtype=torch.int32, device=dev)
-    s_ws = torch.empty(pkv.sample_workspace_size(bs, cfg.vocab), dtype=torch.uint8, device=dev)
+    s_ws = pkv.sample_workspace(bs, cfg.vocab, dev)
 
     def step(i):
         layer = i % LAYERS_FILLED

@@ -195,10 +195,14 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  * whose running kept mass exceeds u * (total kept mass) (the last kept token
  * if rounding finds none).
  *   ws        device workspace of pkv_sample_workspace_size(bs, vocab) bytes,
- *             16-byte aligned; required for bf16 logits (per-slice records and
- *             window lists), unused for fp32. PKV_ERR_WORKSPACE if missing or
- *             short, PKV_ERR_ALIGN if misaligned. vocab is limited to 2^21
- *             (bf16) / 2^20 (fp32) tokens (PKV_ERR_SHAPE above).
+ *             16-byte aligned; required for bf16 logits (per-slice records,
+ *             sub-slice masses and key histograms, written by the first of the
+ *             two kernels and read by the second), unused for fp32. Its
+ *             contents need no initialisation and are not kept between
+ *             calls; calls that share a workspace must not overlap in time
+ *             (different streams race). PKV_ERR_WORKSPACE if missing or
+ *             short, PKV_ERR_ALIGN if misaligned. vocab is limited to 2^20
+ *             tokens (PKV_ERR_SHAPE above).
  */
 int pkv_sample(const void* logits, int32_t logits_dtype, int32_t bs, int32_t vocab,
                int64_t row_stride, const float* temperature, const int32_t* top_k,

@@ -15,11 +15,11 @@ Build the library with ``python -m paged_kv_attention_scatter_amd.build``.
 
 from .api import (HEAD_DIM, decode_workspace_size, extend_workspace_size, make_pool, num_pages,
                   paged_attention_decode, paged_attention_extend, prepare_sampling, read_faults,
-                  sample, sample_workspace_size, store_kv, version)
+                  sample, sample_workspace, sample_workspace_size, store_kv, version)
 from ._lib import LIB_PATH, PkvError, lib
 
 __all__ = [
     "HEAD_DIM", "LIB_PATH", "PkvError", "lib", "make_pool", "store_kv", "paged_attention_decode",
     "paged_attention_extend", "sample", "num_pages", "prepare_sampling", "read_faults",
-    "decode_workspace_size", "extend_workspace_size", "sample_workspace_size", "version",
+    "decode_workspace_size", "extend_workspace_size", "sample_workspace", "sample_workspace_size", "version",
 ]

@@ -184,6 +184,12 @@ def sample_workspace_size(bs: int, vocab: int) -> int:
     return int(lib().pkv_sample_workspace_size(bs, vocab))
 
 
+def sample_workspace(bs: int, vocab: int, device):
+    """A sampler workspace for calls of at most bs rows over this vocabulary."""
+    torch = _torch()
+    return torch.empty(max(1, sample_workspace_size(bs, vocab)), dtype=torch.uint8, device=device)
+
+
 def sample(logits, temperature=None, top_k=None, top_p=None, uniforms=None, *, out=None, workspace=None,
            stream=None):
     """One token per row (pkv_sample). temperature None = all-greedy batch."""

@@ -183,6 +183,12 @@ PKV_INLINE uint32_t bf16x2_keys(uint32_t w) {
   const uint32_t x = w ^ (sg | 0x80008000u);     // positive: b | 0x8000; negative: 0x7fff - |b|
   return as_u32(as_u16x2(x) - as_u16x2(sg));      // negative halves + 1
 }
+// The inverse: two biased keys -> the two bf16 values (-0 comes back as +0).
+PKV_INLINE uint32_t bf16x2_from_keys(uint32_t k) {
+  const i16x2 sgn = __builtin_bit_cast(i16x2, k ^ 0x80008000u) >> (int16_t)15;  // 0xffff where key < 0x8000
+  const uint32_t sg = __builtin_bit_cast(uint32_t, sgn);
+  return as_u32(as_u16x2(k ^ (sg | 0x80008000u)) - as_u16x2(sg));
+}
 // The bf16 value of a biased key.
 PKV_INLINE float key16_value(uint32_t k) {
   const uint32_t b = k >= 0x8000u ? (k - 0x8000u) : (0x8000u | (0x8000u - k));
@@ -191,17 +197,18 @@ PKV_INLINE float key16_value(uint32_t k) {
 
 // ---------------------------------------------------------------- shared state
 
+template <int NW>
 struct SampleLds {
-  float gsum[kSampleWaves * kSampleMaxRounds];  // memory passes: group masses, group = (wave, round)
+  float gsum[NW * kSampleMaxRounds];  // memory passes: group masses, group = (wave, round)
   uint32_t hist[256];    // window counts
   float wtab[256];       // weight of the key d below the maximum
   uint32_t rcnt[256];    // radix descent: digit counts
   double rmass[256];     //                digit masses
-  int32_t seg_n[kSampleWaves];
-  double wave_f[kSampleWaves];
-  int32_t wave_i[kSampleWaves];
-  int32_t wave_j[kSampleWaves];
-  double scan_f[kSampleWaves];
+  int32_t seg_n[NW];
+  double wave_f[NW];
+  int32_t wave_i[NW];
+  int32_t wave_j[NW];
+  double scan_f[NW];
   int32_t pick_bin;
   uint32_t pick_cnt;
   double pick_above;
@@ -209,37 +216,40 @@ struct SampleLds {
 };
 
 // Block-wide reductions, returned in every thread; they start and end with a barrier.
-PKV_INLINE double block_sum_f64(SampleLds& s, double v) {
+template <int NW>
+PKV_INLINE double block_sum_f64(SampleLds<NW>& s, double v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum_f64(v);
   __syncthreads();
   if (lane == 0) s.wave_f[wave] = v;
   __syncthreads();
   double t = 0.0;
-  for (int w = 0; w < kSampleWaves; ++w) t += s.wave_f[w];
+  for (int w = 0; w < NW; ++w) t += s.wave_f[w];
   __syncthreads();
   return t;
 }
-PKV_INLINE int32_t block_reduce_i32(SampleLds& s, int32_t v, bool want_max) {
+template <int NW>
+PKV_INLINE int32_t block_reduce_i32(SampleLds<NW>& s, int32_t v, bool want_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = want_max ? wave_max_i32(v) : wave_min_i32(v);
   __syncthreads();
   if (lane == 0) s.wave_j[wave] = v;
   __syncthreads();
   int32_t t = s.wave_j[0];
-  for (int w = 1; w < kSampleWaves; ++w) t = want_max ? max(t, s.wave_j[w]) : min(t, s.wave_j[w]);
+  for (int w = 1; w < NW; ++w) t = want_max ? max(t, s.wave_j[w]) : min(t, s.wave_j[w]);
   __syncthreads();
   return t;
 }
 // Exclusive block scans in thread order; *total = the sum over the block.
-PKV_INLINE int32_t block_excl_scan_i32(SampleLds& s, int32_t v, int32_t* total) {
+template <int NW>
+PKV_INLINE int32_t block_excl_scan_i32(SampleLds<NW>& s, int32_t v, int32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t incl = wave_incl_scan_i32(v, lane);
   __syncthreads();
   if (lane == 63) s.wave_j[wave] = incl;
   __syncthreads();
   int32_t off = 0, tot = 0;
-  for (int w = 0; w < kSampleWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) off += s.wave_j[w];
     tot += s.wave_j[w];
   }
@@ -249,7 +259,8 @@ PKV_INLINE int32_t block_excl_scan_i32(SampleLds& s, int32_t v, int32_t* total) 
 }
 // Returns the exclusive prefix; *incl_out = the inclusive one (equal to the
 // next thread's exclusive prefix, bit for bit).
-PKV_INLINE double block_scan_f64(SampleLds& s, double v, double* incl_out, double* total) {
+template <int NW>
+PKV_INLINE double block_scan_f64(SampleLds<NW>& s, double v, double* incl_out, double* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double excl;
   const double incl = wave_scan_f64(v, lane, &excl);
@@ -257,7 +268,7 @@ PKV_INLINE double block_scan_f64(SampleLds& s, double v, double* incl_out, doubl
   if (lane == 63) s.scan_f[wave] = incl;
   __syncthreads();
   double off = 0.0, tot = 0.0;
-  for (int w = 0; w < kSampleWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) off += s.scan_f[w];
     tot += s.scan_f[w];
   }
@@ -270,8 +281,8 @@ PKV_INLINE double block_scan_f64(SampleLds& s, double v, double* incl_out, doubl
 // Scan over 256 bins in ascending order by the first four waves (one bin per
 // thread): every thread gets the first bin whose inclusive running amount
 // reaches `goal` (-1 if none), the amount strictly before it and count(bin).
-template <class AF, class CF>
-PKV_INLINE void window_select(SampleLds& s, AF amount, CF count, double goal, int* bin, double* before,
+template <int NW, class AF, class CF>
+PKV_INLINE void window_select(SampleLds<NW>& s, AF amount, CF count, double goal, int* bin, double* before,
                               uint32_t* cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __syncthreads();
@@ -302,7 +313,7 @@ PKV_INLINE void window_select(SampleLds& s, AF amount, CF count, double goal, in
 
 // ---------------------------------------------------------------- the row in memory
 
-template <typename T>
+template <typename T, int NW>
 struct SampleRow {
   using E = SampleElem<T>;
   static constexpr int EPC = E::kPerChunk;
@@ -313,7 +324,7 @@ struct SampleRow {
     base = b;
     V = vocab;
     nchunks = (vocab + EPC - 1) / EPC;
-    cpw = (nchunks + kSampleWaves - 1) / kSampleWaves;
+    cpw = (nchunks + NW - 1) / NW;
     rounds = (cpw + kWave - 1) / kWave;
     wave = w;
     lane = l;
@@ -352,8 +363,8 @@ struct SampleRow {
 PKV_INLINE float row_weight(float l, float lmax, float c2) { return fast_exp2((l - lmax) * c2); }
 
 // Block sum of v(i, l) over the row.
-template <class RowT, class VF>
-PKV_INLINE double row_sum(const RowT& row, SampleLds& s, VF v) {
+template <class RowT, int NW, class VF>
+PKV_INLINE double row_sum(const RowT& row, SampleLds<NW>& s, VF v) {
   double t = 0.0;
   row.for_rounds([&](int c, const u32x4& x, bool ok) {
     float cs = 0.f;
@@ -367,8 +378,8 @@ PKV_INLINE double row_sum(const RowT& row, SampleLds& s, VF v) {
 // exceeds target_of(total); if none, the last element with v > 0 (-1 if no
 // element has v > 0). Group masses are stored per (wave, round); wave 0
 // locates the group, the group's wave scans its one chunk round.
-template <class RowT, class VF, class TF>
-PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_of) {
+template <class RowT, int NW, class VF, class TF>
+PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds<NW>& s, VF v, TF target_of) {
   const int wave = row.wave, lane = row.lane, R = row.rounds;
   int32_t tlast = -1;
   __syncthreads();
@@ -388,7 +399,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
   __syncthreads();
   if (wave == 0) {
     // groups in index order: g = wave * R + round; each lane takes a contiguous run
-    const int G = kSampleWaves * R, per = (G + kWave - 1) / kWave;
+    const int G = NW * R, per = (G + kWave - 1) / kWave;
     const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
     double own = 0.0;
     for (int g = g0; g < g1; ++g) own += (double)s.gsum[g];
@@ -416,7 +427,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
   const int gstar = s.pick_bin;
   const double rem = s.pick_above;
   int32_t last = -1;
-  for (int w = 0; w < kSampleWaves; ++w) last = max(last, s.wave_i[w]);
+  for (int w = 0; w < NW; ++w) last = max(last, s.wave_i[w]);
   if (gstar >= 0 && wave == gstar / R) {
     const int c = gstar % R;
     const u32x4 x = row.fetch(c);
@@ -459,8 +470,8 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds& s, VF v, TF target_
 // < goal <= that plus the group's mass (the lowest group if rounding never
 // reaches goal). Returns the key; *above = count or mass strictly above it,
 // *eq = the group's count.
-template <class RowT, class PF, class WF>
-PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds& s, PF pred, WF weight, bool by_mass, double goal,
+template <class RowT, int NW, class PF, class WF>
+PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds<NW>& s, PF pred, WF weight, bool by_mass, double goal,
                                   double* above_out, uint32_t* eq_out) {
   using E = typename RowT::E;
   uint32_t prefix = 0, mask = 0;
@@ -468,7 +479,7 @@ PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds& s, PF pred, WF wei
   uint32_t eq = 0;
   for (int shift = E::kKeyBits - 8; shift >= 0; shift -= 8) {
     __syncthreads();
-    for (int b = threadIdx.x; b < 256; b += kSampleThreads) {
+    for (int b = threadIdx.x; b < 256; b += NW * kWave) {
       s.rcnt[b] = 0;
       s.rmass[b] = 0.0;
     }
@@ -541,8 +552,8 @@ struct SampleParams {
 // Cuts and draw over the row in memory (any cut depth, any number of kept
 // tokens): radix descents for the top-k threshold and the top-p cut,
 // group-mass scans for the ties at each cut and for the draw.
-template <class RowT>
-PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds& s, const SampleParams& sp, float lmax) {
+template <class RowT, int NW>
+PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const SampleParams& sp, float lmax) {
   using E = typename RowT::E;
   const float c2 = sp.c2;
   auto wt = [&](float l) { return row_weight(l, lmax, c2); };
@@ -608,12 +619,12 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds& s, const SamplePar
 
 template <typename T>
 __global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a) {
-  __shared__ SampleLds s;
+  __shared__ SampleLds<kSampleWaves> s;
   const int row_id = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row_id, a.vocab);
-  SampleRow<T> row;
+  SampleRow<T, kSampleWaves> row;
   row.init(reinterpret_cast<const T*>(a.logits) + (int64_t)row_id * a.row_stride, a.vocab, wave, lane);
 
   // maximum and the first index of it (-0 == +0 compare equal)
@@ -648,244 +659,64 @@ __global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a
 
 // ---------------------------------------------------------------- bf16: slice kernel + finish kernel
 
-constexpr int kSliceThreads = 256;
-constexpr int kSliceRounds = 4;                                 // 16-byte chunks per thread
-constexpr int kSliceTokens = kSliceThreads * kSliceRounds * 8;  // 8192 tokens per slice
-constexpr int kSliceCap = 1024;                                 // window tokens a slice can hand over
-constexpr int kFinishCap = 8192;                                // window tokens a row can hold in LDS
-
-// What a slice hands to the finish kernel.
-struct SliceRec {
-  int32_t kmax;     // largest biased key of the slice
-  int32_t argmax;   // first row index holding it
-  int32_t count;    // tokens within the window of the slice maximum (may exceed kSliceCap)
-  int32_t pad;
-  double mass;      // sum of exp2((l - l_slice_max) * c2) over the slice (rows that need it)
-};
+constexpr int kSliceThreads = 256;                                // 4 waves: many workgroups per CU
+constexpr int kSliceWaves = kSliceThreads / kWave;
+constexpr int kSliceRounds = 4;                                   // 16-byte chunks per thread
+constexpr int kSliceTokens = kSliceThreads * kSliceRounds * 8;    // 8192 tokens per slice
+constexpr int kHistBins = 256;      // window: keys within 255 of a maximum
+constexpr int kHistWords = kHistBins / 2;                         // 16-bit counts, two per word
+constexpr int kHistUnits = kHistBins / 8;                         // 16-byte units of a histogram
+constexpr int kMaxSlices = 128;     // slices per row (2^20 tokens)
+constexpr int kFinishThreads = 512;
+constexpr int kFinishWaves = kFinishThreads / kWave;
+constexpr int kDrawChunks = kSliceTokens / (8 * kFinishThreads);  // 2: 16 tokens per finishing thread
 
 __host__ __device__ inline int sample_slices(int V) { return (V + kSliceTokens - 1) / kSliceTokens; }
+static_assert((int64_t)kMaxSlices * kSliceTokens <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves * 8,
+              "the generic path covers every row the slices cover");
+static_assert(kMaxSlices <= kFinishThreads, "one slice per finishing thread");
 
-// Slice kernel: workgroup b handles slice b % S of row b / S. It reads its
-// 8192 tokens once (thread t holds chunks t, t + 256, t + 512, t + 768, so
-// index order within the slice is (round, thread, token)), turns them into
-// biased 16-bit keys, and writes its maximum, the first index of it, its
-// mass (rows whose draw or top-p runs over the whole row) and, in index
-// order, every token within kSampleWindow keys of its maximum as
-// (row index, key). The window of the row maximum is inside the union of
-// these windows, since no slice maximum exceeds the row maximum. A handed-over
-// token is one word: (offset in the slice) << 16 | key; the list is built in
-// LDS and written out with 16-byte stores.
-__global__ void __launch_bounds__(kSliceThreads, 8) sample_slice_kernel(SampleArgs a, SliceRec* recs,
-                                                                        uint32_t* ents) {
-  constexpr int W = kSampleWindow;
-  __shared__ uint32_t sh_u[kSliceThreads / kWave];
-  __shared__ int32_t sh_i[kSliceThreads / kWave];
-  __shared__ double sh_d[kSliceThreads / kWave];
-  __shared__ uint32_t sh_sc[2][kSliceThreads / kWave];
-  __shared__ __attribute__((aligned(16))) uint32_t sh_list[kSliceCap];
-  const int V = a.vocab, S = sample_slices(V);
-  const int row = blockIdx.x / S, slice = blockIdx.x % S;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  SampleParams sp;
-  sp.load(a, row, V);
-  const bool need_mass = !sp.greedy && !sp.use_k;            // plain rows and top-p over the whole row
-  const bool need_list = !sp.greedy && (sp.use_k || sp.use_p);
-  const int t0 = slice * kSliceTokens;
-  const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
-                                                     (int64_t)row * a.row_stride);
-  const int last_chunk = (V - 1) / 8;
+// What the slices leave for the finish kernel.
+struct SampleWs {
+  uint64_t* recs;      // [bs * S]: slice maximum key | first index of it << 32
+  double* masses;      // [bs * S]: slice mass relative to the slice maximum
+  uint32_t* hists;     // [bs * S * kHistWords]: slice window histograms (16-bit counts)
+};
 
-  // Load (indices clamped to the row's last chunk: every read stays inside
-  // the row), then mask the tokens at or past V to -inf. Only the raw words
-  // stay in registers; keys are recomputed where needed (three ops a pair).
-  u32x4 raw[kSliceRounds];
-#pragma unroll
-  for (int i = 0; i < kSliceRounds; ++i) {
-    const int ch = t0 / 8 + i * kSliceThreads + tid;
-    raw[i] = __builtin_nontemporal_load(crow + min(ch, last_chunk));
-  }
-  u16x2 mx = {0, 0};
-#pragma unroll
-  for (int i = 0; i < kSliceRounds; ++i) {
-    const int tok = t0 + 8 * (i * kSliceThreads + tid);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w = raw[i][j];
-      if (tok + 2 * j >= V) w = 0xff80ff80u;
-      else if (tok + 2 * j + 1 >= V) w = (w & 0xffffu) | 0xff800000u;
-      raw[i][j] = w;
-      mx = __builtin_elementwise_max(mx, as_u16x2(bf16x2_keys(w)));
-    }
-  }
-  const uint32_t tk = max((uint32_t)mx.x, (uint32_t)mx.y);
-  // mass relative to this thread's maximum (rescaled to the slice maximum below)
-  double mass = 0.0;
-  if (need_mass) {
-    const float c2 = sp.c2, off = -fmaxf(key16_value(tk), -1e30f) * c2;
-#pragma unroll
-    for (int i = 0; i < kSliceRounds; ++i) {
-      float cs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        cs += fast_exp2(fmaf(__uint_as_float(raw[i][j] << 16), c2, off));
-        cs += fast_exp2(fmaf(__uint_as_float(raw[i][j] & 0xffff0000u), c2, off));
-      }
-      mass += (double)cs;
-    }
-  }
-  // slice maximum
-  const uint32_t wk = (uint32_t)wave_max_i32((int32_t)tk);
-  if (lane == 0) sh_u[wave] = wk;
-  __syncthreads();
-  uint32_t kmax = sh_u[0];
-#pragma unroll
-  for (int w = 1; w < kSliceThreads / kWave; ++w) kmax = max(kmax, sh_u[w]);
-  if (need_mass) {
-    mass = wave_sum_f64(mass * (double)fast_exp2((fmaxf(key16_value(tk), -1e30f) -
-                                                   fmaxf(key16_value(kmax), -1e30f)) * sp.c2));
-    if (lane == 0) sh_d[wave] = mass;
-  }
-  // first index holding it
-  int32_t found = 0x7fffffff;
-  if (tk == kmax) {
-#pragma unroll
-    for (int i = kSliceRounds - 1; i >= 0; --i)
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        const int tok = t0 + 8 * (i * kSliceThreads + tid) + 2 * j;
-        const uint32_t k = bf16x2_keys(raw[i][j]);
-        if ((k >> 16) == kmax) found = tok + 1;
-        if ((k & 0xffffu) == kmax) found = tok;
-      }
-  }
-  found = wave_min_i32(found);
-  if (lane == 0) sh_i[wave] = found;
-  // window tokens: key > th, i.e. the saturated key - th is nonzero
-  int32_t count = 0;
-  if (need_list) {
-    const uint32_t th = kmax > (uint32_t)W ? kmax - (uint32_t)W : 0u;
-    const u16x2 thpk = as_u16x2(th * 0x10001u);
-    uint32_t n[kSliceRounds];
-#pragma unroll
-    for (int i = 0; i < kSliceRounds; ++i) {
-      n[i] = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u16x2 sv = __builtin_elementwise_sub_sat(as_u16x2(bf16x2_keys(raw[i][j])), thpk);
-        n[i] += (sv.x != 0) + (sv.y != 0);
-      }
-    }
-    // positions in (round, thread) order: two 16-bit-lane scans over the block
-    const uint32_t p01 = n[0] | (n[1] << 16), p23 = n[2] | (n[3] << 16);
-    const uint32_t i01 = (uint32_t)wave_incl_scan_i32((int32_t)p01, lane);
-    const uint32_t i23 = (uint32_t)wave_incl_scan_i32((int32_t)p23, lane);
-    if (lane == 63) {
-      sh_sc[0][wave] = i01;
-      sh_sc[1][wave] = i23;
-    }
-    __syncthreads();
-    uint32_t o01 = 0, o23 = 0, t01 = 0, t23 = 0;
-#pragma unroll
-    for (int w = 0; w < kSliceThreads / kWave; ++w) {
-      if (w < wave) {
-        o01 += sh_sc[0][w];
-        o23 += sh_sc[1][w];
-      }
-      t01 += sh_sc[0][w];
-      t23 += sh_sc[1][w];
-    }
-    const uint32_t e01 = o01 + i01 - p01, e23 = o23 + i23 - p23;  // exclusive, per 16-bit lane
-    const uint32_t tot[4] = {t01 & 0xffffu, t01 >> 16, t23 & 0xffffu, t23 >> 16};
-    uint32_t pos[4] = {e01 & 0xffffu, (e01 >> 16) + tot[0], (e23 & 0xffffu) + tot[0] + tot[1],
-                       (e23 >> 16) + tot[0] + tot[1] + tot[2]};
-    count = (int32_t)(tot[0] + tot[1] + tot[2] + tot[3]);
-#pragma unroll
-    for (int i = 0; i < kSliceRounds; ++i) {
-      if (n[i]) {
-        const uint32_t off = 8 * (i * kSliceThreads + tid);  // token offset within the slice
-        uint32_t p = pos[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t kw = bf16x2_keys(raw[i][j]);
-            const uint32_t k = h ? (kw >> 16) : (kw & 0xffffu);
-            if (k > th) {
-              if (p < (uint32_t)kSliceCap) sh_list[p] = ((off + 2 * j + h) << 16) | k;
-              ++p;
-            }
-          }
-      }
-    }
-    __syncthreads();
-    const int nw = (min(count, kSliceCap) + 3) / 4;  // 16-byte stores
-    u32x4* out = reinterpret_cast<u32x4*>(ents + (int64_t)blockIdx.x * kSliceCap);
-    for (int q = tid; q < nw; q += kSliceThreads) out[q] = reinterpret_cast<const u32x4*>(sh_list)[q];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    SliceRec r;
-    r.kmax = (int32_t)kmax;
-    int32_t am = sh_i[0];
-    for (int w = 1; w < kSliceThreads / kWave; ++w) am = min(am, sh_i[w]);
-    r.argmax = am;
-    r.count = count;
-    r.pad = 0;
-    double m = 0.0;
-    if (need_mass)
-      for (int w = 0; w < kSliceThreads / kWave; ++w) m += sh_d[w];
-    r.mass = m;
-    recs[blockIdx.x] = r;
-  }
-}
-
-// Exclusive block scan of v (thread order) that also returns the block
-// maximum of m, with the same three barriers; *incl_out equals the next
-// thread's exclusive prefix bit for bit.
-PKV_INLINE double block_scan_f64_max(SampleLds& s, double v, int32_t m, double* incl_out, double* total,
-                                     int32_t* mmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double excl;
-  const double incl = wave_scan_f64(v, lane, &excl);
-  m = wave_max_i32(m);
-  __syncthreads();
-  if (lane == 63) {
-    s.scan_f[wave] = incl;
-    s.wave_j[wave] = m;
-  }
-  __syncthreads();
-  double off = 0.0, tot = 0.0;
-  int32_t mx = s.wave_j[0];
-  for (int w = 0; w < kSampleWaves; ++w) {
-    if (w < wave) off += s.scan_f[w];
-    tot += s.scan_f[w];
-    mx = max(mx, s.wave_j[w]);
-  }
-  __syncthreads();
-  *total = tot;
-  *mmax = mx;
-  *incl_out = off + incl;
-  return off + excl;
-}
-
-// First of W <= 128 bins (ascending) whose running amount reaches goal, by
-// one wave (two bins per lane): *bin = -1 if none, *before = the amount
-// strictly before it, *cnt = count(bin). No barriers.
-template <class AF, class CF>
-PKV_INLINE void wave_select128(AF amount, CF count, double goal, int* bin, double* before, uint32_t* cnt) {
+// First of NB bins (ascending) whose running amount reaches goal, by one
+// wave (NB / 64 consecutive bins per lane): *bin = -1 if none, *before = the
+// amount strictly before it, *cnt = count(bin). No barriers.
+template <int NB, class AF, class CF>
+PKV_INLINE void wave_select_bins(AF amount, CF count, double goal, int* bin, double* before, uint32_t* cnt) {
+  constexpr int P = NB / kWave;
   const int lane = threadIdx.x & 63;
-  const double a0 = amount(2 * lane), a1 = amount(2 * lane + 1);
+  double a[P], sum = 0.0;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    a[e] = amount(P * lane + e);
+    sum += a[e];
+  }
   double excl;
-  const double incl = wave_scan_f64(a0 + a1, lane, &excl);
+  const double incl = wave_scan_f64(sum, lane, &excl);
   int b = -1;
   double bef = 0.0;
-  if (a0 + a1 > 0.0 && excl < goal && goal <= incl) {  // at most one lane
-    if (a0 > 0.0 && goal <= excl + a0) {
-      b = 2 * lane;
-      bef = excl;
-    } else {
-      b = 2 * lane + 1;
-      bef = excl + a0;
+  if (sum > 0.0 && excl < goal && goal <= incl) {  // at most one lane: the lanes' intervals meet exactly
+    double run = excl, lastbef = 0.0;
+    int lastb = -1;
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+      if (a[e] > 0.0) {
+        if (b < 0 && goal <= run + a[e]) {
+          b = P * lane + e;
+          bef = run;
+        }
+        lastb = P * lane + e;
+        lastbef = run;
+        run += a[e];
+      }
+    if (b < 0) {  // rounding inside the lane: its last non-empty bin
+      b = lastb;
+      bef = lastbef;
     }
   }
   const uint64_t who = __ballot(b >= 0);
@@ -902,341 +733,426 @@ PKV_INLINE void wave_select128(AF amount, CF count, double goal, int* bin, doubl
   *cnt = (uint32_t)__shfl((int32_t)c, l0, 64);
 }
 
-// Finish kernel: one workgroup per row merges the slices' results.
-__global__ void __launch_bounds__(kSampleThreads) sample_finish_kernel(SampleArgs a, const SliceRec* recs,
-                                                                       const uint32_t* ents) {
-  constexpr int W = kSampleWindow;
-  static_assert(W <= 128, "wave_select128 covers 128 bins");
-  __shared__ SampleLds s;
-  __shared__ int32_t f_idx[kFinishCap];
-  __shared__ uint8_t f_d[kFinishCap];
-  __shared__ int32_t f_cnt[256 + 1];
+// Slice kernel: workgroup b reads slice b / bs of row b % bs (rows vary
+// fastest, so greedy and sampled rows share every CU). Thread t holds
+// chunks t, t + 256, t + 512, t + 768 of the slice. The tokens become biased
+// 16-bit keys; the slice writes its maximum and the first index of it, its
+// mass relative to its maximum (rows without top-k) and a count histogram of
+// the keys within 255 of its maximum (bin d = kmax - key; rows with top-k or
+// top-p).
+__global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs a, SampleWs ws) {
+  __shared__ uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
+  __shared__ double wmass[kSliceWaves];
+  __shared__ uint32_t wave_k[kSliceWaves];
+  __shared__ int32_t wave_i[kSliceWaves];
+  const int V = a.vocab, S = sample_slices(V);
+  const int row = blockIdx.x % a.bs, slice = blockIdx.x / a.bs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  SampleParams sp;
+  sp.load(a, row, V);
+  const bool need_mass = !sp.greedy && !sp.use_k;
+  const bool need_hist = !sp.greedy && (sp.use_k || sp.use_p);
+  const bool tail = slice == S - 1;  // the only slice with tokens at or past V
+  const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
+                                                     (int64_t)row * a.row_stride);
+  const int last_chunk = (V - 1) / 8;
+  const int t0s = slice * kSliceTokens;
+  u32x4 key[kSliceRounds];
+#pragma unroll
+  for (int i = 0; i < kSliceRounds; ++i)  // indices clamped to the row's last chunk: reads stay in the row
+    key[i] = __builtin_nontemporal_load(crow + min(t0s / 8 + i * kSliceThreads + tid, last_chunk));
+  if (need_hist)  // ordered before the atomics by the barrier of the block maximum
+    for (int b = tid; b < kHistBins + kWave; b += kSliceThreads) hist[b] = 0;
+  // Biased keys; a token at or past V gets key 0, below every real key, so
+  // it never wins the maximum and never enters a window.
+  // (The checks against V run in the tail slice only: a uniform branch.)
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < kSliceRounds; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t k = bf16x2_keys(key[i][j]);
+        const int tok = t0s + 8 * (i * kSliceThreads + tid) + 2 * j;
+        if (tok >= V) k = 0u;
+        else if (tok + 1 >= V) k &= 0xffffu;
+        key[i][j] = k;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSliceRounds; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[i][j] = bf16x2_keys(key[i][j]);
+  }
+  u16x2 mx = {0, 0};
+#pragma unroll
+  for (int i = 0; i < kSliceRounds; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, as_u16x2(key[i][j]));
+  const uint32_t tk = max((uint32_t)mx.x, (uint32_t)mx.y);
+  // mass relative to this thread's maximum (rescaled below): fp32 within a
+  // chunk, fp64 above
+  double mass = 0.0;
+  if (need_mass) {
+    const float c2 = sp.c2, off = -fmaxf(key16_value(tk), -1e30f) * c2;
+    auto chunk_mass = [&](const u32x4& k, bool masked) {
+      float cs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = bf16x2_from_keys(k[j]);
+        float w0 = fast_exp2(fmaf(__uint_as_float(w << 16), c2, off));
+        float w1 = fast_exp2(fmaf(__uint_as_float(w & 0xffff0000u), c2, off));
+        if (masked) {  // key 0: no token
+          if ((k[j] & 0xffffu) == 0u) w0 = 0.f;
+          if ((k[j] >> 16) == 0u) w1 = 0.f;
+        }
+        cs += w0;
+        cs += w1;
+      }
+      return cs;
+    };
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(key[i], true);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(key[i], false);
+    }
+  }
+  const uint32_t wk = (uint32_t)wave_max_i32((int32_t)tk);
+  if (lane == 0) wave_k[wave] = wk;
+  __syncthreads();
+  uint32_t kmax = wave_k[0];
+#pragma unroll
+  for (int w = 1; w < kSliceWaves; ++w) kmax = max(kmax, wave_k[w]);
+  if (need_mass) {
+    const double sc = (double)fast_exp2((fmaxf(key16_value(tk), -1e30f) - fmaxf(key16_value(kmax), -1e30f)) * sp.c2);
+    const double m = wave_sum_f64(mass * sc);
+    if (lane == 0) wmass[wave] = m;
+  }
+  // first index holding the maximum
+  int32_t found = 0x7fffffff;
+  if (tk == kmax) {
+#pragma unroll
+    for (int i = kSliceRounds - 1; i >= 0; --i)
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const int tok = t0s + 8 * (i * kSliceThreads + tid) + 2 * j;
+        if ((key[i][j] >> 16) == kmax) found = tok + 1;
+        if ((key[i][j] & 0xffffu) == kmax) found = tok;
+      }
+  }
+  found = wave_min_i32(found);
+  if (lane == 0) wave_i[wave] = found;
+  // window histogram (keys > th, bin d = kmax - key); a token outside the
+  // window goes to this lane's discard bin, so no lane ever branches
+  if (need_hist) {
+    const uint32_t th = kmax > (uint32_t)kHistBins ? kmax - (uint32_t)kHistBins : 0u;
+    const uint32_t discard = kHistBins + lane;
+#pragma unroll
+    for (int i = 0; i < kSliceRounds; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = key[i][j] & 0xffffu, hi = key[i][j] >> 16;
+        atomicAdd(&hist[lo > th ? kmax - lo : discard], 1u);
+        atomicAdd(&hist[hi > th ? kmax - hi : discard], 1u);
+      }
+  }
+  __syncthreads();
+  const int64_t slot = (int64_t)row * S + slice;  // the row's slices in index order
+  if (need_hist && tid < kHistWords)  // counts <= 8192 fit 16 bits
+    ws.hists[slot * kHistWords + tid] = hist[2 * tid] | (hist[2 * tid + 1] << 16);
+  if (tid == 0) {
+    int32_t am = wave_i[0];
+    double m = 0.0;
+    for (int w = 0; w < kSliceWaves; ++w) {
+      am = min(am, wave_i[w]);
+      if (need_mass) m += wmass[w];
+    }
+    ws.recs[slot] = (uint64_t)kmax | ((uint64_t)(uint32_t)am << 32);
+    if (need_mass) ws.masses[slot] = m;
+  }
+}
+
+// Finish kernel: one workgroup per row. The row maximum is the largest
+// slice maximum, so every slice histogram is the row histogram's bins
+// d >= kmax_row - kmax_slice. All tokens of a bin share one key and one
+// weight, so the top-k threshold and the top-p cut come from counts times
+// weights; the ties at the cut keep the first n equal-key tokens in index
+// order, which fixes every slice's kept mass without reading a token. The
+// draw (kept weights in index order, first running mass > u * W) picks one
+// slice by those masses and scans its 8192 tokens (thread t: tokens
+// [16t, 16t + 16)). Cuts below the window take the generic path over the
+// row in memory.
+__global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArgs a, SampleWs ws) {
+  __shared__ SampleLds<kFinishWaves> s;
+  __shared__ int32_t sl_delta[kMaxSlices];
+  __shared__ double sl_mass[kMaxSlices];
+  __shared__ int32_t sl_cut[kMaxSlices];
   __shared__ int32_t h_i[8];
-  __shared__ double h_f[2];
+  __shared__ double h_f[4];
   const int V = a.vocab, S = sample_slices(V);
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row, V);
-  const float c2 = sp.c2;
-  const SliceRec* rr = recs + (int64_t)row * S;
+  const bool need_mass = !sp.greedy && !sp.use_k;
   const bool plain = !sp.greedy && !sp.use_k && !sp.use_p;
+  const float c2 = sp.c2;
+  const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
+                                                     (int64_t)row * a.row_stride);
+  const int last_chunk = (V - 1) / 8;
+  const int64_t slot0 = (int64_t)row * S;
 
-  // ---- wave 0: everything about the slices (at most 256; lane l holds slices l, l + 64, ...)
-  if (wave == 0) {
-    SliceRec rec[4];
+  // The slices' histograms as 16-byte units, loaded first (their addresses
+  // need nothing else): unit q holds bins [8u, 8u + 8) (u = q % 32) of slice
+  // q / 32; thread t takes units t + 512e.
+  const u32x4* hrow = reinterpret_cast<const u32x4*>(ws.hists + slot0 * kHistWords);
+  const int NU = S * kHistUnits;
+  constexpr int kU = kMaxSlices * kHistUnits / kFinishThreads;  // 8 units per thread at most
+  u32x4 v[kU];
+  if (!sp.greedy && !plain)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u * kWave + lane < S) rec[u] = rr[u * kWave + lane];  // one round of loads
-    int32_t mk = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u * kWave + lane < S) mk = max(mk, rec[u].kmax);
-    mk = wave_max_i32(mk);  // row maximum
-    int32_t am = 0x7fffffff;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (u * kWave + lane < S && rec[u].kmax == mk) am = min(am, rec[u].argmax);
-    am = wave_min_i32(am);  // its first index: slices are in index order
-    int32_t T = 0, ovf = 0, psl = -1;
-    double wall = 0.0, rem = INFINITY;
-    if (!sp.greedy) {
-      const float lmax = key16_value((uint32_t)mk);
-      double sm[4];  // slice masses in units of the row maximum
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        sm[u] = u * kWave + lane < S && !sp.use_k
-                    ? rec[u].mass * (double)fast_exp2((fmaxf(key16_value((uint32_t)rec[u].kmax), -1e30f) - lmax) * c2)
-                    : 0.0;
-      if (!sp.use_k) wall = wave_sum_f64(sm[0] + sm[1] + sm[2] + sm[3]);
-      if (plain) {  // the slice where the running mass passes u * W
-        const double target = (double)sp.u * wall;
-        double off = 0.0;
-        int32_t last = -1;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (psl < 0 && u * kWave < S) {
-            double ex;
-            const double in = wave_scan_f64(sm[u], lane, &ex);
-            const uint64_t who = __ballot(sm[u] > 0.0 && off + ex <= target && target < off + in);
-            if (who) {
-              const int l0 = __ffsll((unsigned long long)who) - 1;
-              psl = u * kWave + l0;
-              rem = target - (off + __shfl(ex, l0, 64));
-            }
-            last = max(last, wave_max_i32(sm[u] > 0.0 ? u * kWave + lane : -1));
-            off += __shfl(in, 63, 64);
-          }
-        }
-        if (psl < 0) psl = max(last, 0);  // rounding left the target past every slice: the last one with mass
-      } else {  // flattened window tokens of the slices whose maximum reaches the threshold
-        const uint32_t thr = (uint32_t)mk >= (uint32_t)(W - 1) ? (uint32_t)mk - (uint32_t)(W - 1) : 0u;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u * kWave < S) {
-            const int sl = u * kWave + lane;
-            int32_t c = 0;
-            if (sl < S && (uint32_t)rec[u].kmax >= thr) {
-              c = min(rec[u].count, kSliceCap);
-              ovf |= rec[u].count > kSliceCap;
-            }
-            const int32_t in = wave_incl_scan_i32(c, lane);
-            if (sl < S) f_cnt[sl] = T + in - c;
-            T += __shfl(in, 63, 64);
-          }
-        }
-        ovf = wave_max_i32(ovf);
-        if (lane == 0) f_cnt[S] = T;
-      }
+    for (int e = 0; e < kU; ++e) {
+      const int q = e * kFinishThreads + tid;
+      v[e] = q < NU ? hrow[q] : u32x4{0u, 0u, 0u, 0u};
     }
-    if (lane == 0) {
-      h_i[0] = mk;
-      h_i[1] = am;
-      h_i[2] = T;
-      h_i[3] = ovf;
-      h_i[4] = psl;
-      h_f[0] = wall;
-      h_f[1] = rem;
-    }
-  }
-  __syncthreads();
-  const uint32_t kmax = (uint32_t)h_i[0];
-  const int32_t argmax = h_i[1] == 0x7fffffff ? 0 : h_i[1];
+
+  // ---- slice records: thread t holds slice t (S <= 512)
+  const uint64_t rec = tid < S ? ws.recs[slot0 + tid] : 0ull;
+  const double smass = (need_mass && tid < S) ? ws.masses[slot0 + tid] : 0.0;
+  const int32_t skmax = tid < S ? (int32_t)(uint32_t)rec : 0;
+  const int32_t mk = block_reduce_i32(s, skmax, true);
+  const int32_t am0 = block_reduce_i32(s, (tid < S && skmax == mk) ? (int32_t)(rec >> 32) : 0x7fffffff, false);
+  const uint32_t rkmax = (uint32_t)mk;
+  const int32_t argmax = am0 == 0x7fffffff ? 0 : am0;  // slices are in index order
   if (sp.greedy) {
     if (tid == 0) a.out[row] = argmax;
     return;
   }
-  const float lmax = key16_value(kmax);
-  const double wall = h_f[0];
-  SampleRow<bf16_t> mrow;  // the row in memory, for the paths the window does not cover
-  mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
+  if (tid < S) sl_delta[tid] = mk - skmax;
+  const float lmax = key16_value(rkmax);
+  // slice masses in units of the row maximum (plain rows and top-p over the whole row)
+  double my_mass = (need_mass && tid < S)
+                       ? smass * (double)fast_exp2((fmaxf(key16_value((uint32_t)skmax), -1e30f) - lmax) * c2)
+                       : 0.0;
 
-  if (plain) {
-    // ---- plain rows: the token inside the chosen slice; thread t scans tokens [16t, 16t + 16)
-    const int sl = h_i[4];
-    const double rem = h_f[1];
-    const bf16_t* tp = reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride +
-                       (int64_t)sl * kSliceTokens + 16 * tid;
-    const int base = sl * kSliceTokens + 16 * tid;
-    float w[16];
-    double own = 0.0;
-    int32_t lastp = -1;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (base + 8 * q < V) x = *reinterpret_cast<const u32x4*>(tp + 8 * q);
-      float cs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = base + 8 * q + e;
-        w[8 * q + e] = i < V ? row_weight(SampleElem<bf16_t>::value(x, e), lmax, c2) : 0.f;
-        if (w[8 * q + e] > 0.f) lastp = i;
-        cs += w[8 * q + e];
-      }
-      own += (double)cs;
+  int dcut = -1;          // cut bin (rows with top-k or top-p); tokens with d < dcut are kept
+  uint32_t take = 0;      // tokens of bin dcut kept: the first ones in index order
+  int32_t cut_before = 0; // cut-bin tokens of the slices before this thread's slice
+  if (!plain) {
+    // ---- the row histogram
+    if (tid < kHistBins) {
+      s.hist[tid] = 0;
+      s.wtab[tid] = (uint32_t)tid <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)tid), lmax, c2) : 0.f;
     }
-    double in2, tot2;
-    int32_t lk;
-    const double ex2 = block_scan_f64_max(s, own, lastp, &in2, &tot2, &lk);
-    if (tid == 0) s.result = -1;
-    __syncthreads();
-    if (own > 0.0 && ex2 <= rem && rem < in2) {
-      double run = ex2;
-      int32_t res = lastp;
-      bool done = false;
+    const double wall = need_mass ? block_sum_f64(s, my_mass) : 0.0;  // (starts and ends with a barrier)
+    if (!need_mass) __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (!done && w[e] > 0.f) {
-          run += (double)w[e];
-          if (run > rem) {
-            res = base + e;
-            done = true;
-          }
+    for (int e = 0; e < kU; ++e) {
+      const int q = e * kFinishThreads + tid;
+      if (e * kFinishThreads < NU && q < NU) {
+        const int b0 = 8 * (q % kHistUnits) + sl_delta[q / kHistUnits];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t n = (v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+          if (n && b0 + c < kHistBins) atomicAdd(&s.hist[b0 + c], n);
         }
-      s.result = res;
-    }
-    __syncthreads();
-    const int32_t r = s.result >= 0 ? s.result : lk;
-    if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
-    return;
-  }
-
-  // ---- rows with top-k or top-p: the window of the row maximum (keys >= thr, d = kmax - key < W)
-  const uint32_t thr = kmax >= (uint32_t)(W - 1) ? kmax - (uint32_t)(W - 1) : 0u;
-  const int32_t T = h_i[2];
-  // Thread t takes flattened positions [g0, g1) (slice by slice, index order).
-  const int gper = (T + kSampleThreads - 1) / kSampleThreads;
-  const int g0 = min(T, tid * gper), g1 = min(T, g0 + gper);
-  int sl0 = 0;  // the slice holding g0: the last slice that starts at or before it
-  for (int lo = 0, hi = S - 1; lo <= hi;) {
-    const int mid = (lo + hi) >> 1;
-    if (f_cnt[mid] <= g0) {
-      sl0 = mid;
-      lo = mid + 1;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  // Batches of kB positions; the first batch stays in registers for the
-  // second pass (one batch covers rows of up to 512 * kB handed-over tokens).
-  constexpr int kB = 16;
-  auto load_batch = [&](int q0, int& sl, uint32_t* idx, uint32_t* key) {
-#pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const int q = q0 + u;
-      idx[u] = 0;
-      key[u] = 0;
-      if (q < g1) {
-        while (f_cnt[sl + 1] <= q) ++sl;
-        const uint32_t e = ents[((int64_t)row * S + sl) * kSliceCap + (q - f_cnt[sl])];
-        idx[u] = (uint32_t)sl * kSliceTokens + (e >> 16);
-        key[u] = e & 0xffffu;  // 0 (below every real key) past g1
       }
     }
-  };
-  uint32_t bidx[kB], bkey[kB];
-  int sl_next = sl0;
-  load_batch(g0, sl_next, bidx, bkey);
-  int32_t npass = 0;
-#pragma unroll
-  for (int u = 0; u < kB; ++u) npass += bkey[u] >= thr && bkey[u] != 0;
-  {
-    int sl = sl_next;
-    for (int q0 = g0 + kB; q0 < g1; q0 += kB) {
-      uint32_t ti[kB], tk[kB];
-      load_batch(q0, sl, ti, tk);
-#pragma unroll
-      for (int u = 0; u < kB; ++u) npass += tk[u] >= thr && tk[u] != 0;
-    }
-  }
-  int32_t n;
-  const int32_t pbase = block_excl_scan_i32(s, npass, &n);
-  const bool ok = h_i[3] == 0 && n <= kFinishCap;
-  if (ok) {
-    int32_t p = pbase;
-    auto put = [&](const uint32_t* ti, const uint32_t* tk) {
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (tk[u] >= thr && tk[u] != 0) {
-          f_idx[p] = (int32_t)ti[u];
-          f_d[p] = (uint8_t)(kmax - tk[u]);
-          ++p;
-        }
-    };
-    put(bidx, bkey);
-    int sl = sl_next;
-    for (int q0 = g0 + kB; q0 < g1; q0 += kB) {
-      uint32_t ti[kB], tk[kB];
-      load_batch(q0, sl, ti, tk);
-      put(ti, tk);
-    }
-  }
-  for (int b = tid; b < 256; b += kSampleThreads) {
-    s.hist[b] = 0;
-    s.wtab[b] = (b < W && (uint32_t)b <= kmax) ? row_weight(key16_value(kmax - (uint32_t)b), lmax, c2) : 0.f;
-  }
-  __syncthreads();
-  if (ok)
-    for (int q = tid; q < n; q += kSampleThreads) atomicAdd(&s.hist[f_d[q]], 1u);
-  __syncthreads();
-
-  // ---- cuts, by wave 0
-  if (wave == 0) {
-    int dcut = -1;
-    uint32_t take = 0;
-    if (ok) {
-      auto hc = [&](int b) { return b < W ? s.hist[b] : 0u; };
+    __syncthreads();
+    // ---- cuts (wave 0)
+    if (wave == 0) {
+      auto hc = [&](int b) { return s.hist[b]; };
       int dk = -1;
       uint32_t kk_take = 0, kk_eq = 0;
       if (sp.use_k) {
         double before;
-        wave_select128([&](int b) { return (double)hc(b); }, hc, (double)sp.k, &dk, &before, &kk_eq);
+        wave_select_bins<kHistBins>([&](int b) { return (double)hc(b); }, hc, (double)sp.k, &dk, &before, &kk_eq);
         if (dk >= 0) kk_take = (uint32_t)sp.k - (uint32_t)before;
       }
-      dcut = dk;
-      take = kk_take;
+      int dc = dk;
+      uint32_t tk2 = kk_take;
       if (sp.use_p && (!sp.use_k || dk >= 0)) {
-        const int dlim = sp.use_k ? dk : W - 1;
+        const int dlim = sp.use_k ? dk : kHistBins - 1;
         auto nb = [&](int b) { return b < dlim ? hc(b) : (b == dlim ? (sp.use_k ? kk_take : hc(b)) : 0u); };
         double Wk = wall;
-        if (sp.use_k) Wk = wave_sum_f64((double)nb(2 * lane) * (double)s.wtab[2 * lane] +
-                                        (double)nb(2 * lane + 1) * (double)s.wtab[2 * lane + 1]);
+        if (sp.use_k) {
+          double part = 0.0;
+#pragma unroll
+          for (int e = 0; e < kHistBins / kWave; ++e) {
+            const int b = (kHistBins / kWave) * lane + e;
+            part += (double)nb(b) * (double)s.wtab[b];
+          }
+          Wk = wave_sum_f64(part);
+        }
         const double target = (double)sp.p * Wk;
         int dstar;
         double above;
         uint32_t n_at;
-        wave_select128([&](int b) { return (double)nb(b) * (double)s.wtab[b]; }, nb, target, &dstar, &above,
-                       &n_at);
-        dcut = dstar;
+        wave_select_bins<kHistBins>([&](int b) { return (double)nb(b) * (double)s.wtab[b]; }, nb, target, &dstar,
+                                    &above, &n_at);
+        dc = dstar;
         if (dstar >= 0) {
           // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
           double need = ceil((target - above) / (double)s.wtab[dstar]);
           if (!(need >= 1.0)) need = 1.0;
-          take = need >= (double)n_at ? n_at : (uint32_t)need;
+          tk2 = need >= (double)n_at ? n_at : (uint32_t)need;
+        }
+      }
+      if (lane == 0) {
+        h_i[3] = dc;
+        h_i[4] = (int32_t)tk2;
+      }
+    }
+    __syncthreads();
+    dcut = h_i[3];
+    take = (uint32_t)h_i[4];
+    if (dcut < 0) {  // the cut lies below the window
+      SampleRow<bf16_t, kFinishWaves> mrow;
+      mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
+      const int32_t idx = sample_generic(mrow, s, sp, lmax);
+      if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
+      return;
+    }
+    // ---- kept mass of every slice: bins above the cut, plus its share of the
+    // first `take` tokens of the cut bin (slices in index order). The 32 units
+    // of a slice are one half-wave; a unit's eight bins (exact counts times
+    // fp32 weights) and the half-wave tree add in fp32 (relative error
+    // below 1e-6 of the slice's kept mass).
+#pragma unroll
+    for (int e = 0; e < kU; ++e) {
+      if (e * kFinishThreads < NU) {  // uniform
+        const int q = e * kFinishThreads + tid;
+        const int sl = q / kHistUnits;
+        const int b0 = q < NU ? 8 * (q % kHistUnits) + sl_delta[min(sl, kMaxSlices - 1)] : kHistBins;
+        float m = 0.f, cc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float n = (float)((v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu);
+          if (b0 + c < dcut) m = fmaf(n, s.wtab[b0 + c], m);
+          else if (b0 + c == dcut) cc = n;
+        }
+        m = group_sum<kHistUnits>(m);
+        cc = group_sum<kHistUnits>(cc);
+        if (q < NU && q % kHistUnits == 0) {
+          sl_mass[sl] = (double)m;
+          sl_cut[sl] = (int32_t)cc;
         }
       }
     }
-    if (lane == 0) {
-      h_i[5] = dcut;
-      h_i[6] = (int32_t)take;
+    __syncthreads();
+    const int32_t cc = tid < S ? sl_cut[tid] : 0;
+    int32_t tot_cut;
+    cut_before = block_excl_scan_i32(s, cc, &tot_cut);
+    const int32_t t_kept = min(max((int32_t)take - cut_before, 0), cc);
+    my_mass = tid < S ? sl_mass[tid] + (double)t_kept * (double)s.wtab[dcut] : 0.0;
+  }
+
+  // ---- the slice holding the draw
+  {
+    double incl, wtot;
+    const double excl = block_scan_f64(s, my_mass, &incl, &wtot);
+    const double target = (double)sp.u * wtot;
+    const int32_t last = block_reduce_i32(s, my_mass > 0.0 ? tid : -1, true);
+    if (tid == 0) {
+      h_i[2] = -1;
+      h_f[0] = INFINITY;
     }
+    __syncthreads();
+    if (my_mass > 0.0 && excl <= target && target < incl) {  // at most one thread
+      h_i[2] = tid;
+      h_f[0] = target - excl;
+      h_i[5] = cut_before;
+    }
+    __syncthreads();
+    const bool none = h_i[2] < 0;  // rounding left the target past every slice
+    __syncthreads();
+    if (none) {  // the last slice with mass
+      if (tid == 0) {
+        h_i[2] = max(last, 0);
+        h_f[0] = INFINITY;
+      }
+      if (tid == max(last, 0)) h_i[5] = cut_before;
+      __syncthreads();
+    }
+  }
+  const int psl = h_i[2];
+  const double rem = h_f[0];
+  const int32_t tie_base = h_i[5];
+
+  // ---- the draw inside slice psl: thread t scans tokens [16t, 16t + 16), in index order
+  const int tok0 = psl * kSliceTokens + 8 * kDrawChunks * tid;
+  const uint32_t cut_key = rkmax - (uint32_t)max(dcut, 0);
+  u32x4 x[kDrawChunks];
+#pragma unroll
+  for (int i = 0; i < kDrawChunks; ++i) x[i] = crow[min(tok0 / 8 + i, last_chunk)];  // clamped: stays in the row
+#pragma unroll
+  for (int i = 0; i < kDrawChunks; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // biased keys; key 0 (below every real key) at or past V
+      const int tok = tok0 + 8 * i + 2 * j;
+      uint32_t k = bf16x2_keys(x[i][j]);
+      if (tok >= V) k = 0u;
+      else if (tok + 1 >= V) k &= 0xffffu;
+      x[i][j] = k;
+    }
+  int32_t rank0 = 0;  // cut-bin tokens of the row before this thread's first token
+  if (!plain) {
+    int32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < kDrawChunks; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) n += ((x[i][j] & 0xffffu) == cut_key) + ((x[i][j] >> 16) == cut_key);
+    int32_t tot;
+    rank0 = tie_base + block_excl_scan_i32(s, n, &tot);
+  }
+  // kept weight of token e of chunk i; `rank` counts the cut-bin tokens seen
+  auto kept_w = [&](const u32x4& xi, int e, int32_t& rank) -> float {
+    const uint32_t kw = xi[e >> 1];
+    const uint32_t k = (e & 1) ? (kw >> 16) : (kw & 0xffffu);
+    if (k == 0u || !(plain || k > cut_key || (k == cut_key && (uint32_t)(rank++) < take))) return 0.f;
+    const uint32_t vw = bf16x2_from_keys(kw);
+    return row_weight(__uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16)), lmax, c2);
+  };
+  double own = 0.0;
+  int32_t lastk = -1;
+  {
+    int32_t rank = rank0;
+#pragma unroll
+    for (int i = 0; i < kDrawChunks; ++i) {
+      float cs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = kept_w(x[i], e, rank);
+        if (w > 0.f) lastk = tok0 + 8 * i + e;
+        cs += w;
+      }
+      own += (double)cs;
+    }
+  }
+  double incl, tot;
+  const double excl = block_scan_f64(s, own, &incl, &tot);
+  const int32_t lk = block_reduce_i32(s, lastk, true);  // the slice's last kept token
+  if (tid == 0) s.result = -1;
+  __syncthreads();
+  if (own > 0.0 && excl <= rem && rem < incl) {  // exactly one thread: the intervals meet bit for bit
+    int32_t rank = rank0, res = -1;
+    double run = excl;
+#pragma unroll
+    for (int i = 0; i < kDrawChunks; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = kept_w(x[i], e, rank);
+        if (res < 0 && w > 0.f) {
+          run += (double)w;
+          if (run > rem) res = tok0 + 8 * i + e;
+        }
+      }
+    s.result = res >= 0 ? res : lastk;  // rounding ran past the thread's tokens: its last kept one
   }
   __syncthreads();
-  const int dcut = h_i[5];
-  const uint32_t take = (uint32_t)h_i[6];
-
-  if (dcut >= 0) {
-    // ---- ties at the cut and the draw, on the list: thread t takes [q0, q1)
-    const int per = (n + kSampleThreads - 1) / kSampleThreads;
-    const int q0 = min(n, tid * per), q1 = min(n, q0 + per);
-    int32_t nat = 0;
-    for (int q = q0; q < q1; ++q) nat += f_d[q] == dcut;
-    int32_t tot_at;
-    const int32_t rank0 = block_excl_scan_i32(s, nat, &tot_at);  // rank of this thread's first token at the cut
-    double own = 0.0;
-    int32_t last_kept = -1;
-    {
-      int32_t rank = rank0;
-      for (int q = q0; q < q1; ++q) {
-        const int d = f_d[q];
-        const bool kept = d < dcut || (d == dcut && (uint32_t)(rank++) < take);
-        if (kept) {
-          own += (double)s.wtab[d];
-          last_kept = f_idx[q];
-        }
-      }
-    }
-    double tot, incl;
-    int32_t lk;  // list order is index order: the largest kept index is the last kept token
-    const double excl = block_scan_f64_max(s, own, last_kept, &incl, &tot, &lk);
-    const double target = (double)sp.u * tot;
-    if (tid == 0) s.result = -1;
-    __syncthreads();
-    if (own > 0.0 && excl <= target && target < incl) {
-      int32_t rank = rank0, res = last_kept;
-      double run = excl;
-      for (int q = q0; q < q1; ++q) {
-        const int d = f_d[q];
-        const bool kept = d < dcut || (d == dcut && (uint32_t)(rank++) < take);
-        if (kept) {
-          run += (double)s.wtab[d];
-          if (run > target) {
-            res = f_idx[q];
-            break;
-          }
-        }
-      }
-      s.result = res;
-    }
-    __syncthreads();
-    const int32_t res = s.result >= 0 ? s.result : lk;
-    if (tid == 0) a.out[row] = res >= 0 ? res : argmax;
-    return;
-  }
-
-  // ---- the cut lies below the window, or a list overflowed
-  const int32_t idx = sample_generic(mrow, s, sp, lmax);
-  if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
+  const int32_t r = s.result >= 0 ? s.result : lk;
+  if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
 }
 
 }  // namespace pkv

@@ -201,3 +201,58 @@ def test_vocab_boundaries_and_masked_tokens(V):
     bad = np.nonzero((got != want) & ~flagged)[0]
     assert bad.size == 0, (V, bad.tolist(), got[bad].tolist(), want[bad].tolist())
     assert got[0] == V - 1 and got[1] == V - 2
+
+
+def test_cut_deep_in_the_window():
+    """A few dozen large logits spread over two binades above a low floor:
+    top-k and top-p cuts land anywhere in the 256-key window of the row
+    maximum, with margins far above the oracle's."""
+    V, bs = 151936, 24
+    rng = _rng("two-level")
+    x = rng.standard_normal((bs, V)).astype(np.float32)
+    for r in range(bs):
+        idx = rng.choice(V, 40, replace=False)
+        x[r, idx] = rng.uniform(3.0, 16.0, 40)
+    T = rng.choice([1.0, 1.5, 2.5], bs).astype(np.float32)
+    K = rng.choice([0, 7, 25, 39], bs).astype(np.int32)
+    P = rng.choice([1.0, 0.5, 0.9, 0.97], bs).astype(np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    _run(_bf16(x), "bf16", T, K, P, u, "two-level", max_flag_frac=0.25)
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves many calls of different batch sizes and
+    parameter mixes (no state is carried from one call to the next)."""
+    V = 151936
+    ws = torch.full((pkv.sample_workspace_size(64, V),), 0xA5, dtype=torch.uint8, device="cuda")
+    rng = _rng("reuse")
+    for it, bs in enumerate((64, 17, 64, 1, 30)):
+        x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+        T = rng.choice([0.0, 0.7, 1.0], bs).astype(np.float32)
+        K = rng.choice([0, 50], bs).astype(np.int32)
+        P = rng.choice([1.0, 0.9, 0.95], bs).astype(np.float32)
+        u = rng.random(bs, dtype=np.float32)
+        xb = _bf16(x)
+        print(f"sample case reuse-{it} bs={bs}", flush=True)
+        tok = pkv.sample(to_dev(xb, "bf16"), to_dev(T), to_dev(K), to_dev(P), to_dev(u), workspace=ws)
+        torch.cuda.synchronize()
+        got = to_host(tok)
+        want, flagged = oracle.sample(oracle.widen(xb, "bf16"), T, K, P, u)
+        bad = np.nonzero((got != want) & ~flagged)[0]
+        assert bad.size == 0, (it, bad.tolist(), got[bad].tolist(), want[bad].tolist())
+
+
+def test_largest_bf16_vocabulary():
+    """The bf16 limit (2^20 tokens: 128 slices, 512 sub-slices per row), with
+    top-p, top-k + top-p and plain rows; one token past it is refused."""
+    V, bs = 1 << 20, 3
+    rng = _rng("max-vocab")
+    x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+    T = np.array([0.7, 1.0, 1.0], np.float32)
+    K = np.array([0, 50, 0], np.int32)
+    P = np.array([0.9, 0.95, 1.0], np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    _run(_bf16(x), "bf16", T, K, P, u, "max-vocab", max_flag_frac=None)
+    with pytest.raises(pkv.PkvError):
+        pkv.sample(torch.zeros((1, V + 8), dtype=torch.bfloat16, device="cuda"),
+                   to_dev(T[:1]), None, None, to_dev(u[:1]))
