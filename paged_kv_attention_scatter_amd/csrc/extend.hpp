@@ -24,8 +24,16 @@
 // reduction -- and O^T = V^T . P^T, whose accumulators again belong to the
 // lane's query, so rescaling is lane-local too. P^T is fed straight from the
 // S^T accumulators as the B operand; that fixes the order in which keys enter
-// the contraction, and V is stored in LDS transposed with the same key order,
-// so every MFMA operand is one 16-byte LDS read.
+// the contraction.
+//
+// LDS: K and V tiles are both row-major [64 keys][128 dims] with the 16-byte
+// unit u of key row k stored at unit u ^ (k & 15): every tile store (16 bytes
+// of one key row per lane), every K fragment read (16 bytes) and every V
+// fragment read is free of bank conflicts. V^T fragments come from the LDS
+// transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i
+// receives element i % 4 of the 8-byte words addressed by lanes 4j + i / 4
+// (j = 0..3), so lanes addressing 4 dims of 4 keys hand every lane 4 keys of
+// its own dim.
 #pragma once
 
 #include "common.hpp"
@@ -63,29 +71,23 @@ struct ExtendArgs {
 constexpr int kExtBlockQ = 128;  // query positions per workgroup
 constexpr int kExtThreads = 512; // 8 waves
 constexpr int kExtBlockK = 64;   // keys per LDS tile
-constexpr int kKPad = 136;       // K tile row: 128 dims + 8 pad (272 B)
-constexpr int kVPad = 72;        // V^T tile row: 64 keys + 8 pad (144 B)
+constexpr int kTileElems = kExtBlockK * kHeadDim;
 
-// Position of key k (0..63) inside a V^T row: within each 32-key chunk the
-// order is (key % 16) / 4, then (key % 32) / 16, then key % 4 -- the order in
-// which the MFMA B operand built from S^T accumulators presents keys.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k & 31) >> 4) + (k & 3);
-}
+// Element offset of dims [8u, 8u + 8) of key row k inside a tile.
+__device__ __forceinline__ int tile_off(int k, int u) { return k * kHeadDim + ((u ^ (k & 15)) << 3); }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // [a.lo, b.lo]
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // [a.hi, b.hi]
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+typedef short i16x4_v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4_v lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_v*)(reinterpret_cast<uintptr_t>(p)));
 }
 
 template <int NH>
 __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   // Two tile buffers: tile kb is computed from buffer kb & 1 while tile kb + 1
   // is written to the other one (one barrier per tile).
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kExtBlockK][kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim][kVPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTileElems];
   __shared__ int32_t sh_qstart;
 
   const int tid = threadIdx.x;
@@ -212,13 +214,10 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) *reinterpret_cast<u32x4*>(&Ks[buf][kq * KPT + e][dg * 8]) = kreg[e];
-    static_assert(KPT == 2, "V^T stores pack two keys");
-    const int p0 = vt_pos(kq * 2);  // keys 2m, 2m + 1 sit side by side in a V^T row
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {  // dims dg*8 + 2w (lo halves) and + 2w + 1 (hi halves)
-      *reinterpret_cast<uint32_t*>(&Vt[buf][dg * 8 + 2 * w][p0]) = pack_lo(vreg[0][w], vreg[1][w]);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][dg * 8 + 2 * w + 1][p0]) = pack_hi(vreg[0][w], vreg[1][w]);
+    for (int e = 0; e < KPT; ++e) {
+      const int k = kq * KPT + e;
+      *reinterpret_cast<u32x4*>(&Ks[buf][tile_off(k, dg)]) = kreg[e];
+      *reinterpret_cast<u32x4*>(&Vs[buf][tile_off(k, dg)]) = vreg[e];
     }
   };
 
@@ -244,15 +243,18 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_v ka =
-            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Ks[buf][kt * 16 + lq][ks * 32 + lg * 8]));
+            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Ks[buf][tile_off(kt * 16 + lq, ks * 4 + lg)]));
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
           s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
       }
 
-    // Online softmax for this lane's query; key of s[kt][i] is kb*64 + kt*16 + 4*lg + i.
+    // Online softmax for this lane's query, on raw scores (the running
+    // maximum m is in score units; weights are exp2(s * sc - m * sc)). The
+    // key of s[kt][i] is kb*64 + kt*16 + 4*lg + i; only the tiles that cross
+    // this wave's diagonal are masked (a wave-uniform branch).
     const bool need_mask = kb * kExtBlockK + kExtBlockK - 1 > C + t_min_wave;
-    const int lim = C + t_eff;
+    const int lim = C + t_eff - kb * kExtBlockK - 4 * lg;  // s[kt][i] is visible iff kt*16 + i <= lim
     bf16x8_v pb[NH][2];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -260,44 +262,54 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[hh][kt][i] * sc;
-          if (need_mask && kb * kExtBlockK + kt * 16 + 4 * lg + i > lim) x = -INFINITY;
-          v[kt * 4 + i] = x;
-        }
+        for (int i = 0; i < 4; ++i) v[kt * 4 + i] = s[hh][kt][i];
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kt * 16 + i > lim) v[kt * 4 + i] = -INFINITY;
+      }
       float mb = v[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mb = fmaxf(mb, v[i]);
       mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
       mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
       const float mn = fmaxf(m[hh], mb);
-      const float corr = fast_exp2(m[hh] - mn);  // m = -inf on the first tile: corr = 0
+      const float corr = fast_exp2((m[hh] - mn) * sc);  // m = -inf on the first tile: corr = 0
+      const float off = -mn * sc;
       m[hh] = mn;
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        v[i] = fast_exp2(v[i] - mn);
+        v[i] = fast_exp2(fmaf(v[i], sc, off));
         ls += v[i];
       }
-      l[hh] = l[hh] * corr + ls;
+      l[hh] = fmaf(l[hh], corr, ls);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8_v b;
+        bf16x8_v bq;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = (__bf16)v[(2 * k2 + (j >> 2)) * 4 + (j & 3)];
-        pb[hh][k2] = b;
+        for (int j = 0; j < 8; ++j) bq[j] = (__bf16)v[(2 * k2 + (j >> 2)) * 4 + (j & 3)];
+        pb[hh][k2] = bq;
       }
     }
 
-    // O^T += V^T . P^T: 8 tiles of 16 dims, 2 k-steps of 32 keys.
+    // O^T += V^T . P^T: 8 tiles of 16 dims, 2 k-steps of 32 keys. Element j
+    // of this lane's operand is key 32*k2 + 16*(j / 4) + 4*lg + j % 4 and dim
+    // 16*dt + lq; lane 4a + b of each 16-lane group addresses dims
+    // 16*dt + 4b .. +3 of key 32*k2 + 16h + 4*lg + a (h = j / 4).
+    const int ta = lq >> 2, tb = lq & 3;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8_v va =
-            __builtin_bit_cast(bf16x8_v, *reinterpret_cast<const u32x4*>(&Vt[buf][dt * 16 + lq][k2 * 32 + lg * 8]));
+        const int k0 = 32 * k2 + 4 * lg + ta;
+        const i16x4_v v0 = lds_read_tr16(&Vs[buf][tile_off(k0, 2 * dt + (tb >> 1)) + 4 * (tb & 1)]);
+        const i16x4_v v1 = lds_read_tr16(&Vs[buf][tile_off(k0 + 16, 2 * dt + (tb >> 1)) + 4 * (tb & 1)]);
+        const bf16x8_v va = __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
           oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
