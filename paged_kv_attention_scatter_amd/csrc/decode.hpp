@@ -314,9 +314,15 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 }
 
 // Merge the partials of every request that was cut by item boundaries; zero
-// the output of requests whose lengths were invalid. One workgroup per request.
+// the output of requests whose lengths were invalid. One workgroup per
+// request; every pass over the request's items issues its loads four at a
+// time, so the merge costs a few memory round trips, not one per item.
+// Threads [16h, 16h + 16) handle head h, eight consecutive dims each
+// (HQ * 16 threads).
 template <typename T, int HQ>
-__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(HQ * 16) decode_combine_kernel(DecodeArgs a) {
+  static_assert(HQ * 16 <= 1024, "16 threads per query head");
+  constexpr int kU = 4;  // loads in flight per thread per pass
   const int r = blockIdx.x;
   const int32_t* cu = a.cu_out;
   const int64_t total = cu[a.bs];
@@ -329,24 +335,42 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   const int P = a.num_items;
   const int i0 = item_of(c0, total, P), i1 = item_of(c1 - 1, total, P);
   if (i0 == i1) return;  // finished in place
-  for (int idx = threadIdx.x; idx < HQ * kHeadDim; idx += blockDim.x) {
-    const int h = idx / kHeadDim, d = idx % kHeadDim;
-    float M = -INFINITY;
-    for (int i = i0; i <= i1; ++i) {
-      if (item_begin(i, total, P) == item_begin(i + 1, total, P)) continue;  // empty item
-      M = fmaxf(M, a.part_ml[((int64_t)(i + r) * HQ + h) * 2]);
-    }
-    float L = 0.f, A = 0.f;
-    for (int i = i0; i <= i1; ++i) {
-      if (item_begin(i, total, P) == item_begin(i + 1, total, P)) continue;
-      const int64_t s = (int64_t)(i + r) * HQ + h;
-      const float mi = a.part_ml[s * 2];
-      const float c = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
-      L += a.part_ml[s * 2 + 1] * c;
-      A += a.part_acc[s * kHeadDim + d] * c;
-    }
-    store_out<T>(ob + (int64_t)h * kHeadDim + d, L > 0.f ? A / L : 0.f);
+  const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+  // An item that holds no key of the request wrote nothing: it is skipped.
+  auto live = [&](int i) { return i <= i1 && item_begin(i, total, P) != item_begin(i + 1, total, P); };
+  auto ml = [&](int i) { return reinterpret_cast<const float2*>(a.part_ml)[(int64_t)(i + r) * HQ + h]; };
+
+  float M = -INFINITY;
+  for (int i = i0; i <= i1; i += kU) {
+    float2 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = live(i + u) ? ml(i + u) : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) M = fmaxf(M, v[u].x);
   }
+  float L = 0.f, A[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = i0; i <= i1; i += kU) {
+    float2 v[kU];
+    u32x4 x[kU][2];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = live(i + u);
+      v[u] = ok ? ml(i + u) : make_float2(-INFINITY, 0.f);
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.part_acc + ((int64_t)(i + u + r) * HQ + h) * kHeadDim + d0);
+      x[u][0] = ok ? src[0] : u32x4{0u, 0u, 0u, 0u};
+      x[u][1] = ok ? src[1] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float c = (v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - M);
+      L += v[u].y * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) A[e] += __uint_as_float(x[u][e >> 2][e & 3]) * c;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) store_out<T>(ob + (int64_t)h * kHeadDim + d0 + e, A[e] * inv);
 }
 
 }  // namespace pkv

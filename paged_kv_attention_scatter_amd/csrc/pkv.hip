@@ -163,7 +163,7 @@ int launch_decode(const pkv::DecodeArgs& a, hipStream_t s) {
                      dim3(NWAVE * 64), dyn, s, a);
   int rc = check_launch("decode_splitk");
   if (rc) return rc;
-  hipLaunchKernelGGL((pkv::decode_combine_kernel<T, HKV * G>), dim3(a.bs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((pkv::decode_combine_kernel<T, HKV * G>), dim3(a.bs), dim3(HKV * G * 16), 0, s, a);
   return check_launch("decode_combine");
 }
 
