@@ -36,6 +36,8 @@
 // its own dim.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace pkv {
@@ -46,8 +48,8 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 struct ExtendArgs {
   const void* k_pool;
   const void* v_pool;
-  int64_t pool_row;      // elements between slots
-  int64_t num_slots;
+  uint32_t row_bytes;    // bytes between slots
+  uint32_t slot_limit;   // slots are valid below this (num_slots, capped at 2^31)
   const void* q;
   int64_t q_stride;      // elements between query rows
   void* o;
@@ -72,6 +74,10 @@ constexpr int kExtBlockQ = 128;  // query positions per workgroup
 constexpr int kExtThreads = 512; // 8 waves
 constexpr int kExtBlockK = 64;   // keys per LDS tile
 constexpr int kTileElems = kExtBlockK * kHeadDim;
+// The running maximum is only moved when a score exceeds it by more than
+// 2^kRescaleLog2 in weight: every weight then stays <= 2^kRescaleLog2, and
+// the accumulators are rescaled only on those (rare) tiles.
+constexpr float kRescaleLog2 = 8.0f;
 
 // Element offset of dims [8u, 8u + 8) of key row k inside a tile.
 __device__ __forceinline__ int tile_off(int k, int u) { return k * kHeadDim + ((u ^ (k & 15)) << 3); }
@@ -182,37 +188,49 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   // Tile loader: thread -> 2 consecutive keys (kq*2 ..) x 8 dims (dg*8 ..).
   // Page-table entries are fetched one tile ahead of the K/V rows they
   // address, and K/V rows one tile ahead of their use, so neither latency
-  // sits between two tiles of MFMA work.
+  // sits between two tiles of MFMA work. Keys past the block's last key and
+  // slots outside the pool load slot 0's row and are zeroed before they reach
+  // LDS (an out-of-pool slot also raises the fault bit once, after the loop).
   const int kq = tid >> 4, dg = tid & 15;
   constexpr int KPT = kExtBlockK * 16 / kExtThreads;  // keys per thread
-  int32_t slot_next[KPT];
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + g * (kHeadDim * 2) + dg * 16;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * (kHeadDim * 2) + dg * 16;
+  int32_t slot_raw[KPT];   // page-table entries of the next tile to load
+  bool key_ok[KPT];        // whether those keys exist (j < n_keys)
   auto load_slots = [&](int kb) {
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       const int j = kb * kExtBlockK + kq * KPT + e;
-      slot_next[e] = (kb < nkb && j < n_keys) ? pt[j] : -1;
+      key_ok[e] = j < n_keys;
+      slot_raw[e] = pt[key_ok[e] ? j : 0];
     }
   };
   u32x4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&]() {  // rows of the slots in slot_next
+  uint32_t zero_bits = 0;  // keys of the loaded tile to store as zeros
+  bool bad_slot = false;
+  auto load_tile = [&]() {
+    zero_bits = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-      int32_t slot = slot_next[e];
-      if (slot != -1 && (slot < 0 || (int64_t)slot >= a.num_slots)) {
-        raise_fault(a.faults, 0x4u);
-        slot = -1;
-      }
-      if (slot >= 0) {
-        const int64_t off = (int64_t)slot * a.pool_row + (int64_t)g * kHeadDim + dg * 8;
-        kreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
-        vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
-      } else {
-        kreg[e] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[e] = (u32x4){0u, 0u, 0u, 0u};
-      }
+      const int32_t slot = key_ok[e] ? slot_raw[e] : -1;
+      const bool ok = (uint32_t)slot < a.slot_limit;
+      bad_slot |= !ok && slot != -1;
+      zero_bits |= ok ? 0u : (1u << e);
+      const uint64_t off = (uint64_t)(ok ? (uint32_t)slot : 0u) * a.row_bytes;
+      kreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+      vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (__any(zero_bits != 0)) {
+#pragma unroll
+      for (int e = 0; e < KPT; ++e)
+        if (zero_bits & (1u << e)) {
+          kreg[e] = (u32x4){0u, 0u, 0u, 0u};
+          vreg[e] = (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       const int k = kq * KPT + e;
@@ -223,15 +241,14 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
 
   const float sc = a.scale_log2;
   const int t_min_wave = qb * kExtBlockQ + wave * 16;
-  load_slots(0);
-  load_tile();        // tile 0
-  load_slots(1);
-  store_tile(0);
-  load_tile();        // tile 1
-  load_slots(2);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  const int ta = lq >> 2, tb = lq & 3;
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const bf16x2_v ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // One key tile from LDS buffer `buf` (a compile-time constant, so every
+  // LDS address below is a loop-invariant register plus an immediate).
+  auto step = [&](int kb, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     // S^T = K . Q^T for 4 key tiles of 16.
     f32x4_v s[NH][4];
 #pragma unroll
@@ -249,10 +266,13 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
           s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
       }
 
-    // Online softmax for this lane's query, on raw scores (the running
-    // maximum m is in score units; weights are exp2(s * sc - m * sc)). The
+    // Online softmax for this lane's query, on raw scores: weights are
+    // exp2(s * sc - m * sc) against the running maximum m (score units). The
     // key of s[kt][i] is kb*64 + kt*16 + 4*lg + i; only the tiles that cross
-    // this wave's diagonal are masked (a wave-uniform branch).
+    // this wave's diagonal are masked (a wave-uniform branch). m moves only
+    // when some lane of the wave sees a score more than kRescaleLog2 above
+    // it (wave-uniform too): then the exact maximum over the query's four
+    // lanes is taken and the accumulators are rescaled.
     const bool need_mask = kb * kExtBlockK + kExtBlockK - 1 > C + t_min_wave;
     const int lim = C + t_eff - kb * kExtBlockK - 4 * lg;  // s[kt][i] is visible iff kt*16 + i <= lim
     bf16x8_v pb[NH][2];
@@ -270,24 +290,30 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
           for (int i = 0; i < 4; ++i)
             if (kt * 16 + i > lim) v[kt * 4 + i] = -INFINITY;
       }
-      float mb = v[0];
+      // IEEE maximum (NaN-propagating) needs no quieting of its inputs and
+      // maps to the three-input v_maximum3_f32.
+      float ml[4];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mb = fmaxf(mb, v[i]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mn = fmaxf(m[hh], mb);
-      const float corr = fast_exp2((m[hh] - mn) * sc);  // m = -inf on the first tile: corr = 0
-      const float off = -mn * sc;
-      m[hh] = mn;
-      float ls = 0.f;
+      for (int i = 0; i < 4; ++i)
+        ml[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[4 * i], v[4 * i + 1]),
+                                              __builtin_elementwise_maximum(v[4 * i + 2], v[4 * i + 3]));
+      const float mloc = __builtin_elementwise_maximum(__builtin_elementwise_maximum(ml[0], ml[1]),
+                                                       __builtin_elementwise_maximum(ml[2], ml[3]));
+      // m = -inf (first tile) always moves; a lane whose keys are all masked
+      // (mloc = -inf) never asks for a move.
+      if (__any((mloc - m[hh]) * sc > kRescaleLog2)) {
+        float mb = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float mn = fmaxf(m[hh], mb);
+        const float corr = fast_exp2((m[hh] - mn) * sc);  // m = -inf: corr = 0
+        m[hh] = mn;
+        l[hh] *= corr;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        v[i] = fast_exp2(fmaf(v[i], sc, off));
-        ls += v[i];
+        for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
       }
-      l[hh] = fmaf(l[hh], corr, ls);
+      const float off = -m[hh] * sc;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
+      for (int i = 0; i < 16; ++i) v[i] = fast_exp2(fmaf(v[i], sc, off));
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8_v bq;
@@ -295,13 +321,26 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         for (int j = 0; j < 8; ++j) bq[j] = (__bf16)v[(2 * k2 + (j >> 2)) * 4 + (j & 3)];
         pb[hh][k2] = bq;
       }
+      // Row sum of the rounded weights (the ones the PV product uses).
+      float ls[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb[hh][k2]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // Copy the element out first: a bit cast of a vector element
+          // expression reads the vector's first element in this compiler.
+          const uint32_t pair = pw[w];
+          ls[k2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pair), ones, ls[k2], false);
+        }
+      }
+      l[hh] += ls[0] + ls[1];
     }
 
     // O^T += V^T . P^T: 8 tiles of 16 dims, 2 k-steps of 32 keys. Element j
     // of this lane's operand is key 32*k2 + 16*(j / 4) + 4*lg + j % 4 and dim
     // 16*dt + lq; lane 4a + b of each 16-lane group addresses dims
     // 16*dt + 4b .. +3 of key 32*k2 + 16h + 4*lg + a (h = j / 4).
-    const int ta = lq >> 2, tb = lq & 3;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -318,12 +357,25 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     // Tile kb + 1 (loaded during this tile) into the other buffer; rows of
     // tile kb + 2 and the slots of tile kb + 3 go out.
     if (kb + 1 < nkb) {
-      store_tile(buf ^ 1);
+      store_tile(std::integral_constant<int, buf ^ 1>{});
       load_tile();
       load_slots(kb + 3);
     }
     __syncthreads();
+  };
+
+  load_slots(0);
+  load_tile();        // tile 0
+  load_slots(1);
+  store_tile(std::integral_constant<int, 0>{});
+  load_tile();        // tile 1
+  load_slots(2);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
   }
+  if (bad_slot) raise_fault(a.faults, 0x4u);
 
   // Normalise and write: lane holds dims dt*16 + 4*lg + i of query t.
 #pragma unroll
