@@ -26,14 +26,18 @@
 // S^T accumulators as the B operand; that fixes the order in which keys enter
 // the contraction.
 //
-// LDS: K and V tiles are both row-major [64 keys][128 dims] with the 16-byte
-// unit u of key row k stored at unit u ^ (k & 15): every tile store (16 bytes
-// of one key row per lane), every K fragment read (16 bytes) and every V
-// fragment read is free of bank conflicts. V^T fragments come from the LDS
-// transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i
-// receives element i % 4 of the 8-byte words addressed by lanes 4j + i / 4
-// (j = 0..3), so lanes addressing 4 dims of 4 keys hand every lane 4 keys of
-// its own dim.
+// LDS: the K tile is row-major [64 keys][128 dims] with the 16-byte unit u
+// of key row k stored at unit u ^ (k & 15), so tile stores (16 bytes of one
+// key row per lane) and K fragment reads (16 bytes) are free of bank
+// conflicts. The V tile is stored transposed, [128 dims][64 keys], two dims
+// to a 256-byte pair row, with the keys of a row in the order the PV operand
+// consumes them (key 32b + 16h + 4g + i at position 32b + 8g + 4h + i) and
+// the 16 units of a pair row XOR-swizzled by a function of the pair-row
+// index: every V fragment is one conflict-free 16-byte read, and the
+// transposing stores (one 4-byte key pair per lane) are conflict-free too.
+// (The LDS transpose read would serve the same operand from a row-major
+// tile, but on gfx950 it moves a quarter of the bytes per cycle of a 16-byte
+// read, which makes it the limit of this kernel.)
 #pragma once
 
 #include <type_traits>
@@ -82,11 +86,15 @@ constexpr float kRescaleLog2 = 8.0f;
 // Element offset of dims [8u, 8u + 8) of key row k inside a tile.
 __device__ __forceinline__ int tile_off(int k, int u) { return k * kHeadDim + ((u ^ (k & 15)) << 3); }
 
-typedef short i16x4_v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i16x4_v lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_v*)(reinterpret_cast<uintptr_t>(p)));
+// V^T tile addressing (element offsets). Pair row rp holds dims 2rp and
+// 2rp + 1; unit (p * 8 + pos / 8) of it moves to that index ^ vt_swz(rp).
+__device__ __forceinline__ int vt_swz(int rp) { return ((rp ^ (rp >> 3)) & 7) | (((rp >> 2) & 1) << 3); }
+__device__ __forceinline__ int vt_off(int dim, int pos) {
+  const int rp = dim >> 1;
+  return rp * 128 + (((((dim & 1) << 3) | (pos >> 3)) ^ vt_swz(rp)) << 3) + (pos & 7);
 }
+// Position of key k (0..63) inside a V^T row.
+__device__ __forceinline__ int vt_pos(int k) { return (k & 32) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3); }
 
 template <int NH>
 __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
@@ -191,7 +199,10 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   // sits between two tiles of MFMA work. Keys past the block's last key and
   // slots outside the pool load slot 0's row and are zeroed before they reach
   // LDS (an out-of-pool slot also raises the fault bit once, after the loop).
-  const int kq = tid >> 4, dg = tid & 15;
+  // A wave loads four key rows, chosen (key pairs kq, kq + 1, kq + 8, kq + 9
+  // of the 32) so that its transposed V stores cover all 64 LDS banks.
+  const int kq = ((tid >> 4) & 1) | (((tid >> 6) & 3) << 1) | (((tid >> 5) & 1) << 3) | ((tid >> 8) << 4);
+  const int dg = tid & 15;
   constexpr int KPT = kExtBlockK * 16 / kExtThreads;  // keys per thread
   const char* kbase = reinterpret_cast<const char*>(a.k_pool) + g * (kHeadDim * 2) + dg * 16;
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * (kHeadDim * 2) + dg * 16;
@@ -235,13 +246,19 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     for (int e = 0; e < KPT; ++e) {
       const int k = kq * KPT + e;
       *reinterpret_cast<u32x4*>(&Ks[buf][tile_off(k, dg)]) = kreg[e];
-      *reinterpret_cast<u32x4*>(&Vs[buf][tile_off(k, dg)]) = vreg[e];
+    }
+    // V^T: dim 8*dg + d of keys 2kq and 2kq + 1 as one 4-byte pair.
+    static_assert(KPT == 2, "the V^T store packs two keys per lane");
+    const int pos0 = vt_pos(kq * KPT);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t pair = __builtin_amdgcn_perm(vreg[1][d >> 1], vreg[0][d >> 1], (d & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&Vs[buf][vt_off(8 * dg + d, pos0)]) = pair;
     }
   };
 
   const float sc = a.scale_log2;
   const int t_min_wave = qb * kExtBlockQ + wave * 16;
-  const int ta = lq >> 2, tb = lq & 3;
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   const bf16x2_v ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -255,6 +272,9 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s[hh][kt] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+    // Each SIMD runs two waves of this workgroup in step; the one issuing
+    // MFMAs is given priority over the one doing softmax arithmetic.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -266,6 +286,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
           s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
       }
 
+    __builtin_amdgcn_s_setprio(0);
     // Online softmax for this lane's query, on raw scores: weights are
     // exp2(s * sc - m * sc) against the running maximum m (score units). The
     // key of s[kt][i] is kb*64 + kt*16 + 4*lg + i; only the tiles that cross
@@ -337,23 +358,22 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       l[hh] += ls[0] + ls[1];
     }
 
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P^T: 8 tiles of 16 dims, 2 k-steps of 32 keys. Element j
-    // of this lane's operand is key 32*k2 + 16*(j / 4) + 4*lg + j % 4 and dim
-    // 16*dt + lq; lane 4a + b of each 16-lane group addresses dims
-    // 16*dt + 4b .. +3 of key 32*k2 + 16h + 4*lg + a (h = j / 4).
+    // of this lane's operand is dim 16*dt + lq, key 32*k2 + 16*(j / 4) +
+    // 4*lg + j % 4: eight consecutive positions of that dim's V^T row.
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const int k0 = 32 * k2 + 4 * lg + ta;
-        const i16x4_v v0 = lds_read_tr16(&Vs[buf][tile_off(k0, 2 * dt + (tb >> 1)) + 4 * (tb & 1)]);
-        const i16x4_v v1 = lds_read_tr16(&Vs[buf][tile_off(k0 + 16, 2 * dt + (tb >> 1)) + 4 * (tb & 1)]);
-        const bf16x8_v va = __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8_v va = __builtin_bit_cast(
+            bf16x8_v, *reinterpret_cast<const u32x4*>(&Vs[buf][vt_off(16 * dt + lq, 32 * k2 + 8 * lg)]));
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
           oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
       }
 
+    __builtin_amdgcn_s_setprio(0);
     // Tile kb + 1 (loaded during this tile) into the other buffer; rows of
     // tile kb + 2 and the slots of tile kb + 3 go out.
     if (kb + 1 < nkb) {

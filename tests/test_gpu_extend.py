@@ -97,6 +97,24 @@ def test_extend_matches_oracle(name, kw):
     assert pkv.read_faults() == 0
 
 
+@pytest.mark.parametrize("grow", [20.0, 60.0])
+def test_extend_growing_scores(grow):
+    """K rows after each request's first 64 keys scaled by `grow`: later scores
+    sit far above the first tile's maximum, so the running maximum moves by
+    large steps and the accumulators are rescaled (softmax stays exact)."""
+    c = _make(11, C=[300, 0, 70], E=[200, 260, 129])
+    K = oracle.widen(c["kv"][0], "bf16")
+    for r in range(len(c["S"])):
+        later = c["table"][r, 64:c["S"][r]]
+        K[later] *= grow
+    c["kv"] = np.stack([f32_to_bf16_bits(K.astype(np.float32)), c["kv"][1]])
+    got = _run(c)
+    ref = _oracle(c)
+    mx, rel = check_attention(got, ref, "bf16", f"grow {grow}")
+    print(f"  grow {grow}: max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0
+
+
 def test_extend_paged_equals_contiguous_bitwise():
     """The same rows through an identity page table and through a permuted one."""
     c = _make(77, C=[100, 0, 9], E=[150, 64, 300])
