@@ -104,54 +104,105 @@ constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave 
 
 // ---------------------------------------------------------------- wave helpers
 
-PKV_INLINE double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Wave-wide reductions and scans on DPP row moves and readlane (no LDS
+// round trips). Every lane of the wave must be active.
+
+// 32-bit DPP move; a lane without a source in its row reads 0.
+template <int CTRL>
+PKV_INLINE int32_t dpp_i32(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
 }
-PKV_INLINE float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+template <int CTRL>
+PKV_INLINE double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int32_t)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int32_t)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-PKV_INLINE int32_t wave_min_i32(int32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+PKV_INLINE int32_t lane_i32(int32_t x, int l) { return __builtin_amdgcn_readlane(x, l); }
+PKV_INLINE double lane_f64(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-PKV_INLINE int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-PKV_INLINE int32_t wave_max_i32(int32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
-}
-PKV_INLINE double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
+// Combine over the 16 lanes of each row (every lane ends with its row's
+// value): lane ^ 1, lane ^ 2, the other quad, the other half.
+template <class T, class Op>
+PKV_INLINE T row_reduce(T v, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    v = op(v, dpp_f64<0xB1>(v));
+    v = op(v, dpp_f64<0x4E>(v));
+    v = op(v, dpp_f64<0x141>(v));
+    v = op(v, dpp_f64<0x140>(v));
+  } else {
+    v = op(v, (T)dpp_i32<0xB1>((int32_t)v));
+    v = op(v, (T)dpp_i32<0x4E>((int32_t)v));
+    v = op(v, (T)dpp_i32<0x141>((int32_t)v));
+    v = op(v, (T)dpp_i32<0x140>((int32_t)v));
   }
   return v;
 }
+PKV_INLINE double wave_sum_f64(double v) {
+  v = row_reduce(v, [](double x, double y) { return x + y; });
+  return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+}
+PKV_INLINE float wave_max_f32(float v) {
+  const int32_t r = row_reduce(__float_as_int(v), [](int32_t x, int32_t y) {
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  });
+  return fmaxf(fmaxf(__int_as_float(lane_i32(r, 0)), __int_as_float(lane_i32(r, 16))),
+               fmaxf(__int_as_float(lane_i32(r, 32)), __int_as_float(lane_i32(r, 48))));
+}
+PKV_INLINE int32_t wave_min_i32(int32_t v) {
+  v = row_reduce(v, [](int32_t x, int32_t y) { return min(x, y); });
+  return min(min(lane_i32(v, 0), lane_i32(v, 16)), min(lane_i32(v, 32), lane_i32(v, 48)));
+}
+PKV_INLINE int32_t wave_sum_i32(int32_t v) {
+  v = row_reduce(v, [](int32_t x, int32_t y) { return x + y; });
+  return (lane_i32(v, 0) + lane_i32(v, 16)) + (lane_i32(v, 32) + lane_i32(v, 48));
+}
+PKV_INLINE int32_t wave_max_i32(int32_t v) {
+  v = row_reduce(v, [](int32_t x, int32_t y) { return max(x, y); });
+  return max(max(lane_i32(v, 0), lane_i32(v, 16)), max(lane_i32(v, 32), lane_i32(v, 48)));
+}
+// Inclusive scans: Kogge-Stone inside each row (shifts 1, 2, 4, 8), then the
+// totals of the rows before (o_k = o_{k-1} + t_{k-1}) added to every lane of
+// row k. *row_off = o_k of this lane's row.
+PKV_INLINE double wave_incl_scan_f64(double v, int lane, double* row_off = nullptr) {
+  v += dpp_f64<0x111>(v);
+  v += dpp_f64<0x112>(v);
+  v += dpp_f64<0x114>(v);
+  v += dpp_f64<0x118>(v);
+  const double o1 = lane_f64(v, 15);
+  const double o2 = o1 + lane_f64(v, 31);
+  const double o3 = o2 + lane_f64(v, 47);
+  const int row = lane >> 4;
+  const double off = row == 0 ? 0.0 : (row == 1 ? o1 : (row == 2 ? o2 : o3));
+  if (row_off) *row_off = off;
+  return row == 0 ? v : v + off;
+}
 // Inclusive scan and the exclusive value taken from the previous lane's
-// inclusive one, so consecutive lanes' [excl, incl) intervals meet exactly.
+// inclusive one, so consecutive lanes' [excl, incl) intervals meet exactly
+// (the first lane of row k gets o_k, which equals lane 16k - 1's inclusive
+// value t_{k-1} + o_{k-1} bit for bit).
 PKV_INLINE double wave_scan_f64(double v, int lane, double* excl) {
-  const double incl = wave_incl_scan_f64(v, lane);
-  const double prev = __shfl_up(incl, 1, 64);
-  *excl = lane > 0 ? prev : 0.0;
+  double off;
+  const double incl = wave_incl_scan_f64(v, lane, &off);
+  const double prev = dpp_f64<0x111>(incl);
+  *excl = (lane & 15) ? prev : off;
   return incl;
 }
 PKV_INLINE int32_t wave_incl_scan_i32(int32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += dpp_i32<0x111>(v);
+  v += dpp_i32<0x112>(v);
+  v += dpp_i32<0x114>(v);
+  v += dpp_i32<0x118>(v);
+  const int32_t o1 = lane_i32(v, 15);
+  const int32_t o2 = o1 + lane_i32(v, 31);
+  const int32_t o3 = o2 + lane_i32(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0 : (row == 1 ? o1 : (row == 2 ? o2 : o3)));
 }
 // Sum over the wave, returned in every lane (fp32 tree).
 PKV_INLINE float wave_total_f32(float v) {
@@ -405,7 +456,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds<NW>& s, VF v, TF tar
     for (int g = g0; g < g1; ++g) own += (double)s.gsum[g];
     double run;
     const double incl = wave_scan_f64(own, lane, &run);
-    const double total = __shfl(incl, 63, 64);
+    const double total = lane_f64(incl, 63);
     const double target = target_of(total);
     if (own > 0.0 && run <= target && target < incl) {
       int gp = -1;
@@ -454,7 +505,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds<NW>& s, VF v, TF tar
         });
         if (found < 0) found = lastv;
       }
-      res = __shfl(found, l0, 64);
+      res = lane_i32(found, l0);
     }
     if (lane == 0) s.result = res;
   }
@@ -727,10 +778,10 @@ PKV_INLINE void wave_select_bins(AF amount, CF count, double goal, int* bin, dou
     return;
   }
   const int l0 = __ffsll((unsigned long long)who) - 1;
-  *bin = __shfl(b, l0, 64);
-  *before = __shfl(bef, l0, 64);
+  *bin = lane_i32(b, l0);
+  *before = lane_f64(bef, l0);
   const uint32_t c = b >= 0 ? count(b) : 0u;
-  *cnt = (uint32_t)__shfl((int32_t)c, l0, 64);
+  *cnt = (uint32_t)lane_i32((int32_t)c, l0);
 }
 
 // Slice kernel: workgroup b reads slice b / bs of row b % bs (rows vary
