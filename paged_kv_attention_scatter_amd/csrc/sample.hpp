@@ -718,9 +718,9 @@ constexpr int kHistBins = 256;      // window: keys within 255 of a maximum
 constexpr int kHistWords = kHistBins / 2;                         // 16-bit counts, two per word
 constexpr int kHistUnits = kHistBins / 8;                         // 16-byte units of a histogram
 constexpr int kMaxSlices = 128;     // slices per row (2^20 tokens)
-constexpr int kFinishThreads = 512;
+constexpr int kFinishThreads = 1024;
 constexpr int kFinishWaves = kFinishThreads / kWave;
-constexpr int kDrawChunks = kSliceTokens / (8 * kFinishThreads);  // 2: 16 tokens per finishing thread
+constexpr int kDrawChunks = kSliceTokens / (8 * kFinishThreads);  // 1: 8 tokens per finishing thread
 
 __host__ __device__ inline int sample_slices(int V) { return (V + kSliceTokens - 1) / kSliceTokens; }
 static_assert((int64_t)kMaxSlices * kSliceTokens <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves * 8,
@@ -932,8 +932,9 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 // order, which fixes every slice's kept mass without reading a token. The
 // draw (kept weights in index order, first running mass > u * W) picks one
 // slice by those masses and scans its 8192 tokens (thread t: tokens
-// [16t, 16t + 16)). Cuts below the window take the generic path over the
-// row in memory.
+// [8t, 8t + 8)). Cuts below the window take the generic path over the
+// row in memory. Per-slice and per-row steps run in wave 0 on DPP scans;
+// the workgroup meets at eight barriers (four for plain rows).
 __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArgs a, SampleWs ws) {
   __shared__ SampleLds<kFinishWaves> s;
   __shared__ int32_t sl_delta[kMaxSlices];
@@ -941,6 +942,9 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   __shared__ int32_t sl_cut[kMaxSlices];
   __shared__ int32_t h_i[8];
   __shared__ double h_f[4];
+  __shared__ int32_t w_cnt[kFinishWaves];
+  __shared__ double w_mass[kFinishWaves];
+  __shared__ int32_t w_last[kFinishWaves];
   const int V = a.vocab, S = sample_slices(V);
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -956,10 +960,10 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
 
   // The slices' histograms as 16-byte units, loaded first (their addresses
   // need nothing else): unit q holds bins [8u, 8u + 8) (u = q % 32) of slice
-  // q / 32; thread t takes units t + 512e.
+  // q / 32; thread t takes units t + 1024e.
   const u32x4* hrow = reinterpret_cast<const u32x4*>(ws.hists + slot0 * kHistWords);
   const int NU = S * kHistUnits;
-  constexpr int kU = kMaxSlices * kHistUnits / kFinishThreads;  // 8 units per thread at most
+  constexpr int kU = kMaxSlices * kHistUnits / kFinishThreads;  // 4 units per thread at most
   u32x4 v[kU];
   if (!sp.greedy && !plain)
 #pragma unroll
@@ -968,36 +972,58 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
       v[e] = q < NU ? hrow[q] : u32x4{0u, 0u, 0u, 0u};
     }
 
-  // ---- slice records: thread t holds slice t (S <= 512)
-  const uint64_t rec = tid < S ? ws.recs[slot0 + tid] : 0ull;
-  const double smass = (need_mass && tid < S) ? ws.masses[slot0 + tid] : 0.0;
-  const int32_t skmax = tid < S ? (int32_t)(uint32_t)rec : 0;
-  const int32_t mk = block_reduce_i32(s, skmax, true);
-  const int32_t am0 = block_reduce_i32(s, (tid < S && skmax == mk) ? (int32_t)(rec >> 32) : 0x7fffffff, false);
-  const uint32_t rkmax = (uint32_t)mk;
-  const int32_t argmax = am0 == 0x7fffffff ? 0 : am0;  // slices are in index order
-  if (sp.greedy) {
-    if (tid == 0) a.out[row] = argmax;
-    return;
+  // ---- slice records (wave 0; lane l holds slices l and l + 64): row
+  // maximum, its first index, slice offsets, slice masses in units of the
+  // row maximum, the window weights.
+  double wall = 0.0;  // (wave 0) mass of the whole row: plain rows and top-p without top-k
+  if (wave == 0) {
+    const bool in0 = lane < S, in1 = lane + 64 < S;
+    const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull, r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
+    const int32_t k0 = (int32_t)(uint32_t)r0, k1 = (int32_t)(uint32_t)r1;
+    const int32_t mk = wave_max_i32(max(k0, k1));
+    const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
+                                        (in1 && k1 == mk) ? (int32_t)(r1 >> 32) : 0x7fffffff));
+    const int32_t argmax = am == 0x7fffffff ? 0 : am;  // slices are in index order
+    if (sp.greedy) {
+      if (lane == 0) a.out[row] = argmax;
+    } else {
+      const uint32_t rkmax = (uint32_t)mk;
+      const float lmax = key16_value(rkmax);
+      if (in0) sl_delta[lane] = mk - k0;
+      if (in1) sl_delta[lane + 64] = mk - k1;
+      double m0 = 0.0, m1 = 0.0;
+      if (need_mass) {
+        if (in0) m0 = ws.masses[slot0 + lane] * (double)fast_exp2((fmaxf(key16_value((uint32_t)k0), -1e30f) - lmax) * c2);
+        if (in1) m1 = ws.masses[slot0 + lane + 64] * (double)fast_exp2((fmaxf(key16_value((uint32_t)k1), -1e30f) - lmax) * c2);
+        wall = wave_sum_f64(m0 + m1);
+      }
+      if (plain) {
+        sl_mass[lane] = m0;
+        sl_mass[lane + 64] = m1;
+      } else {
+#pragma unroll
+        for (int e = 0; e < kHistBins / kWave; ++e) {
+          const int b = e * kWave + lane;
+          s.hist[b] = 0;
+          s.wtab[b] = (uint32_t)b <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)b), lmax, c2) : 0.f;
+        }
+      }
+      if (lane == 0) {
+        h_i[0] = mk;
+        h_i[1] = argmax;
+      }
+    }
   }
-  if (tid < S) sl_delta[tid] = mk - skmax;
+  if (sp.greedy) return;
+  __syncthreads();  // 1
+  const uint32_t rkmax = (uint32_t)h_i[0];
+  const int32_t argmax = h_i[1];
   const float lmax = key16_value(rkmax);
-  // slice masses in units of the row maximum (plain rows and top-p over the whole row)
-  double my_mass = (need_mass && tid < S)
-                       ? smass * (double)fast_exp2((fmaxf(key16_value((uint32_t)skmax), -1e30f) - lmax) * c2)
-                       : 0.0;
 
-  int dcut = -1;          // cut bin (rows with top-k or top-p); tokens with d < dcut are kept
-  uint32_t take = 0;      // tokens of bin dcut kept: the first ones in index order
-  int32_t cut_before = 0; // cut-bin tokens of the slices before this thread's slice
+  int dcut = -1;      // cut bin (rows with top-k or top-p); tokens with d < dcut are kept
+  uint32_t take = 0;  // tokens of bin dcut kept: the first ones in index order
   if (!plain) {
     // ---- the row histogram
-    if (tid < kHistBins) {
-      s.hist[tid] = 0;
-      s.wtab[tid] = (uint32_t)tid <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)tid), lmax, c2) : 0.f;
-    }
-    const double wall = need_mass ? block_sum_f64(s, my_mass) : 0.0;  // (starts and ends with a barrier)
-    if (!need_mass) __syncthreads();
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
       const int q = e * kFinishThreads + tid;
@@ -1010,7 +1036,7 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // 2
     // ---- cuts (wave 0)
     if (wave == 0) {
       auto hc = [&](int b) { return s.hist[b]; };
@@ -1055,7 +1081,7 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
         h_i[4] = (int32_t)tk2;
       }
     }
-    __syncthreads();
+    __syncthreads();  // 3
     dcut = h_i[3];
     take = (uint32_t)h_i[4];
     if (dcut < 0) {  // the cut lies below the window
@@ -1065,11 +1091,11 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
       if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
       return;
     }
-    // ---- kept mass of every slice: bins above the cut, plus its share of the
-    // first `take` tokens of the cut bin (slices in index order). The 32 units
-    // of a slice are one half-wave; a unit's eight bins (exact counts times
-    // fp32 weights) and the half-wave tree add in fp32 (relative error
-    // below 1e-6 of the slice's kept mass).
+    // ---- kept mass of every slice: bins above the cut, plus (below) its
+    // share of the first `take` tokens of the cut bin (slices in index
+    // order). The 32 units of a slice are one half-wave; a unit's eight bins
+    // (exact counts times fp32 weights) and the half-wave tree add in fp32
+    // (relative error below 1e-6 of the slice's kept mass).
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
       if (e * kFinishThreads < NU) {  // uniform
@@ -1091,47 +1117,66 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
         }
       }
     }
-    __syncthreads();
-    const int32_t cc = tid < S ? sl_cut[tid] : 0;
-    int32_t tot_cut;
-    cut_before = block_excl_scan_i32(s, cc, &tot_cut);
-    const int32_t t_kept = min(max((int32_t)take - cut_before, 0), cc);
-    my_mass = tid < S ? sl_mass[tid] + (double)t_kept * (double)s.wtab[dcut] : 0.0;
+    __syncthreads();  // 4
   }
 
-  // ---- the slice holding the draw
-  {
-    double incl, wtot;
-    const double excl = block_scan_f64(s, my_mass, &incl, &wtot);
-    const double target = (double)sp.u * wtot;
-    const int32_t last = block_reduce_i32(s, my_mass > 0.0 ? tid : -1, true);
-    if (tid == 0) {
-      h_i[2] = -1;
-      h_f[0] = INFINITY;
+  // ---- the slice holding the draw (wave 0; lane l holds slices l and l + 64)
+  if (wave == 0) {
+    const bool in0 = lane < S, in1 = lane + 64 < S;
+    int32_t cc0 = 0, cc1 = 0;
+    if (!plain) {
+      cc0 = in0 ? sl_cut[lane] : 0;
+      cc1 = in1 ? sl_cut[lane + 64] : 0;
     }
-    __syncthreads();
-    if (my_mass > 0.0 && excl <= target && target < incl) {  // at most one thread
-      h_i[2] = tid;
-      h_f[0] = target - excl;
-      h_i[5] = cut_before;
+    // cut-bin tokens of the slices before each slice
+    const int32_t i0 = wave_incl_scan_i32(cc0, lane);
+    const int32_t i1 = lane_i32(i0, 63) + wave_incl_scan_i32(cc1, lane);
+    const int32_t cb0 = i0 - cc0, cb1 = i1 - cc1;
+    double ms0 = in0 ? sl_mass[lane] : 0.0, ms1 = in1 ? sl_mass[lane + 64] : 0.0;
+    if (!plain) {
+      const double wcut = (double)s.wtab[dcut];
+      ms0 += (double)min(max((int32_t)take - cb0, 0), cc0) * wcut;
+      ms1 += (double)min(max((int32_t)take - cb1, 0), cc1) * wcut;
     }
-    __syncthreads();
-    const bool none = h_i[2] < 0;  // rounding left the target past every slice
-    __syncthreads();
-    if (none) {  // the last slice with mass
-      if (tid == 0) {
-        h_i[2] = max(last, 0);
-        h_f[0] = INFINITY;
-      }
-      if (tid == max(last, 0)) h_i[5] = cut_before;
-      __syncthreads();
+    // running kept mass over the slices in index order; consecutive slices'
+    // [excl, incl) intervals meet exactly
+    double ex0, ex1;
+    const double in_0 = wave_scan_f64(ms0, lane, &ex0);
+    const double t0 = lane_f64(in_0, 63);
+    const double in_1 = wave_scan_f64(ms1, lane, &ex1) + t0;
+    ex1 += t0;
+    const double target = (double)sp.u * lane_f64(in_1, 63);
+    const uint64_t b0 = __ballot(ms0 > 0.0 && ex0 <= target && target < in_0);
+    const uint64_t b1 = __ballot(ms1 > 0.0 && ex1 <= target && target < in_1);
+    int32_t psl, tb;
+    double rem;
+    if (b0) {
+      const int l = __ffsll((unsigned long long)b0) - 1;
+      psl = l;
+      rem = target - lane_f64(ex0, l);
+      tb = lane_i32(cb0, l);
+    } else if (b1) {
+      const int l = __ffsll((unsigned long long)b1) - 1;
+      psl = 64 + l;
+      rem = target - lane_f64(ex1, l);
+      tb = lane_i32(cb1, l);
+    } else {  // rounding left the target past every slice: the last slice with mass
+      psl = max(wave_max_i32(max(ms0 > 0.0 ? lane : -1, ms1 > 0.0 ? lane + 64 : -1)), 0);
+      rem = INFINITY;
+      tb = psl < 64 ? lane_i32(cb0, psl) : lane_i32(cb1, psl - 64);
+    }
+    if (lane == 0) {
+      h_i[2] = psl;
+      h_f[0] = rem;
+      h_i[5] = tb;
     }
   }
+  __syncthreads();  // 5
   const int psl = h_i[2];
   const double rem = h_f[0];
   const int32_t tie_base = h_i[5];
 
-  // ---- the draw inside slice psl: thread t scans tokens [16t, 16t + 16), in index order
+  // ---- the draw inside slice psl: thread t scans tokens [8t, 8t + 8), in index order
   const int tok0 = psl * kSliceTokens + 8 * kDrawChunks * tid;
   const uint32_t cut_key = rkmax - (uint32_t)max(dcut, 0);
   u32x4 x[kDrawChunks];
@@ -1154,8 +1199,12 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     for (int i = 0; i < kDrawChunks; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) n += ((x[i][j] & 0xffffu) == cut_key) + ((x[i][j] >> 16) == cut_key);
-    int32_t tot;
-    rank0 = tie_base + block_excl_scan_i32(s, n, &tot);
+    const int32_t inc = wave_incl_scan_i32(n, lane);
+    if (lane == 63) w_cnt[wave] = inc;
+    __syncthreads();  // 6
+    int32_t off = tie_base;
+    for (int w = 0; w < wave; ++w) off += w_cnt[w];
+    rank0 = off + inc - n;
   }
   // kept weight of token e of chunk i; `rank` counts the cut-bin tokens seen
   auto kept_w = [&](const u32x4& xi, int e, int32_t& rank) -> float {
@@ -1165,6 +1214,7 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     const uint32_t vw = bf16x2_from_keys(kw);
     return row_weight(__uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16)), lmax, c2);
   };
+  float kw[kDrawChunks][8];  // kept weights of this thread's tokens
   double own = 0.0;
   int32_t lastk = -1;
   {
@@ -1174,34 +1224,44 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
       float cs = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float w = kept_w(x[i], e, rank);
-        if (w > 0.f) lastk = tok0 + 8 * i + e;
-        cs += w;
+        kw[i][e] = kept_w(x[i], e, rank);
+        if (kw[i][e] > 0.f) lastk = tok0 + 8 * i + e;
+        cs += kw[i][e];
       }
       own += (double)cs;
     }
   }
-  double incl, tot;
-  const double excl = block_scan_f64(s, own, &incl, &tot);
-  const int32_t lk = block_reduce_i32(s, lastk, true);  // the slice's last kept token
+  // running kept mass over the threads in index order: wave scans, then the
+  // waves before (accumulated in wave order, so consecutive threads'
+  // [excl, incl) intervals meet exactly)
+  double exw;
+  const double inw = wave_scan_f64(own, lane, &exw);
+  const int32_t lkw = wave_max_i32(lastk);
+  if (lane == 63) w_mass[wave] = inw;
+  if (lane == 0) w_last[wave] = lkw;
   if (tid == 0) s.result = -1;
-  __syncthreads();
+  __syncthreads();  // 7
+  double offm = 0.0;
+  int32_t lk = -1;  // the slice's last kept token
+  for (int w = 0; w < kFinishWaves; ++w) {
+    if (w < wave) offm += w_mass[w];
+    lk = max(lk, w_last[w]);
+  }
+  const double excl = offm + exw, incl = offm + inw;
   if (own > 0.0 && excl <= rem && rem < incl) {  // exactly one thread: the intervals meet bit for bit
-    int32_t rank = rank0, res = -1;
+    int32_t res = -1;
     double run = excl;
 #pragma unroll
     for (int i = 0; i < kDrawChunks; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = kept_w(x[i], e, rank);
-        if (res < 0 && w > 0.f) {
-          run += (double)w;
+      for (int e = 0; e < 8; ++e)
+        if (res < 0 && kw[i][e] > 0.f) {
+          run += (double)kw[i][e];
           if (run > rem) res = tok0 + 8 * i + e;
         }
-      }
     s.result = res >= 0 ? res : lastk;  // rounding ran past the thread's tokens: its last kept one
   }
-  __syncthreads();
+  __syncthreads();  // 8
   const int32_t r = s.result >= 0 ? s.result : lk;
   if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
 }
