@@ -808,10 +808,10 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
                                                      (int64_t)row * a.row_stride);
   const int last_chunk = (V - 1) / 8;
   const int t0s = slice * kSliceTokens;
-  u32x4 key[kSliceRounds];
+  u32x4 raw[kSliceRounds], key[kSliceRounds];
 #pragma unroll
   for (int i = 0; i < kSliceRounds; ++i)  // indices clamped to the row's last chunk: reads stay in the row
-    key[i] = __builtin_nontemporal_load(crow + min(t0s / 8 + i * kSliceThreads + tid, last_chunk));
+    raw[i] = __builtin_nontemporal_load(crow + min(t0s / 8 + i * kSliceThreads + tid, last_chunk));
   if (need_hist)  // ordered before the atomics by the barrier of the block maximum
     for (int b = tid; b < kHistBins + kWave; b += kSliceThreads) hist[b] = 0;
   // Biased keys; a token at or past V gets key 0, below every real key, so
@@ -822,7 +822,7 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
     for (int i = 0; i < kSliceRounds; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t k = bf16x2_keys(key[i][j]);
+        uint32_t k = bf16x2_keys(raw[i][j]);
         const int tok = t0s + 8 * (i * kSliceThreads + tid) + 2 * j;
         if (tok >= V) k = 0u;
         else if (tok + 1 >= V) k &= 0xffffu;
@@ -832,7 +832,7 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 #pragma unroll
     for (int i = 0; i < kSliceRounds; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) key[i][j] = bf16x2_keys(key[i][j]);
+      for (int j = 0; j < 4; ++j) key[i][j] = bf16x2_keys(raw[i][j]);
   }
   u16x2 mx = {0, 0};
 #pragma unroll
@@ -840,16 +840,17 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, as_u16x2(key[i][j]));
   const uint32_t tk = max((uint32_t)mx.x, (uint32_t)mx.y);
-  // mass relative to this thread's maximum (rescaled below): fp32 within a
-  // chunk, fp64 above
+  // mass relative to this thread's maximum (rescaled below), from the raw
+  // bf16 values (the keys only mark the tail's missing tokens): fp32 within
+  // a chunk, fp64 above
   double mass = 0.0;
   if (need_mass) {
     const float c2 = sp.c2, off = -fmaxf(key16_value(tk), -1e30f) * c2;
-    auto chunk_mass = [&](const u32x4& k, bool masked) {
+    auto chunk_mass = [&](const u32x4& x, const u32x4& k, bool masked) {
       float cs = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = bf16x2_from_keys(k[j]);
+        const uint32_t w = x[j];
         float w0 = fast_exp2(fmaf(__uint_as_float(w << 16), c2, off));
         float w1 = fast_exp2(fmaf(__uint_as_float(w & 0xffff0000u), c2, off));
         if (masked) {  // key 0: no token
@@ -863,10 +864,10 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
     };
     if (tail) {
 #pragma unroll
-      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(key[i], true);
+      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(raw[i], key[i], true);
     } else {
 #pragma unroll
-      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(key[i], false);
+      for (int i = 0; i < kSliceRounds; ++i) mass += (double)chunk_mass(raw[i], key[i], false);
     }
   }
   const uint32_t wk = (uint32_t)wave_max_i32((int32_t)tk);
@@ -895,18 +896,33 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
   found = wave_min_i32(found);
   if (lane == 0) wave_i[wave] = found;
   // window histogram (keys > th, bin d = kmax - key); a token outside the
-  // window goes to this lane's discard bin, so no lane ever branches
+  // window goes to a discard bin, so no lane ever branches. Outside the tail
+  // every key is in [1, kmax]: d = kmax - key for two tokens at once, and
+  // min(d, 256 + lane) sends a token outside the window to a discard bin
+  // (this lane's, or for d in [256, 256 + lane) another lane's).
   if (need_hist) {
-    const uint32_t th = kmax > (uint32_t)kHistBins ? kmax - (uint32_t)kHistBins : 0u;
-    const uint32_t discard = kHistBins + lane;
+    if (tail) {
+      const uint32_t th = kmax > (uint32_t)kHistBins ? kmax - (uint32_t)kHistBins : 0u;
+      const uint32_t discard = kHistBins + lane;
 #pragma unroll
-    for (int i = 0; i < kSliceRounds; ++i)
+      for (int i = 0; i < kSliceRounds; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = key[i][j] & 0xffffu, hi = key[i][j] >> 16;
-        atomicAdd(&hist[lo > th ? kmax - lo : discard], 1u);
-        atomicAdd(&hist[hi > th ? kmax - hi : discard], 1u);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = key[i][j] & 0xffffu, hi = key[i][j] >> 16;
+          atomicAdd(&hist[lo > th ? kmax - lo : discard], 1u);
+          atomicAdd(&hist[hi > th ? kmax - hi : discard], 1u);
+        }
+    } else {
+      const u16x2 km2 = as_u16x2(kmax * 0x10001u), disc2 = as_u16x2((uint32_t)(kHistBins + lane) * 0x10001u);
+#pragma unroll
+      for (int i = 0; i < kSliceRounds; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t d = as_u32(__builtin_elementwise_min(km2 - as_u16x2(key[i][j]), disc2));
+          atomicAdd(&hist[d & 0xffffu], 1u);
+          atomicAdd(&hist[d >> 16], 1u);
+        }
+    }
   }
   __syncthreads();
   const int64_t slot = (int64_t)row * S + slice;  // the row's slices in index order
