@@ -10,7 +10,10 @@ workload is the 256-request decode batch (device_len ~ U[1024, 8192], bf16,
 from 0.9 x free HBM at 114688 bytes per page; logits [256, 151936], 128
 greedy rows and 128 at T=0.7, top_p=0.9). The causal extend kernel is timed
 on the 8-request prefill case (extend_len ~ U[512, 4096] over a 0-50% cached
-prefix) over the same pool.
+prefix) over the same pool. After that pool is freed, the mixed batch (240
+decode requests with device_len ~ U[4096, 32768] plus two 2048-token prefill
+chunks, page_size 16, sampler at T=1, top_k=50, top_p=0.95) is timed per
+launch and as one step; its figures go into the components.
 
 Inputs are resident in HBM before timing. The pool's contents are seeded
 N(0, 1) values written by torch on the device; lengths, page tables, q,
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3])
     ap.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--skip-extend", action="store_true")
+    ap.add_argument("--skip-mixed", action="store_true",
+                    help="skip the mixed chunked-prefill + decode batch (page_size 16) timed after the main step")
     ap.add_argument("--copy-calib", action="store_true",
                     help="before warm-up, run plain 1 GiB device copies (untimed) whose counter "
                          "readings calibrate FETCH_SIZE/WRITE_SIZE")
@@ -242,6 +247,11 @@ def main():
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
+    if not args.skip_mixed:
+        del pool, kp, vp, logit_bufs, step
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["components"].update(bench_mixed(torch, pkv, dev, args))
     print(json.dumps(result), flush=True)
 
 
@@ -280,6 +290,99 @@ def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
             "extend_tflops": round(tflops, 1), "extend_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "extend_workload": f"8 requests, extend_len {int(E.min())}..{int(E.max())}, "
                                f"prefix {int(C.min())}..{int(C.max())}, bf16, page_size 1"}
+
+
+def bench_mixed(torch, pkv, dev, args):
+    """The mixed batch: 240 decode requests (device_len ~ U[4096, 32768]) and 2
+    prefill chunks of 2048 tokens over cached prefixes of 2048 j tokens, bf16,
+    page_size 16, one layer's pool sized 1.25 x the pages the batch uses; the
+    sampler over [242, 151936] logits, every row at T=1, top_k=50,
+    top_p=0.95. One decode launch, one extend launch and the sampler on one
+    stream: timed apart and as one step."""
+    from workloads import (HEAD_DIM, HKV, HQ, config, default_num_pages, draw_lengths, draw_page_table,
+                           draw_q, draw_sampling_params, draw_uniforms)
+    cfg = config(5)
+    C, S = draw_lengths(cfg)
+    nump = default_num_pages(cfg, S)
+    table = draw_page_table(cfg, S, nump)
+    E = (S - C).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(E)])
+    dec = np.nonzero(E == 1)[0].astype(np.int32)
+    ext = np.nonzero(E > 1)[0].astype(np.int32)
+    q_all = draw_q(cfg, C, S).view(np.int16)
+    q_dec = torch.from_numpy(q_all[cu[dec]]).to(dev).view(torch.bfloat16)
+    q_ext = torch.from_numpy(np.concatenate([q_all[cu[r]:cu[r + 1]] for r in ext])).to(dev).view(torch.bfloat16)
+    num_slots = (nump + 1) * cfg.page_size
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+    kp = torch.empty((num_slots, HKV, HEAD_DIM), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    vp = torch.empty((num_slots, HKV, HEAD_DIM), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    d_table = torch.from_numpy(table).to(dev)
+    d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
+    d_dec, d_ext = torch.from_numpy(dec).to(dev), torch.from_numpy(ext).to(dev)
+    Cd, Sd = d_C[d_dec].contiguous(), d_S[d_dec].contiguous()
+    Ce, Se = d_C[d_ext].contiguous(), d_S[d_ext].contiguous()
+    dec_kv = int(S[dec].sum())
+    max_ext = int(E[ext].max())
+    ws = torch.empty(pkv.decode_workspace_size(len(dec), HQ, dec_kv), dtype=torch.uint8, device=dev)
+    o_dec, o_ext = torch.empty_like(q_dec), torch.empty_like(q_ext)
+    rows = cfg.rows
+    bufs = [(torch.randn((rows, cfg.vocab), generator=gen, device=dev) * cfg.logit_sigma).to(torch.bfloat16)
+            for _ in range(4)]
+    T, K, P = pkv.prepare_sampling(*zip(*draw_sampling_params(cfg)), vocab=cfg.vocab)
+    to = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    d_T, d_K, d_P, d_u = to(T), to(K), to(P), to(draw_uniforms(cfg))
+    tokens = torch.empty(rows, dtype=torch.int32, device=dev)
+    s_ws = pkv.sample_workspace(rows, cfg.vocab, dev)
+    ps = cfg.page_size
+
+    def decode():
+        pkv.paged_attention_decode(q_dec, kp, vp, d_table, Cd, Sd, table_idx=d_dec, max_total_kv=dec_kv,
+                                   page_size=ps, out=o_dec, workspace=ws)
+
+    def extend():
+        pkv.paged_attention_extend(q_ext, kp, vp, d_table, Ce, Se, table_idx=d_ext, max_extend=max_ext,
+                                   page_size=ps, out=o_ext)
+
+    def sample(i):
+        pkv.sample(bufs[i % len(bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    n = max(10, args.steps // 4)
+    dec_us = timed(lambda i: decode(), n)
+    ext_us = timed(lambda i: extend(), n)
+    smp_us = timed(sample, 4 * n)
+    step_us = timed(lambda i: (decode(), extend(), sample(i)), n)
+    kv_bytes = dec_kv * HKV * HEAD_DIM * 2 * 2
+    flops = 4.0 * HEAD_DIM * HQ * float(np.sum(E[ext] * C[ext] + E[ext] * (E[ext] + 1) / 2.0))
+    dec_gbs = kv_bytes / (dec_us * 1e-6) / 1e9
+    ext_tf = flops / (ext_us * 1e-6) / 1e12
+    smp_gbs = rows * cfg.vocab * 2 / (smp_us * 1e-6) / 1e9
+    log(f"mixed242: decode {dec_us:.1f} us ({dec_gbs:.0f} GB/s) | extend {ext_us:.1f} us ({ext_tf:.0f} TFLOP/s) "
+        f"| sample {smp_us:.1f} us ({smp_gbs:.0f} GB/s) | step {step_us:.1f} us")
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the mixed batch")
+    return {"mixed242_workload": f"240 decode rows (device_len {int(S[dec].min())}..{int(S[dec].max())}, "
+                                 f"sum {dec_kv}) + 2 prefill chunks of 2048 over prefixes {C[ext].tolist()}, "
+                                 f"page_size 16, {num_slots} slots; sampler [242, {cfg.vocab}] T=1 k=50 p=0.95",
+            "mixed242_decode_us": round(dec_us, 2), "mixed242_decode_kv_gbs": round(dec_gbs, 1),
+            "mixed242_decode_frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "mixed242_extend_us": round(ext_us, 2), "mixed242_extend_tflops": round(ext_tf, 1),
+            "mixed242_extend_frac_mfma": round(ext_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mixed242_sample_us": round(smp_us, 2), "mixed242_sampler_gbs": round(smp_gbs, 1),
+            "mixed242_sampler_tokens_per_s": round(rows / (smp_us * 1e-6), 1),
+            "mixed242_step_us": round(step_us, 2)}
 
 
 def cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg):

@@ -180,3 +180,53 @@ def test_extend_prefill_case_sampled_rows():
     mx, rel = check_attention(np.stack(gots), np.stack(refs), dt, "extend8 sampled")
     print(f"  {len(gots)} rows: max|d|={mx:.3e} relL2={rel:.3e}")
     assert pkv.read_faults() == 0
+
+
+def test_extend_mixed_batch_chunks_full_size():
+    """The two 2048-token prefill chunks of the mixed batch (page_size 16,
+    cached prefixes of 2048 j tokens) at full size, picked from the batch's
+    page table through table_idx, in the launch configuration the benchmark
+    times. The pool is drawn on the device; store_kv writes the chunks' new
+    rows first; the oracle checks 24 seeded positions per chunk against the
+    pool rows read back after the store."""
+    from workloads import default_num_pages, draw_lengths, draw_page_table, draw_q
+    cfg = config(5)
+    C, S = draw_lengths(cfg)
+    nump = default_num_pages(cfg, S)
+    table = draw_page_table(cfg, S, nump)
+    q_all = draw_q(cfg, C, S)
+    E = (S - C).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(E)])
+    ext = np.nonzero(E > 1)[0].astype(np.int32)
+    q = np.concatenate([q_all[cu[r]:cu[r + 1]] for r in ext])
+    Ce, Se = C[ext], S[ext]
+    num_slots = (nump + 1) * cfg.page_size
+    print(f"extend mixed-batch chunks: C={Ce.tolist()} S={Se.tolist()} slots {num_slots}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(2005)
+    kp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    n_new = int((Se - Ce).sum())
+    nk = torch.randn((n_new, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    nv = torch.randn((n_new, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    out_loc = np.concatenate([table[r, C[r]:S[r]] for r in ext]).astype(np.int32)
+    pkv.store_kv(kp, vp, to_dev(out_loc), nk, nv, page_size=cfg.page_size)
+    o = pkv.paged_attention_extend(to_dev(q, "bf16"), kp, vp, to_dev(table), to_dev(Ce), to_dev(Se),
+                                   table_idx=to_dev(ext), max_extend=int((Se - Ce).max()),
+                                   page_size=cfg.page_size)
+    torch.cuda.synchronize()
+    got = to_host(o)
+    rng = np.random.default_rng(5)
+    cq = np.concatenate([[0], np.cumsum(Se - Ce)])
+    gots, refs = [], []
+    for i, r in enumerate(ext):
+        slots = torch.from_numpy(table[r, :S[r]].astype(np.int64)).cuda()
+        K = oracle.widen(to_host(kp.index_select(0, slots)), "bf16")
+        V = oracle.widen(to_host(vp.index_select(0, slots)), "bf16")
+        Er = int(Se[i] - Ce[i])
+        for t in np.unique(np.concatenate([[0, Er - 1], rng.integers(0, Er, 22)])):
+            qrow = oracle.widen(q[cq[i] + t:cq[i] + t + 1], "bf16")
+            refs.append(attention_request(qrow, K[:Ce[i] + t + 1], V[:Ce[i] + t + 1], int(Ce[i] + t))[0])
+            gots.append(got[cq[i] + t])
+    mx, rel = check_attention(np.stack(gots), np.stack(refs), "bf16", "mixed-batch chunks sampled")
+    print(f"  {len(gots)} rows: max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0
