@@ -196,7 +196,7 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  * if rounding finds none).
  *   ws        device workspace of pkv_sample_workspace_size(bs, vocab) bytes,
  *             16-byte aligned; required for bf16 logits (per-slice records,
- *             sub-slice masses and key histograms, written by the first of the
+ *             slice masses and key histograms, written by the first of the
  *             two kernels and read by the second), unused for fp32. Its
  *             contents need no initialisation and are not kept between
  *             calls; calls that share a workspace must not overlap in time

@@ -7,29 +7,29 @@
 // the rest. Greedy rows (T <= 1e-6, or no temperature array) are argmax.
 //
 // The pages' GPU path calls FlashInfer's rejection-sampling kernels; this is
-// a different, exact design with one workgroup per row. Ranking uses
+// a different, exact design. Ranking uses
 // order-preserving integer keys of the logits (-0 ranks with +0), so argmax
 // and top-k are exact and ties go to the lower index; weights are
 // w(l) = exp2((l - l_max) * log2(e) / T), so equal logits weigh the same.
 //
 // bf16 rows (slice kernel + finish kernel):
 // * Each row is cut into slices of 8192 tokens, one workgroup per slice
-//   (about 19 per row on a 151936-token vocabulary, so the chip is full even
-//   for small batches). A slice reads its tokens once, turns them into
+//   (19 per row on a 151936-token vocabulary, so the chip is full even for
+//   small batches). A slice reads its tokens once, turns them into
 //   order-preserving biased 16-bit keys with packed 16-bit integer ops (-0
-//   and +0 share a key) and hands over its maximum, the first index of it,
-//   its mass (rows whose draw or top-p runs over the whole row) and, in
-//   index order, every token within 128 key values of its maximum.
-// * The finish kernel (one workgroup per row) takes the row maximum, keeps
-//   the handed-over tokens within 128 keys of it (a superset is handed over,
-//   since no slice maximum exceeds the row's) in an LDS list in index order,
-//   and finds the top-k threshold and the top-p cut from a count histogram of
-//   the list: all tokens of a bin share one key and one weight. The ties at
-//   the cut (the first n equal-key tokens in index order are kept) and the
-//   draw (kept weights in index order, first running mass > u * W) run on
-//   the list. Rows with neither top-k nor top-p locate their slice by the
-//   slices' masses and scan it. Cuts below the window and lists that
-//   overflow take the generic path below over the row in memory.
+//   and +0 share a key) and hands over its maximum key and the first index
+//   of it, its mass relative to its maximum (rows without top-k) and a
+//   256-bin count histogram of the keys within 255 of its maximum (rows with
+//   top-k or top-p).
+// * The finish kernel (one workgroup per row) takes the row maximum and
+//   shifts every slice histogram by the slice's distance to it, so the bins
+//   add into the row's window histogram. All tokens of a bin share one key
+//   and one weight: the top-k threshold and the top-p cut come from counts
+//   times weights, the ties at the cut keep the first n equal-key tokens in
+//   index order, and every slice's kept mass follows from its histogram.
+//   The draw (kept weights in index order, first running mass > u * W)
+//   picks one slice by those masses and scans its 8192 tokens. Cuts below
+//   the window take the generic path below over the row in memory.
 //
 // fp32 rows (the memory kernel) and the generic path: every
 // pass reads 16-byte chunks from memory (wave w owns a contiguous chunk range,
@@ -99,7 +99,6 @@ struct SampleElem<float> {
 
 constexpr int kSampleThreads = 512;
 constexpr int kSampleWaves = kSampleThreads / kWave;
-constexpr int kSampleWindow = 128;      // bf16: key values at or below the maximum in the window list
 constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave with a group-mass slot
 
 // ---------------------------------------------------------------- wave helpers

@@ -168,7 +168,7 @@ def test_sample_zero_rows_is_noop(L):
 
 
 def test_sample_workspace_size(L):
-    """bf16 rows need slice records and window lists; the size grows with the batch."""
+    """bf16 rows need slice records, masses and histograms; the size grows with the batch."""
     a, b = L.pkv_sample_workspace_size(1, 151936), L.pkv_sample_workspace_size(256, 151936)
     assert 0 < a < b and L.pkv_sample_workspace_size(0, 151936) == 0
 

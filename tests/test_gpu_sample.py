@@ -243,7 +243,7 @@ def test_workspace_reused_across_calls():
 
 
 def test_largest_bf16_vocabulary():
-    """The bf16 limit (2^20 tokens: 128 slices, 512 sub-slices per row), with
+    """The bf16 limit (2^20 tokens: 128 slices per row), with
     top-p, top-k + top-p and plain rows; one token past it is refused."""
     V, bs = 1 << 20, 3
     rng = _rng("max-vocab")
