@@ -20,11 +20,13 @@ Sources (the pages are cited by title and section):
   always token-granular).
 * "第 0 步：一个能跑的最小推理引擎" (mini-sglang handbook, step 0) -- the
   dense reference ``attention`` function (GQA by repeat_interleave, scale
-  1/sqrt(D), causal mask on absolute positions).
+  1/sqrt(D), causal mask on absolute positions); its ``rmsnorm`` and ``rope``
+  operators and the per-head q/k norm before the rotation.
 * "Mini-SGLang 完整剖析" -- sections 4.4.3 (KV pool layout, store_kv scatter),
-  4.6.4/4.6.5 (page_size > 1 conversion, cu_seqlens), 4.6.7 (store_kv runs
-  before the attention kernel), 4.8.4-4.8.6 (greedy rule, sparse argument
-  construction), 4.9.4 (store kernel shape contract), 5.2 (worked page counts).
+  4.6.4/4.6.5 (page_size > 1 conversion, cu_seqlens), 4.6.7 (q/k norm and
+  RoPE in place, then store_kv runs before the attention kernel), 4.8.4-4.8.6
+  (greedy rule, sparse argument construction), 4.9.4 (store kernel shape
+  contract), 5.2 (worked page counts).
 * "Mini-SGLang 源码解析（四）：GPU 计算引擎系统" -- sections 14.3/14.4
   (greedy fast path, top-k renormalisation example).
 
@@ -40,10 +42,11 @@ from .sampling_params import SamplingParams, is_greedy, prepare
 from .store_kv import store_kv
 from .attention import gather_kv, attention_request, attention_decode, attention_extend
 from .sampler import sample, sample_row, DELTA
+from .qk_norm_rope import rmsnorm, rope, rope_angles, rope_inv_freq, qk_norm_rope
 
 __all__ = [
     "widen", "bf16_bits_to_f64", "Req", "bytes_per_page", "num_pages",
     "SamplingParams", "is_greedy", "prepare", "store_kv", "gather_kv",
     "attention_request", "attention_decode", "attention_extend", "sample",
-    "sample_row", "DELTA",
+    "sample_row", "DELTA", "rmsnorm", "rope", "rope_angles", "rope_inv_freq", "qk_norm_rope",
 ]
