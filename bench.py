@@ -244,6 +244,7 @@ def main():
 
     if not args.skip_extend:
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
+    result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
@@ -290,6 +291,53 @@ def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
             "extend_tflops": round(tflops, 1), "extend_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "extend_workload": f"8 requests, extend_len {int(E.min())}..{int(E.max())}, "
                                f"prefix {int(C.min())}..{int(C.max())}, bf16, page_size 1"}
+
+
+def bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
+    """q/k RMSNorm + rotary embedding + K/V store, fused (the step before
+    attention): on the 256 new tokens of the decode batch (positions
+    device_len - 1, slots from its page table) and on the 19,892 new tokens
+    of the 8-request prefill (positions cached_len + t, slots from its page
+    table), over layer 0 of the pool. Bytes per token: q read and written
+    (16 heads), k and v read, K and V rows written (8 heads), bf16: 16 KiB."""
+    from workloads import HEAD_DIM, HKV, HQ, config, draw_lengths, draw_page_table
+    kp, vp = pool[0, 0], pool[1, 0]
+    wq = (torch.rand(HEAD_DIM, generator=gen, device=dev) + 0.5).to(torch.bfloat16)
+    wk = (torch.rand(HEAD_DIM, generator=gen, device=dev) + 0.5).to(torch.bfloat16)
+    cases = {}
+    C4, S4 = draw_lengths(config(4))
+    t4 = draw_page_table(config(4), S4, num_pages)
+    for name, pos, loc in (
+            ("decode256", (S - 1).astype(np.int32), table[np.arange(len(S)), S - 1].astype(np.int32)),
+            ("prefill8", np.concatenate([np.arange(c, s) for c, s in zip(C4, S4)]).astype(np.int32),
+             np.concatenate([t4[r, C4[r]:S4[r]] for r in range(len(S4))]).astype(np.int32))):
+        n = len(pos)
+        q = torch.randn((n, HQ, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((n, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((n, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        qo = torch.empty_like(q)
+        d_pos, d_loc = torch.from_numpy(pos).to(dev), torch.from_numpy(loc).to(dev)
+        run = lambda: pkv.qk_norm_rope_store_kv(kp, vp, d_loc, q, k, v, d_pos, wq, wk, q_out=qo)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        reps = max(20, args.steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = n * 2 * (2 * HQ + 4 * HKV) * HEAD_DIM
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"qk norm+rope+store {name}: {n} tokens, {us:.1f} us, {gbs:.0f} GB/s")
+        cases[f"qk_rope_store_{name}_us"] = round(us, 2)
+        cases[f"qk_rope_store_{name}_gbs"] = round(gbs, 1)
+        cases[f"qk_rope_store_{name}_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the qk norm/rope/store timing")
+    return cases
 
 
 def bench_mixed(torch, pkv, dev, args):

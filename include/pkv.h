@@ -4,7 +4,9 @@
  * The C ABI of libpkv.so: the data-parallel hot path of one step of a
  * mini-SGLang-style engine's forward_batch, per layer:
  *
- *   1. pkv_store_kv                 scatter this step's K/V rows into the paged pool;
+ *   1. pkv_store_kv                 scatter this step's K/V rows into the paged pool
+ *      (pkv_qk_norm_rope_store_kv   the same store fused with Qwen3's per-head q/k
+ *                                   RMSNorm and the rotary embedding);
  *   2. pkv_paged_attention_decode   GQA attention of one new token per request
  *      pkv_paged_attention_extend   causal GQA attention of a chunk of new tokens
  *                                   over a cached prefix (prefill / extend);
@@ -117,6 +119,37 @@ typedef struct {
 int pkv_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,
                  const void* k, int64_t k_stride, const void* v, int64_t v_stride,
                  void* stream);
+
+/*
+ * q/k norm + rotary embedding + store_kv, fused ([TINY] its rmsnorm and rope
+ * operators and the layer function: Qwen3 normalises each q and k head with
+ * its own weight, then rotates it; [DISS] 4.6.7: the layer does both in
+ * place before the attention backend stores k and v). For token i in [0, n)
+ * at position p = positions[i], every head vector x of 128 dims is
+ *   y = w * x / sqrt(mean(x^2) + eps)          (w = q_norm_weight or k_norm_weight)
+ *   y'[j] = y[j] cos(a_j) - y[j+64] sin(a_j),  y'[j+64] = y[j] sin(a_j) + y[j+64] cos(a_j),
+ *   a_j = fp32(p) * f_j (an fp32 product),     f_j = fp32(1 / fp32(rope_theta^(2j/128))), j < 64;
+ * q_out[i] = y' of every query head, pool.k[out_loc[i]] = y' of every KV
+ * head, pool.v[out_loc[i]] = v[i] bit-for-bit. Arithmetic in fp32; q_out and
+ * the K rows are rounded to nearest even into pool.dtype.
+ *   out_loc   device, [n] of int32 (PKV_I32) or int64 (PKV_I64) slots; an
+ *             out-of-range slot skips that token's K/V store and is flagged
+ *             (PKV_FAULT_STORE_SLOT); its q_out row is still written.
+ *   q, q_out  device, [n, num_q_heads, 128] in pool.dtype, token rows
+ *             q_stride / q_out_stride elements apart (0 = dense). q_out may
+ *             be q (in place); otherwise they must not overlap.
+ *   k, v      device, [n, kv_heads, 128] in pool.dtype, rows k_stride / v_stride apart.
+ *   positions device, int32 [n], absolute token positions (cached_len + t for
+ *             the t-th new token of a request).
+ *   q_norm_weight, k_norm_weight  device, [128] in pool.dtype, 16-byte aligned.
+ *   eps >= 0, rope_theta > 1 (taken as the fp32 value passed).
+ * num_q_heads <= 32 and kv_heads <= 16 (PKV_ERR_SHAPE above).
+ */
+int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,
+                              const void* q, int64_t q_stride, void* q_out, int64_t q_out_stride,
+                              int32_t num_q_heads, const void* k, int64_t k_stride, const void* v,
+                              int64_t v_stride, const int32_t* positions, const void* q_norm_weight,
+                              const void* k_norm_weight, float eps, float rope_theta, void* stream);
 
 /*
  * Decode attention ([TINY] attention with one query row; [DISS] 4.6.5 decode

@@ -89,6 +89,44 @@ def store_kv(k_pool, v_pool, out_loc, k, v, *, page_size: int = 1, stream=None) 
                              _stream(stream)))
 
 
+def qk_norm_rope_store_kv(k_pool, v_pool, out_loc, q, k, v, positions, q_norm_weight, k_norm_weight, *,
+                          eps: float = 1e-6, rope_theta: float = 1_000_000.0, page_size: int = 1, q_out=None,
+                          stream=None):
+    """Per-head RMSNorm of q and k, rotary embedding at `positions`, then the
+    K/V store (pkv_qk_norm_rope_store_kv). Returns q_out ([n, num_q_heads,
+    128], the normalised and rotated q; pass q_out=q to work in place)."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool, page_size)
+    width = pool.kv_heads * HEAD_DIM
+    n = out_loc.shape[0]
+    for t, name in ((out_loc, "out_loc"), (positions, "positions"), (q, "q"), (k, "k"), (v, "v"),
+                    (q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        _cuda(t, name)
+    if out_loc.dtype not in (torch.int32, torch.int64) or out_loc.dim() != 1 or out_loc.stride(0) != 1:
+        raise ValueError("out_loc must be a dense 1-D int32 or int64 tensor")
+    if positions.dtype != torch.int32 or positions.dim() != 1 or positions.shape[0] != n or positions.stride(0) != 1:
+        raise ValueError("positions must be a dense int32 tensor of len(out_loc) entries")
+    if q.dtype != k_pool.dtype or k.dtype != k_pool.dtype or v.dtype != k_pool.dtype:
+        raise ValueError("q, k, v must have the pool dtype")
+    if q.shape[0] != n or k.shape[0] != n or v.shape[0] != n:
+        raise ValueError("q, k, v must have len(out_loc) rows")
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if w.dtype != k_pool.dtype or w.numel() != HEAD_DIM or not w.is_contiguous():
+            raise ValueError(f"{name} must be a dense [{HEAD_DIM}] tensor of the pool dtype")
+    hq = q.shape[1] if q.dim() == 3 else q.shape[-1] // HEAD_DIM
+    qs = _rows(q, "q", hq * HEAD_DIM)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    qos = _rows(q_out, "q_out", hq * HEAD_DIM)
+    ks, vs = _rows(k, "k", width), _rows(v, "v", width)
+    loc_t = PKV_I32 if out_loc.dtype == torch.int32 else PKV_I64
+    check(lib().pkv_qk_norm_rope_store_kv(byref(pool), _ptr(out_loc), loc_t, n, q.data_ptr(), qs,
+                                          q_out.data_ptr(), qos, hq, k.data_ptr(), ks, v.data_ptr(), vs,
+                                          _ptr(positions), q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                                          float(eps), float(rope_theta), _stream(stream)))
+    return q_out
+
+
 def decode_workspace_size(bs: int, num_q_heads: int, max_total_kv: int) -> int:
     return int(lib().pkv_decode_workspace_size(bs, num_q_heads, max_total_kv))
 

@@ -16,6 +16,7 @@
 #include "pkv.h"
 #include "common.hpp"
 #include "store_kv.hpp"
+#include "qk_rope.hpp"
 #include "decode.hpp"
 #include "extend.hpp"
 #include "sample.hpp"
@@ -241,6 +242,95 @@ int pkv_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, in
                        static_cast<const pkv::u32x4*>(k), k_pk, static_cast<const pkv::u32x4*>(v), v_pk, packets,
                        ds->faults);
   return check_launch("store_kv");
+}
+
+int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,
+                              const void* q, int64_t q_stride, void* q_out, int64_t q_out_stride,
+                              int32_t num_q_heads, const void* k, int64_t k_stride, const void* v,
+                              int64_t v_stride, const int32_t* positions, const void* q_norm_weight,
+                              const void* k_norm_weight, float eps, float rope_theta, void* stream) {
+  int isz = 0;
+  int rc = check_pool(pool, &isz);
+  if (rc) return rc;
+  if (n < 0) return fail(PKV_ERR_SHAPE, "n = %lld < 0", (long long)n);
+  if (loc_type != PKV_I32 && loc_type != PKV_I64)
+    return fail(PKV_ERR_DTYPE, "loc_type %d is not PKV_I32 or PKV_I64", loc_type);
+  if (num_q_heads < 1 || num_q_heads % pool->kv_heads)
+    return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of kv_heads %d", num_q_heads,
+                pool->kv_heads);
+  if (num_q_heads > 32 || pool->kv_heads > 16)
+    return fail(PKV_ERR_SHAPE, "qk norm/rope supports up to 32 query and 16 KV heads (%d, %d)", num_q_heads,
+                pool->kv_heads);
+  if (!(eps >= 0.f) || !(rope_theta > 1.f))
+    return fail(PKV_ERR_SHAPE, "need eps >= 0 and rope_theta > 1 (eps %g, rope_theta %g)", eps, rope_theta);
+  if (n == 0) return ok();
+  if (!out_loc || !positions) return fail(PKV_ERR_NULL, "out_loc / positions is NULL");
+  if (!q_norm_weight || !k_norm_weight) return fail(PKV_ERR_NULL, "a norm weight is NULL");
+  if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
+    return fail(PKV_ERR_ALIGN, "norm weights must be 16-byte aligned");
+  const int64_t qrow = (int64_t)num_q_heads * pkv::kHeadDim, kvrow = (int64_t)pool->kv_heads * pkv::kHeadDim;
+  if (q_stride == 0) q_stride = qrow;
+  if (q_out_stride == 0) q_out_stride = qrow;
+  if ((rc = check_rows(q, q_stride, qrow, isz, "q"))) return rc;
+  if ((rc = check_rows(q_out, q_out_stride, qrow, isz, "q_out"))) return rc;
+  if ((rc = check_rows(k, k_stride, kvrow, isz, "k"))) return rc;
+  if ((rc = check_rows(v, v_stride, kvrow, isz, "v"))) return rc;
+  constexpr int TPB = pkv::kQkRopeThreads / pkv::kWave;  // tokens per workgroup
+  const int64_t blocks = (n + TPB - 1) / TPB;
+  if (blocks > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "n = %lld too large", (long long)n);
+  DeviceState* ds;
+  if ((rc = device_state(&ds))) return rc;
+  pkv::QkRopeArgs a;
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.pool_row = pool->row_stride;
+  a.num_slots = pool->num_slots;
+  a.out_loc = out_loc;
+  a.n = n;
+  a.q = q;
+  a.q_stride = q_stride;
+  a.q_out = q_out;
+  a.q_out_stride = q_out_stride;
+  a.k = k;
+  a.k_stride = k_stride;
+  a.v = v;
+  a.v_stride = v_stride;
+  a.positions = positions;
+  a.q_w = q_norm_weight;
+  a.k_w = k_norm_weight;
+  a.hq = num_q_heads;
+  a.hkv = pool->kv_heads;
+  a.eps = eps;
+  // 1 / theta^(2j/128): the power in fp64 rounded to fp32, then an fp32 division
+  for (int j = 0; j < pkv::kHeadDim / 2; ++j) {
+    const float p = (float)std::pow((double)rope_theta, (double)(2 * j) / (double)pkv::kHeadDim);
+    a.inv_freq[j] = 1.0f / p;
+  }
+  a.faults = ds->faults;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mq = (num_q_heads + 3) / 4, mk = (pool->kv_heads + 3) / 4;
+  const bool i64 = loc_type == PKV_I64;
+#define PKV_QKR_LAUNCH(T, MQ, MK)                                                                               \
+  hipLaunchKernelGGL(i64 ? (pkv::qk_rope_store_kernel<T, int64_t, MQ, MK>) : (pkv::qk_rope_store_kernel<T, int32_t, MQ, MK>), \
+                     dim3((uint32_t)blocks), dim3(pkv::kQkRopeThreads), 0, s, a)
+#define PKV_QKR_MK(T, MQ)                  \
+  if (mk <= 1) PKV_QKR_LAUNCH(T, MQ, 1);   \
+  else if (mk <= 2) PKV_QKR_LAUNCH(T, MQ, 2); \
+  else PKV_QKR_LAUNCH(T, MQ, 4);
+#define PKV_QKR_MQ(T)                     \
+  if (mq <= 1) { PKV_QKR_MK(T, 1) }       \
+  else if (mq <= 2) { PKV_QKR_MK(T, 2) }  \
+  else if (mq <= 4) { PKV_QKR_MK(T, 4) }  \
+  else { PKV_QKR_MK(T, 8) }
+  if (pool->dtype == PKV_BF16) {
+    PKV_QKR_MQ(pkv::bf16_t)
+  } else {
+    PKV_QKR_MQ(float)
+  }
+#undef PKV_QKR_MQ
+#undef PKV_QKR_MK
+#undef PKV_QKR_LAUNCH
+  return check_launch("qk_norm_rope_store_kv");
 }
 
 size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv) {

@@ -125,6 +125,29 @@ def test_store_kv_zero_rows_is_noop(L):
     assert _store(L, _pool(), n=0, loc=None) == 0
 
 
+def _qkr(L, pool, n=4, loc=0x30000, loc_t=0, q=0x60000, qs=0, qo=0x70000, qos=0, hq=16, k=0x40000, ks=1024,
+         v=0x50000, vs=1024, pos=0x80000, wq=0xA0000, wk=0xB0000, eps=1e-6, theta=1e6):
+    return L.pkv_qk_norm_rope_store_kv(ctypes.byref(pool), loc, loc_t, n, q, qs, qo, qos, hq, k, ks, v, vs, pos,
+                                       wq, wk, eps, theta, None)
+
+
+@pytest.mark.parametrize("pool,kw,status", [
+    (dict(head_dim=64), {}, -3), (dict(dtype=7), {}, -2), (dict(k=None), {}, -1),
+    (dict(), dict(loc_t=5), -2), (dict(), dict(loc=None), -1), (dict(), dict(pos=None), -1),
+    (dict(), dict(wq=None), -1), (dict(), dict(wk=0xB0004), -5), (dict(), dict(hq=12), -3),
+    (dict(), dict(hq=64), -3), (dict(), dict(eps=-1.0), -3), (dict(), dict(theta=0.5), -3),
+    (dict(), dict(qs=1000), -3), (dict(), dict(qo=0x70008), -5), (dict(), dict(ks=512), -3),
+    (dict(), dict(n=-1), -3), (dict(), dict(q=None), -1),
+])
+def test_qk_norm_rope_store_argument_errors(L, pool, kw, status):
+    assert _qkr(L, _pool(**pool), **kw) == status
+    assert L.pkv_last_error().decode()
+
+
+def test_qk_norm_rope_store_zero_rows_is_noop(L):
+    assert _qkr(L, _pool(), n=0, loc=None, pos=None) == 0
+
+
 def _decode(L, pool, bs=4, hq=16, q=0x60000, o=0x70000, pt=0x80000, dl=0x90000, max_kv=100,
             ws=0xA0000, ws_bytes=1 << 30, rows=4, pts=64):
     return L.pkv_paged_attention_decode(ctypes.byref(pool), q, 0, o, 0, bs, hq, pt, rows, pts, None, None,

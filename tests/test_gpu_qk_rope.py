@@ -1,0 +1,189 @@
+"""GPU parity of pkv_qk_norm_rope_store_kv (per-head q/k RMSNorm, rotary
+embedding, K/V store) against the oracle.
+
+Tolerance, from the arithmetic: the kernel works in fp32 -- a few fp32
+roundings (relative 2^-24 each) on values of the head's scale, fp32 sin/cos
+of the same fp32 angle the oracle uses (a few ulp) -- so its fp32 result is
+within ~1e-6 of the head's scale of the exact value; bf16 outputs are then
+rounded to nearest even. Each element must lie within one bf16 ulp of the
+fp64 oracle value plus 2^-20 times the largest |value| of its head (the
+second term covers cancellation in the rotation); fp32 outputs within 2^-20
+times that scale. V rows are copies and must be bit-exact, as must every pool
+slot the call does not write."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import f32_to_bf16_bits
+from gpu_util import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+pkv = pytest.importorskip("paged_kv_attention_scatter_amd")
+
+THETA, EPS = 1_000_000.0, 1e-6
+SENTINEL = 0x7FC0
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv.read_faults()
+
+
+def _rng(name):
+    return np.random.default_rng(zlib.crc32(name.encode()))
+
+
+def _case(name, n, hq, hkv, dtype, slots=None, max_pos=32768):
+    rng = _rng(name)
+    num_slots = slots or (n + 17)
+    as_dt = (lambda x: f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    return dict(
+        q=as_dt(rng.standard_normal((n, hq, 128), dtype=np.float32)),
+        k=as_dt(rng.standard_normal((n, hkv, 128), dtype=np.float32) * 2.0),
+        v=as_dt(rng.standard_normal((n, hkv, 128), dtype=np.float32)),
+        wq=as_dt(rng.uniform(0.5, 1.5, 128).astype(np.float32)),
+        wk=as_dt(rng.uniform(0.5, 1.5, 128).astype(np.float32)),
+        pos=rng.integers(0, max_pos, n).astype(np.int32),
+        loc=rng.permutation(num_slots)[:n].astype(np.int32),
+        num_slots=num_slots, hq=hq, hkv=hkv, dtype=dtype)
+
+
+def _pool(c):
+    shape = (c["num_slots"], c["hkv"], 128)
+    if c["dtype"] == "bf16":
+        return np.full(shape, SENTINEL, np.uint16), np.full(shape, SENTINEL, np.uint16)
+    return np.full(shape, np.nan, np.float32), np.full(shape, np.nan, np.float32)
+
+
+def _check(got, ref, dtype, what):
+    """got: kernel output (bf16 bits or fp32) [..., heads, 128]; ref: fp64."""
+    g = oracle.widen(got, dtype)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    tol = scale * 2.0 ** -20
+    if dtype == "bf16":
+        e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126)))
+        tol = tol + 2.0 ** (e - 7)
+    err = np.abs(g - ref)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, f"{what}: {len(bad)} elements off, first {bad[:3].tolist()} err {err[tuple(bad[0])]:.3e}"
+    return float(np.max(err / np.maximum(scale, 1e-30)))
+
+
+def _bits(x):
+    return np.ascontiguousarray(x).view(np.uint8)
+
+
+def _run(c, loc_dtype=torch.int32, in_place=False, q_pad=0, kv_pad=0):
+    dt = c["dtype"]
+    kp_h, vp_h = _pool(c)
+    kp, vp = to_dev(kp_h, dt), to_dev(vp_h, dt)
+    n, hq, hkv = c["q"].shape[0], c["hq"], c["hkv"]
+
+    def padded(x, pad, heads):  # rows with `pad` extra elements
+        if not pad:
+            return to_dev(x, dt)
+        big = np.zeros((n, heads * 128 + pad), dtype=x.dtype)
+        big[:, :heads * 128] = x.reshape(n, -1)
+        return to_dev(big, dt)[:, :heads * 128].view(n, heads, 128)
+
+    q = padded(c["q"], q_pad, hq)
+    k, v = padded(c["k"], kv_pad, hkv), padded(c["v"], kv_pad, hkv)
+    loc = to_dev(c["loc"]).to(loc_dtype)
+    print(f"qk-rope case n={n} hq={hq} hkv={hkv} {dt} loc={loc_dtype} in_place={in_place} "
+          f"pads={q_pad},{kv_pad}", flush=True)
+    qo = pkv.qk_norm_rope_store_kv(kp, vp, loc, q, k, v, to_dev(c["pos"]), to_dev(c["wq"], dt), to_dev(c["wk"], dt),
+                                   eps=EPS, rope_theta=THETA, q_out=q if in_place else None)
+    torch.cuda.synchronize()
+    w = lambda x: oracle.widen(x, dt)
+    rq, rk = oracle.qk_norm_rope(w(c["q"]), w(c["k"]), c["pos"], w(c["wq"]), w(c["wk"]), EPS, THETA)
+    eq = _check(to_host(qo), rq, dt, "q_out")
+    kp_g, vp_g = to_host(kp), to_host(vp)
+    ek = _check(kp_g[c["loc"]], rk, dt, "pool K rows")
+    assert np.array_equal(_bits(vp_g[c["loc"]]), _bits(c["v"])), "pool V rows differ"
+    untouched = np.setdiff1d(np.arange(c["num_slots"]), c["loc"])
+    assert np.array_equal(_bits(kp_g[untouched]), _bits(kp_h[untouched])), "K slots outside out_loc written"
+    assert np.array_equal(_bits(vp_g[untouched]), _bits(vp_h[untouched])), "V slots outside out_loc written"
+    assert pkv.read_faults() == 0
+    print(f"  max err / head scale: q {eq:.2e}, k {ek:.2e}")
+
+
+@pytest.mark.parametrize("n,hq,hkv", [(37, 16, 8), (5, 8, 4), (9, 32, 8), (13, 4, 2), (3, 2, 1), (64, 16, 16)])
+def test_matches_oracle_bf16(n, hq, hkv):
+    _run(_case(f"bf16-{n}-{hq}-{hkv}", n, hq, hkv, "bf16"))
+
+
+def test_matches_oracle_fp32():
+    _run(_case("f32", 21, 16, 8, "f32"))
+
+
+def test_int64_slots_strides_and_in_place():
+    _run(_case("strided", 19, 16, 8, "bf16"), loc_dtype=torch.int64, in_place=True, q_pad=8, kv_pad=24)
+
+
+def test_position_zero_normalises_only():
+    """At position 0 the rotation is the identity: the output is the RMSNorm alone."""
+    c = _case("pos0", 8, 16, 8, "bf16")
+    c["pos"][:] = 0
+    _run(c)
+
+
+def test_bad_slot_skips_kv_and_raises_fault():
+    c = _case("badslot", 6, 16, 8, "bf16")
+    kp_h, vp_h = _pool(c)
+    kp, vp = to_dev(kp_h, "bf16"), to_dev(vp_h, "bf16")
+    loc = c["loc"].copy()
+    loc[2] = c["num_slots"] + 5
+    print("qk-rope case bad slot", flush=True)
+    qo = pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), to_dev(c["q"], "bf16"), to_dev(c["k"], "bf16"),
+                                   to_dev(c["v"], "bf16"), to_dev(c["pos"]), to_dev(c["wq"], "bf16"),
+                                   to_dev(c["wk"], "bf16"), eps=EPS, rope_theta=THETA)
+    torch.cuda.synchronize()
+    assert pkv.read_faults() & 0x1
+    w = lambda x: oracle.widen(x, "bf16")
+    rq, rk = oracle.qk_norm_rope(w(c["q"]), w(c["k"]), c["pos"], w(c["wq"]), w(c["wk"]), EPS, THETA)
+    _check(to_host(qo), rq, "bf16", "q_out (all tokens)")
+    good = np.array([i for i in range(6) if i != 2])
+    _check(to_host(kp)[loc[good]], rk[good], "bf16", "K rows of the valid tokens")
+    written = set(loc[good].tolist())
+    rest = np.array([s for s in range(c["num_slots"]) if s not in written])
+    assert np.array_equal(_bits(to_host(kp)[rest]), _bits(kp_h[rest]))
+
+
+def test_prefill_token_count_sampled():
+    """The 8-request prefill's token count (19,892 new tokens, 16 query and 8
+    KV heads, positions cached_len + t), in the launch configuration the
+    benchmark times; every 61st token is checked against the oracle, all V
+    rows bit-exact."""
+    from workloads import config, draw_lengths
+    C, S = draw_lengths(config(4))
+    pos = np.concatenate([np.arange(c, s) for c, s in zip(C, S)]).astype(np.int32)
+    n = len(pos)
+    rng = _rng("prefill")
+    num_slots = n + 1000
+    loc = rng.permutation(num_slots)[:n].astype(np.int32)
+    gen = torch.Generator(device="cuda").manual_seed(44)
+    q = torch.randn((n, 16, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((n, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((n, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    wq = (torch.rand(128, generator=gen, device="cuda") + 0.5).to(torch.bfloat16)
+    wk = (torch.rand(128, generator=gen, device="cuda") + 0.5).to(torch.bfloat16)
+    kp = torch.zeros((num_slots, 8, 128), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    print(f"qk-rope prefill case n={n}", flush=True)
+    qo = pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), q, k, v, to_dev(pos), wq, wk, eps=EPS, rope_theta=THETA)
+    torch.cuda.synchronize()
+    assert pkv.read_faults() == 0
+    pick = np.arange(0, n, 61)
+    w = lambda x: oracle.widen(x, "bf16")
+    qh, kh, vh = to_host(q)[pick], to_host(k)[pick], to_host(v)
+    rq, rk = oracle.qk_norm_rope(w(qh), w(kh), pos[pick], w(to_host(wq)), w(to_host(wk)), EPS, THETA)
+    _check(to_host(qo)[pick], rq, "bf16", "prefill q_out sampled")
+    _check(to_host(kp)[loc[pick]], rk, "bf16", "prefill K rows sampled")
+    assert np.array_equal(_bits(to_host(vp)[loc]), _bits(vh)), "prefill V rows differ"
