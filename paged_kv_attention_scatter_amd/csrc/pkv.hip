@@ -301,11 +301,18 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
   a.hq = num_q_heads;
   a.hkv = pool->kv_heads;
   a.eps = eps;
-  // 1 / theta^(2j/128): the power in fp64 rounded to fp32, then an fp32 division
-  for (int j = 0; j < pkv::kHeadDim / 2; ++j) {
-    const float p = (float)std::pow((double)rope_theta, (double)(2 * j) / (double)pkv::kHeadDim);
-    a.inv_freq[j] = 1.0f / p;
+  // 1 / theta^(2j/128): the power in fp64 rounded to fp32, then an fp32
+  // division (kept per host thread for the last theta, a pure function of it)
+  thread_local float freq_theta = 0.f;
+  thread_local float freq[pkv::kHeadDim / 2];
+  if (freq_theta != rope_theta) {
+    for (int j = 0; j < pkv::kHeadDim / 2; ++j) {
+      const float p = (float)std::pow((double)rope_theta, (double)(2 * j) / (double)pkv::kHeadDim);
+      freq[j] = 1.0f / p;
+    }
+    freq_theta = rope_theta;
   }
+  std::memcpy(a.inv_freq, freq, sizeof freq);
   a.faults = ds->faults;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mq = (num_q_heads + 3) / 4, mk = (pool->kv_heads + 3) / 4;
