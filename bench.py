@@ -59,7 +59,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode256_traffic.md")
-DECODE_SOURCES = ["paged_kv_attention_scatter_amd/csrc/decode.hpp", "paged_kv_attention_scatter_amd/csrc/pkv.hip",
+DECODE_SOURCES = ["paged_kv_attention_scatter_amd/csrc/decode.hpp", "paged_kv_attention_scatter_amd/csrc/decode_host.inc",
                   "paged_kv_attention_scatter_amd/csrc/common.hpp"]
 
 

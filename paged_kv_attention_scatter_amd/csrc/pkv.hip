@@ -126,63 +126,7 @@ int check_rows(const void* p, int64_t stride, int64_t min_stride, int isz, const
   return PKV_OK;
 }
 
-// ------------------------------------------------------------------ decode plan
-
-constexpr int kDecodeMaxItems = 1024;     // 256 CUs x 4 resident workgroups
-constexpr int kDecodeKeysPerItem = 256;   // smallest item worth a workgroup
-constexpr int kDecodeMaxBatch = 4096;     // prefix sums of lengths live in LDS
-
-int decode_items(int64_t max_total_kv) {
-  int64_t p = (max_total_kv + kDecodeKeysPerItem - 1) / kDecodeKeysPerItem;
-  if (p < 1) p = 1;
-  if (p > kDecodeMaxItems) p = kDecodeMaxItems;
-  return (int)p;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-struct DecodeWs {
-  size_t cu, ml, acc, total;
-};
-
-DecodeWs decode_ws_layout(int32_t bs, int32_t hq, int64_t max_total_kv) {
-  const int64_t slots = (int64_t)decode_items(max_total_kv) + bs;
-  DecodeWs w;
-  w.cu = 0;
-  w.ml = align256((size_t)(bs + 1) * 4);
-  w.acc = w.ml + align256((size_t)slots * hq * 2 * 4);
-  w.total = w.acc + align256((size_t)slots * hq * pkv::kHeadDim * 4);
-  return w;
-}
-
-template <typename T, int HKV, int G>
-int launch_decode(const pkv::DecodeArgs& a, hipStream_t s) {
-  constexpr int NWAVE = 4;
-  constexpr int KB = sizeof(T) == 2 ? 4 : 2;
-  const size_t dyn = (size_t)(a.bs + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((pkv::decode_splitk_kernel<T, HKV, G, NWAVE, KB>), dim3(a.num_items),
-                     dim3(NWAVE * 64), dyn, s, a);
-  int rc = check_launch("decode_splitk");
-  if (rc) return rc;
-  hipLaunchKernelGGL((pkv::decode_combine_kernel<T, HKV * G>), dim3(a.bs), dim3(HKV * G * 16), 0, s, a);
-  return check_launch("decode_combine");
-}
-
-template <typename T>
-int dispatch_decode(int hkv, int g, const pkv::DecodeArgs& a, hipStream_t s) {
-#define PKV_DECODE_CASE(H, GG) \
-  if (hkv == H && g == GG) return launch_decode<T, H, GG>(a, s);
-  if constexpr (sizeof(T) == 2) {
-    PKV_DECODE_CASE(8, 1) PKV_DECODE_CASE(8, 2) PKV_DECODE_CASE(8, 4)
-    PKV_DECODE_CASE(4, 1) PKV_DECODE_CASE(4, 2) PKV_DECODE_CASE(4, 4)
-  } else {
-    PKV_DECODE_CASE(8, 1) PKV_DECODE_CASE(8, 2) PKV_DECODE_CASE(8, 4)
-    PKV_DECODE_CASE(4, 1) PKV_DECODE_CASE(4, 2) PKV_DECODE_CASE(4, 4)
-    PKV_DECODE_CASE(2, 2) PKV_DECODE_CASE(2, 4)
-  }
-#undef PKV_DECODE_CASE
-  return fail(PKV_ERR_SHAPE, "decode: kv_heads %d with %d query heads per KV head is not built", hkv, g);
-}
 
 }  // namespace
 
@@ -340,70 +284,6 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
   return check_launch("qk_norm_rope_store_kv");
 }
 
-size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv) {
-  if (bs < 1 || num_q_heads < 1) return 0;
-  return decode_ws_layout(bs, num_q_heads, max_total_kv).total;
-}
-
-int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_stride, void* o,
-                               int64_t o_stride, int32_t bs, int32_t num_q_heads,
-                               const int32_t* page_table, int32_t pt_rows, int64_t pt_stride,
-                               const int32_t* table_idx, const int32_t* cached_len,
-                               const int32_t* device_len, int64_t max_total_kv, float sm_scale,
-                               void* ws, size_t ws_bytes, void* stream) {
-  (void)cached_len;
-  int isz = 0;
-  int rc = check_pool(pool, &isz);
-  if (rc) return rc;
-  if (bs < 0 || bs > kDecodeMaxBatch) return fail(PKV_ERR_SHAPE, "bs %d outside [0, %d]", bs, kDecodeMaxBatch);
-  if (bs == 0) return ok();
-  if (num_q_heads < 1 || num_q_heads % pool->kv_heads)
-    return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of kv_heads %d", num_q_heads,
-                pool->kv_heads);
-  const int64_t qrow = (int64_t)num_q_heads * pkv::kHeadDim;
-  if (q_stride == 0) q_stride = qrow;
-  if (o_stride == 0) o_stride = qrow;
-  if ((rc = check_rows(q, q_stride, qrow, isz, "q"))) return rc;
-  if ((rc = check_rows(o, o_stride, qrow, isz, "o"))) return rc;
-  if (!page_table || !device_len) return fail(PKV_ERR_NULL, "page_table / device_len is NULL");
-  if (pt_rows < 1 || pt_stride < 1) return fail(PKV_ERR_SHAPE, "page table must have >= 1 row and column");
-  if (max_total_kv < 1 || max_total_kv > 0x7fffffffLL)
-    return fail(PKV_ERR_LENGTHS, "max_total_kv %lld outside [1, 2^31)", (long long)max_total_kv);
-  const DecodeWs lay = decode_ws_layout(bs, num_q_heads, max_total_kv);
-  if (!ws || ws_bytes < lay.total)
-    return fail(PKV_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", lay.total, ws ? ws_bytes : 0);
-  if (!aligned16(ws)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
-  DeviceState* ds;
-  if ((rc = device_state(&ds))) return rc;
-  if (sm_scale == 0.f) sm_scale = 1.0f / std::sqrt((float)pkv::kHeadDim);
-  pkv::DecodeArgs a;
-  a.k_pool = pool->k;
-  a.v_pool = pool->v;
-  a.pool_row = pool->row_stride;
-  a.num_slots = pool->num_slots;
-  a.q = q;
-  a.q_stride = q_stride;
-  a.o = o;
-  a.o_stride = o_stride;
-  a.bs = bs;
-  a.num_items = decode_items(max_total_kv);
-  a.page_table = page_table;
-  a.pt_rows = pt_rows;
-  a.pt_stride = pt_stride;
-  a.table_idx = table_idx;
-  a.device_len = device_len;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  char* w = static_cast<char*>(ws);
-  a.cu_out = reinterpret_cast<int32_t*>(w + lay.cu);
-  a.part_ml = reinterpret_cast<float*>(w + lay.ml);
-  a.part_acc = reinterpret_cast<float*>(w + lay.acc);
-  a.faults = ds->faults;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int g = num_q_heads / pool->kv_heads;
-  if (pool->dtype == PKV_BF16) return dispatch_decode<pkv::bf16_t>(pool->kv_heads, g, a, s);
-  return dispatch_decode<float>(pool->kv_heads, g, a, s);
-}
-
 // ------------------------------------------------------------------ host-only helpers
 
 int64_t pkv_num_pages(int32_t head_dim, int32_t kv_heads, int32_t tp_size, int32_t page_size,
@@ -451,5 +331,6 @@ int pkv_prepare_sampling(int32_t n, const float* T, const int32_t* K, const floa
 }  // extern "C"
 
 // Entry points whose host code lives next to their kernels.
+#include "decode_host.inc"
 #include "extend_host.inc"
 #include "sample_host.inc"
