@@ -25,8 +25,8 @@ Sources (the pages are cited by title and section):
 * "Mini-SGLang 完整剖析" -- sections 4.4.3 (KV pool layout, store_kv scatter),
   4.6.4/4.6.5 (page_size > 1 conversion, cu_seqlens), 4.6.7 (q/k norm and
   RoPE in place, then store_kv runs before the attention kernel), 4.8.4-4.8.6
-  (greedy rule, sparse argument construction), 4.9.4 (store kernel shape
-  contract), 5.2 (worked page counts).
+  (greedy rule, sparse argument construction), 4.9.2-4.9.3 (the embedding
+  gather), 4.9.4 (store kernel shape contract), 5.2 (worked page counts).
 * "Mini-SGLang 源码解析（四）：GPU 计算引擎系统" -- sections 14.3/14.4
   (greedy fast path, top-k renormalisation example).
 
@@ -43,10 +43,12 @@ from .store_kv import store_kv
 from .attention import gather_kv, attention_request, attention_decode, attention_extend
 from .sampler import sample, sample_row, DELTA
 from .qk_norm_rope import rmsnorm, rope, rope_angles, rope_inv_freq, qk_norm_rope
+from .embedding import embedding_gather
 
 __all__ = [
     "widen", "bf16_bits_to_f64", "Req", "bytes_per_page", "num_pages",
     "SamplingParams", "is_greedy", "prepare", "store_kv", "gather_kv",
     "attention_request", "attention_decode", "attention_extend", "sample",
     "sample_row", "DELTA", "rmsnorm", "rope", "rope_angles", "rope_inv_freq", "qk_norm_rope",
+    "embedding_gather",
 ]
