@@ -246,6 +246,7 @@ def main():
     if not args.skip_extend:
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
     result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
+    result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
@@ -348,6 +349,43 @@ def bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the qk norm/rope/store timing")
     return cases
+
+
+def bench_embedding(torch, pkv, gen, dev, args):
+    """Embedding row gather (the first op of forward_batch) from a
+    Qwen3-0.6B-shaped table ([151936, 1024] bf16, drawn on the device) for 256
+    decode tokens and for the 19,892 tokens of the 8-request prefill (seeded
+    random ids). Bytes per token: one 2 KiB row read and one written."""
+    V, H = 151936, 1024
+    W = torch.empty((V, H), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    rng = np.random.default_rng(31)
+    out = {}
+    for name, n in (("decode256", 256), ("prefill8", 19892)):
+        ids = torch.from_numpy(rng.integers(0, V, n).astype(np.int32)).to(dev)
+        o = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+        pkv.embedding_gather(W, ids, out=o)  # checked once
+        fn = pkv.lib().pkv_embedding_gather
+        c_args = (W.data_ptr(), 1, V, H, H, ids.data_ptr(), n, 0, V, o.data_ptr(), H,
+                  torch.cuda.current_stream().cuda_stream)
+        for _ in range(3):
+            if fn(*c_args) != 0:
+                raise RuntimeError(pkv.lib().pkv_last_error().decode())
+        torch.cuda.synchronize()
+        reps = max(20, args.steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(*c_args)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = n * H * 2 * 2 / (us * 1e-6) / 1e9
+        log(f"embedding gather {name}: {n} tokens, {us:.1f} us, {gbs:.0f} GB/s")
+        out[f"embedding_{name}_us"] = round(us, 2)
+        out[f"embedding_{name}_gbs"] = round(gbs, 1)
+        out[f"embedding_{name}_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+    del W
+    return out
 
 
 def bench_mixed(torch, pkv, dev, args):

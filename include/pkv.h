@@ -7,6 +7,8 @@
  *   1. pkv_store_kv                 scatter this step's K/V rows into the paged pool
  *      (pkv_qk_norm_rope_store_kv   the same store fused with Qwen3's per-head q/k
  *                                   RMSNorm and the rotary embedding);
+ *      (pkv_embedding_gather        the embedding rows of the step's token ids,
+ *                                   the first op of forward_batch)
  *   2. pkv_paged_attention_decode   GQA attention of one new token per request
  *      pkv_paged_attention_extend   causal GQA attention of a chunk of new tokens
  *                                   over a cached prefix (prefill / extend);
@@ -119,6 +121,26 @@ typedef struct {
 int pkv_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,
                  const void* k, int64_t k_stride, const void* v, int64_t v_stride,
                  void* stream);
+
+/*
+ * Embedding row gather of the vocab-parallel embedding ([DISS] 4.9.2-4.9.3:
+ * VocabParallelEmbedding's indexing(weights, ids, vocab_range), the first op
+ * of forward_batch). For i in [0, n):
+ *   out[i] = weight[ids[i] - vocab_start]  if vocab_start <= ids[i] < vocab_end,
+ *   out[i] = 0 (every element)             otherwise,
+ * rows copied bit for bit, so the outputs of shards that partition the
+ * vocabulary add up to the whole table's gather (reading of vocab_range: the
+ * pages name it without spelling it out).
+ *   weight    device, [weight_rows, hidden] of dtype (PKV_BF16 or PKV_F32), rows
+ *             weight_stride elements apart, 16-byte aligned (unused if weight_rows == 0).
+ *   ids       device, int32 [n]; any value is allowed (out of range -> zero row).
+ *   out       device, [n, hidden] of dtype, rows out_stride elements apart.
+ *   hidden * itemsize a multiple of 16 bytes; 0 <= vocab_start <= vocab_end and
+ *   vocab_end - vocab_start <= weight_rows (PKV_ERR_SHAPE otherwise).
+ */
+int pkv_embedding_gather(const void* weight, int32_t dtype, int64_t weight_rows, int64_t weight_stride,
+                         int32_t hidden, const int32_t* ids, int64_t n, int64_t vocab_start, int64_t vocab_end,
+                         void* out, int64_t out_stride, void* stream);
 
 /*
  * q/k norm + rotary embedding + store_kv, fused ([TINY] its rmsnorm and rope

@@ -39,6 +39,8 @@ _P_f32 = POINTER(c_float)
 SIGNATURES = {
     "pkv_store_kv": (c_int32, [POINTER(PkvPool), c_void_p, c_int32, c_int64, c_void_p, c_int64,
                                c_void_p, c_int64, c_void_p]),
+    "pkv_embedding_gather": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_void_p, c_int64, c_int64,
+                                      c_int64, c_void_p, c_int64, c_void_p]),
     "pkv_qk_norm_rope_store_kv": (c_int32, [POINTER(PkvPool), c_void_p, c_int32, c_int64, c_void_p, c_int64,
                                            c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                            c_void_p, c_void_p, c_void_p, c_float, c_float, c_void_p]),

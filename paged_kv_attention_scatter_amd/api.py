@@ -89,6 +89,31 @@ def store_kv(k_pool, v_pool, out_loc, k, v, *, page_size: int = 1, stream=None) 
                              _stream(stream)))
 
 
+def embedding_gather(weight, ids, *, vocab_start: int = 0, vocab_end=None, out=None, stream=None):
+    """Rows of the vocab-parallel embedding (pkv_embedding_gather): out[i] =
+    weight[ids[i] - vocab_start] for ids in [vocab_start, vocab_end), zero rows
+    for the others. weight: [rows, hidden]; ids: int32 [n]. Returns out [n, hidden]."""
+    torch = _torch()
+    _cuda(weight, "weight")
+    _cuda(ids, "ids")
+    if weight.dim() != 2 or weight.stride(1) != 1:
+        raise ValueError("weight must be [rows, hidden] with dense rows")
+    if ids.dtype != torch.int32 or ids.dim() != 1 or ids.stride(0) != 1:
+        raise ValueError("ids must be a dense 1-D int32 tensor")
+    rows, hidden = weight.shape
+    if vocab_end is None:
+        vocab_end = vocab_start + rows
+    n = ids.shape[0]
+    if out is None:
+        out = torch.empty((n, hidden), dtype=weight.dtype, device=weight.device)
+    if out.dtype != weight.dtype or out.dim() != 2 or out.shape != (n, hidden) or out.stride(1) != 1:
+        raise ValueError("out must be [len(ids), hidden] of the weight dtype with dense rows")
+    check(lib().pkv_embedding_gather(weight.data_ptr(), _dtype_code(weight), rows, weight.stride(0), hidden,
+                                     _ptr(ids), n, vocab_start, vocab_end, out.data_ptr(), out.stride(0),
+                                     _stream(stream)))
+    return out
+
+
 def qk_norm_rope_store_kv(k_pool, v_pool, out_loc, q, k, v, positions, q_norm_weight, k_norm_weight, *,
                           eps: float = 1e-6, rope_theta: float = 1_000_000.0, page_size: int = 1, q_out=None,
                           stream=None):

@@ -17,6 +17,7 @@
 #include "common.hpp"
 #include "store_kv.hpp"
 #include "qk_rope.hpp"
+#include "embed.hpp"
 #include "decode.hpp"
 #include "extend.hpp"
 #include "sample.hpp"
@@ -186,6 +187,49 @@ int pkv_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, in
                        static_cast<const pkv::u32x4*>(k), k_pk, static_cast<const pkv::u32x4*>(v), v_pk, packets,
                        ds->faults);
   return check_launch("store_kv");
+}
+
+int pkv_embedding_gather(const void* weight, int32_t dtype, int64_t weight_rows, int64_t weight_stride,
+                         int32_t hidden, const int32_t* ids, int64_t n, int64_t vocab_start, int64_t vocab_end,
+                         void* out, int64_t out_stride, void* stream) {
+  const int isz = itemsize(dtype);
+  if (!isz) return fail(PKV_ERR_DTYPE, "dtype %d is not PKV_F32 or PKV_BF16", dtype);
+  if (n < 0 || hidden < 1 || weight_rows < 0)
+    return fail(PKV_ERR_SHAPE, "need n >= 0, hidden >= 1, weight_rows >= 0 (%lld, %d, %lld)", (long long)n, hidden,
+                (long long)weight_rows);
+  if (((int64_t)hidden * isz) % 16)
+    return fail(PKV_ERR_SHAPE, "hidden * itemsize = %lld is not a multiple of 16 bytes", (long long)hidden * isz);
+  if (vocab_start < 0 || vocab_end < vocab_start || vocab_end - vocab_start > weight_rows)
+    return fail(PKV_ERR_SHAPE, "vocab range [%lld, %lld) does not fit %lld weight rows", (long long)vocab_start,
+                (long long)vocab_end, (long long)weight_rows);
+  if (n == 0) return ok();
+  if (!ids) return fail(PKV_ERR_NULL, "ids is NULL");
+  int rc;
+  if (weight_rows > 0 && (rc = check_rows(weight, weight_stride, hidden, isz, "weight"))) return rc;
+  if ((rc = check_rows(out, out_stride, hidden, isz, "out"))) return rc;
+  DeviceState* ds;
+  if ((rc = device_state(&ds))) return rc;
+  const int32_t packets = (int32_t)((int64_t)hidden * isz / 16);
+  const int pk = packets % 4 == 0 ? 4 : (packets % 2 == 0 ? 2 : 1);
+  const int64_t threads = n * (packets / pk);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(PKV_ERR_SHAPE, "n = %lld too large", (long long)n);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pkv::u32x4* w = static_cast<const pkv::u32x4*>(weight);
+  pkv::u32x4* o = static_cast<pkv::u32x4*>(out);
+  const int64_t w_pk = weight_stride * isz / 16, o_pk = out_stride * isz / 16;
+  if (weight_rows == 0) vocab_end = vocab_start;  // every id is outside the shard
+  if (pk == 4)
+    hipLaunchKernelGGL(pkv::embed_gather_kernel<4>, dim3((uint32_t)blocks), dim3(256), 0, s, w, w_pk, ids, n,
+                       vocab_start, vocab_end, o, o_pk, packets);
+  else if (pk == 2)
+    hipLaunchKernelGGL(pkv::embed_gather_kernel<2>, dim3((uint32_t)blocks), dim3(256), 0, s, w, w_pk, ids, n,
+                       vocab_start, vocab_end, o, o_pk, packets);
+  else
+    hipLaunchKernelGGL(pkv::embed_gather_kernel<1>, dim3((uint32_t)blocks), dim3(256), 0, s, w, w_pk, ids, n,
+                       vocab_start, vocab_end, o, o_pk, packets);
+  (void)ds;
+  return check_launch("embedding_gather");
 }
 
 int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t loc_type, int64_t n,

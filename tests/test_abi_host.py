@@ -148,6 +148,24 @@ def test_qk_norm_rope_store_zero_rows_is_noop(L):
     assert _qkr(L, _pool(), n=0, loc=None, pos=None) == 0
 
 
+def _emb(L, w=0x10000, dt=1, rows=100, ws=1024, hidden=1024, ids=0x20000, n=4, a=0, b=100, out=0x30000, os_=1024):
+    return L.pkv_embedding_gather(w, dt, rows, ws, hidden, ids, n, a, b, out, os_, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=9), -2), (dict(hidden=4), -3), (dict(hidden=1028), -3), (dict(n=-1), -3), (dict(a=-1), -3),
+    (dict(a=10, b=5), -3), (dict(b=101), -3), (dict(ids=None), -1), (dict(w=None), -1), (dict(out=None), -1),
+    (dict(ws=1000), -3), (dict(w=0x10008), -5), (dict(os_=1028), -5), (dict(rows=-1), -3),
+])
+def test_embedding_gather_argument_errors(L, kw, status):
+    assert _emb(L, **kw) == status
+    assert L.pkv_last_error().decode()
+
+
+def test_embedding_gather_zero_rows_is_noop(L):
+    assert _emb(L, n=0, ids=None) == 0
+
+
 def _decode(L, pool, bs=4, hq=16, q=0x60000, o=0x70000, pt=0x80000, dl=0x90000, max_kv=100,
             ws=0xA0000, ws_bytes=1 << 30, rows=4, pts=64):
     return L.pkv_paged_attention_decode(ctypes.byref(pool), q, 0, o, 0, bs, hq, pt, rows, pts, None, None,
