@@ -247,6 +247,7 @@ def main():
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
     result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
     result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
+    result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
@@ -385,6 +386,72 @@ def bench_embedding(torch, pkv, gen, dev, args):
         out[f"embedding_{name}_gbs"] = round(gbs, 1)
         out[f"embedding_{name}_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
     del W
+    return out
+
+
+def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
+    """A decode step (store_kv, decode attention, sampler) of the first bs
+    requests of the 256-request batch, bs = 1, 8 and 64, over layer 0 of the
+    pool: issued eagerly through the Python binding, and replayed from a HIP
+    graph captured once (torch.cuda.CUDAGraph over the same calls). Small
+    steps are bound by the host's launch rate; the replay is not."""
+    from workloads import HEAD_DIM, HKV, HQ, config, draw_sampling_params
+    V = config(3).vocab
+    rows = draw_sampling_params(config(3))
+    T_all, K_all, P_all = pkv.prepare_sampling(*zip(*rows), vocab=V)
+    kp, vp = pool[0, 0], pool[1, 0]
+    out = {}
+    for bs in (1, 8, 64):
+        s_q = q[:bs].clone()
+        s_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        s_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        s_loc = torch.from_numpy(table[np.arange(bs), S[:bs] - 1].astype(np.int32)).to(dev)
+        s_table = torch.from_numpy(np.ascontiguousarray(table[:bs])).to(dev)
+        s_C, s_S = torch.from_numpy(C[:bs].copy()).to(dev), torch.from_numpy(S[:bs].copy()).to(dev)
+        s_logits = (torch.randn((bs, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
+        T, P = torch.from_numpy(T_all[:bs].copy()).to(dev), torch.from_numpy(P_all[:bs].copy()).to(dev)
+        u = torch.rand(bs, generator=gen, device=dev)
+        max_kv = int(S[:bs].sum())
+        o = torch.empty_like(s_q)
+        tok = torch.empty(bs, dtype=torch.int32, device=dev)
+        ws_d = torch.empty(pkv.decode_workspace_size(bs, HQ, max_kv), dtype=torch.uint8, device=dev)
+        ws_s = pkv.sample_workspace(bs, V, dev)
+
+        def step():
+            pkv.store_kv(kp, vp, s_loc, s_k, s_v)
+            pkv.paged_attention_decode(s_q, kp, vp, s_table, s_C, s_S, max_total_kv=max_kv, out=o, workspace=ws_d)
+            pkv.sample(s_logits, T, None, P, u, out=tok, workspace=ws_s)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        reps = max(50, args.steps)
+        times = {}
+        for name, fn in (("eager", step), ("graph", graph.replay)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name] = e0.elapsed_time(e1) / reps * 1e3
+        log(f"decode step bs={bs}: eager {times['eager']:.1f} us, graph replay {times['graph']:.1f} us")
+        out[f"step_bs{bs}_eager_us"] = round(times["eager"], 2)
+        out[f"step_bs{bs}_graph_us"] = round(times["graph"], 2)
+        del graph
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the graph timing")
     return out
 
 
