@@ -10,6 +10,11 @@ sections 14.3-14.4:
   keeps a token iff the renormalised mass ranked *before* it is < p (so the
   most probable token always survives); top-k is applied before top-p; one
   token is drawn from what is left.
+* min_p ("Engine 与采样器", section 练习 and its answer): a token survives iff
+  its probability is at least min_p times the largest one, taken on the
+  full temperature-scaled distribution; the mask is computed before top-k
+  and top-p and intersected with their masks (top-p still renormalises over
+  the top-k set alone). min_p <= 0 means no min_p; values above 1 act as 1.
 
 Readings where the pages leave the step open (each listed in the design
 notes):
@@ -26,7 +31,9 @@ notes):
   mass), or the last kept index if rounding finds none (the pages fix only the
   distribution, via torch.multinomial or FlashInfer's rejection sampler);
 * a row is *flagged* when a floating-point boundary lies within DELTA
-  (relative to the kept mass) of the decision: the top-p cut or the draw. The
+  (relative to the kept mass) of the decision: the top-p cut or the draw, or
+  (relative to min_p) a token's probability ratio to the largest one at the
+  min_p threshold. The
   GPU computes those sums in another order and precision, so flagged rows are
   excluded from the bit-exact comparison and counted. Argmax and top-k are
   pure order comparisons and are never flagged. Two boundaries are exact on
@@ -49,9 +56,9 @@ DELTA = 1e-5
 
 
 def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
-               delta: float = DELTA, info: dict | None = None):
-    """logits: f64 [V]. T, top_k, top_p are this row's device-side values
-    (float32/int32 as the kernel sees them). Returns (token, flagged)."""
+               delta: float = DELTA, info: dict | None = None, min_p: float = 0.0):
+    """logits: f64 [V]. T, top_k, top_p, min_p are this row's device-side
+    values (float32/int32 as the kernel sees them). Returns (token, flagged)."""
     l = np.asarray(logits, dtype=np.float64)
     V = l.shape[0]
     if np.float32(T) <= np.float32(MIN_T):
@@ -76,6 +83,22 @@ def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
         ranked = ranked[:n_keep]
         if info is not None:
             info["top_p_margin"] = float(margin)
+    mp = min(np.float64(np.float32(min_p)), 1.0)
+    if mp > 0.0:
+        # e is the probability over the largest one (e_max = 1); ranked is in
+        # descending order, so the mask keeps a prefix of it
+        keep = e[ranked] >= mp
+        n_mp = int(np.count_nonzero(keep))
+        margin = np.inf
+        if n_mp > 0:
+            margin = (e[ranked[n_mp - 1]] - mp) / mp
+        if n_mp < len(ranked):
+            margin = min(margin, (mp - e[ranked[n_mp]]) / mp)
+        if margin < delta:
+            flagged = True
+        ranked = ranked[:n_mp]
+        if info is not None:
+            info["min_p_margin"] = float(margin)
     w = np.zeros(V, dtype=np.float64)
     w[ranked] = e[ranked]
     c = np.cumsum(w)
@@ -96,9 +119,9 @@ def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
 
 
 def sample(logits: np.ndarray, temperature, top_k, top_p, uniforms, delta: float = DELTA,
-           rows=None):
-    """logits: f64 [bs, V]; temperature / top_k / top_p: per-row device
-    arrays or None (None temperature = all-greedy batch). Returns
+           rows=None, min_p=None):
+    """logits: f64 [bs, V]; temperature / top_k / top_p / min_p: per-row
+    device arrays or None (None temperature = all-greedy batch). Returns
     (tokens int32 [bs], flagged bool [bs])."""
     bs = logits.shape[0]
     tokens = np.full(bs, -1, dtype=np.int32)
@@ -109,6 +132,7 @@ def sample(logits: np.ndarray, temperature, top_k, top_p, uniforms, delta: float
             continue
         k = -1 if top_k is None else int(top_k[r])
         p = 1.0 if top_p is None else float(top_p[r])
+        mp = 0.0 if min_p is None else float(min_p[r])
         tokens[r], flagged[r] = sample_row(logits[r], float(temperature[r]), k, p,
-                                           float(uniforms[r]), delta)
+                                           float(uniforms[r]), delta, min_p=mp)
     return tokens, flagged

@@ -211,3 +211,73 @@ def test_zero_uniform_lands_on_a_kept_token():
     logits = np.array([0.0, 5.0, 4.0, -1.0])
     assert oracle.sample_row(logits, 1.0, 1, 1.0, 0.0)[0] == 1
     assert oracle.sample_row(logits, 1.0, 2, 1.0, 0.0)[0] == 1
+
+
+# ---------------------------------------------------------------- min_p ("Engine 与采样器", 练习 2 and its answer)
+
+def _draws_mp(logits, T, k, p, mp, us):
+    return np.array([oracle.sample_row(np.asarray(logits, float), T, k, p, float(np.float32(u)), min_p=mp)[0]
+                     for u in us])
+
+
+def test_min_p_closed_form_matches_top_k2():
+    """logits [5,4,3,0,0,0] at T = 1: the second token has e^-1 = 0.368 of the
+    largest probability and the third e^-2 = 0.135, so min_p = 0.3 keeps exactly
+    the first two, like top-k = 2: token 0 iff u < 1 / (1 + e^-1)."""
+    us = np.linspace(0.0, 0.999, 2001)
+    got = _draws_mp([5, 4, 3, 0, 0, 0], 1.0, -1, 1.0, 0.3, us)
+    assert set(got.tolist()) == {0, 1}
+    assert np.array_equal(got == 0, us < 1.0 / (1.0 + np.exp(-1.0)))
+    assert np.array_equal(got, _draw_all([5, 4, 3, 0, 0, 0], 1.0, 2, 1.0, us))
+
+
+def test_min_p_zero_is_no_filter_and_one_keeps_the_maximum():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal(50) * 2
+    us = rng.random(200)
+    assert np.array_equal(_draws_mp(logits, 0.8, -1, 0.9, 0.0, us), _draw_all(logits, 0.8, -1, 0.9, us))
+    assert set(_draws_mp(logits, 0.8, -1, 1.0, 1.0, us).tolist()) == {int(np.argmax(logits))}
+    tied = np.array([1.0, 3.0, 3.0, 2.0])          # min_p = 1 keeps both tied maxima
+    assert set(_draws_mp(tied, 1.0, -1, 1.0, 1.0, np.linspace(0, 0.99, 100)).tolist()) == {1, 2}
+
+
+def test_min_p_is_relative_to_the_tempered_maximum():
+    """The threshold scales with the temperature: ratio e^(-(l0 - l1) / T)."""
+    logits = np.array([2.0, 1.0, -10.0])
+    us = np.linspace(0, 0.999, 500)
+    assert set(_draws_mp(logits, 1.0, -1, 1.0, 0.5, us).tolist()) == {0}          # e^-1 < 0.5
+    assert set(_draws_mp(logits, 2.0, -1, 1.0, 0.5, us).tolist()) == {0, 1}       # e^-0.5 >= 0.5
+
+
+def test_min_p_mask_intersects_top_p_on_the_full_distribution():
+    """Probabilities [0.4, 0.35, 0.25], min_p = 0.7 (drops the third: 0.625 <
+    0.7), top_p = 0.5. The page's answer intersects masks computed on the full
+    distribution: top-p keeps the first two (0.4 before the second is < 0.5),
+    so token 1 is drawn with probability 0.35 / 0.75. Renormalising top-p over
+    the min_p survivors first would keep token 0 alone."""
+    logits = np.log([0.4, 0.35, 0.25])
+    us = np.linspace(0.0, 0.999, 4001)
+    got = _draws_mp(logits, 1.0, -1, 0.5, 0.7, us)
+    assert set(got.tolist()) == {0, 1}
+    assert np.array_equal(got == 0, us < 0.4 / 0.75)
+
+
+def test_min_p_kept_set_is_the_intersection():
+    rng = np.random.default_rng(9)
+    for trial in range(30):
+        logits = rng.standard_normal(300) * 3
+        T, k, p, mp = 0.7, int(rng.choice([-1, 5, 40])), float(rng.choice([1.0, 0.9, 0.6])), float(rng.choice([0.01, 0.1, 0.4]))
+        i_all, i_kp, i_mp = {}, {}, {}
+        oracle.sample_row(logits, T, k, p, 0.5, info=i_all, min_p=mp)
+        oracle.sample_row(logits, T, k, p, 0.5, info=i_kp)
+        oracle.sample_row(logits, T, -1, 1.0, 0.5, info=i_mp, min_p=mp)
+        assert i_all["kept"] == min(i_kp["kept"], i_mp["kept"]), trial
+
+
+def test_min_p_boundary_is_flagged():
+    """A token whose probability ratio sits on min_p is rounding-sensitive: flagged."""
+    logits = np.array([0.0, np.log(0.25)])
+    _, flagged = oracle.sample_row(logits, 1.0, -1, 1.0, 0.3, min_p=0.25)
+    assert flagged
+    _, flagged = oracle.sample_row(logits, 1.0, -1, 1.0, 0.3, min_p=0.2)
+    assert not flagged
