@@ -36,10 +36,12 @@ notes):
   min_p threshold. The
   GPU computes those sums in another order and precision, so flagged rows are
   excluded from the bit-exact comparison and counted. Argmax and top-k are
-  pure order comparisons and are never flagged. Two boundaries are exact on
+  pure order comparisons and are never flagged. Three boundaries are exact on
   any hardware and never flag: the start of the first kept token (no kept
-  mass precedes it) and the end of the last kept token (running past it
-  returns that same token).
+  mass precedes it), the end of the last kept token (running past it
+  returns that same token), and min_p at a token whose logit equals the
+  maximum (its ratio to the largest probability is exactly 1, and min_p is
+  at most 1).
 
 DELTA = 1e-5 leaves room for an implementation that computes each weight in
 fp32 as 2^((l - l_max) * log2(e) / T) (relative error below ~2e-6 for every
@@ -90,7 +92,7 @@ def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
         keep = e[ranked] >= mp
         n_mp = int(np.count_nonzero(keep))
         margin = np.inf
-        if n_mp > 0:
+        if n_mp > 0 and l[ranked[n_mp - 1]] < l.max():      # ratio exactly 1 at the maximum: exact
             margin = (e[ranked[n_mp - 1]] - mp) / mp
         if n_mp < len(ranked):
             margin = min(margin, (mp - e[ranked[n_mp]]) / mp)

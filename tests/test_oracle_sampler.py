@@ -281,3 +281,16 @@ def test_min_p_boundary_is_flagged():
     assert flagged
     _, flagged = oracle.sample_row(logits, 1.0, -1, 1.0, 0.3, min_p=0.2)
     assert not flagged
+
+
+def test_min_p_one_at_the_maximum_is_exact():
+    """min_p = 1 (or above, acting as 1) sits exactly on the ratio of every
+    token at the maximum logit, which is 1 on any arithmetic: not flagged.
+    A token just below the maximum is on the threshold's other side by its
+    own (tiny) ratio gap: flagged."""
+    for logits in (np.array([0.5, 2.0, -1.0]), np.array([1.0, 3.0, 3.0, 2.0])):
+        for mp in (1.0, 3.0):
+            _, flagged = oracle.sample_row(logits, 0.8, -1, 1.0, 0.7, min_p=mp)
+            assert not flagged
+    _, flagged = oracle.sample_row(np.array([3.0, 3.0 - 1e-9]), 1.0, -1, 1.0, 0.2, min_p=1.0)
+    assert flagged
