@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--skip-extend", action="store_true")
     ap.add_argument("--skip-mixed", action="store_true",
                     help="skip the mixed chunked-prefill + decode batch (page_size 16) timed after the main step")
+    ap.add_argument("--skip-components", action="store_true",
+                    help="skip the q/k norm + RoPE + store, embedding and graph-replay timings")
     ap.add_argument("--copy-calib", action="store_true",
                     help="before warm-up, run plain 1 GiB device copies (untimed) whose counter "
                          "readings calibrate FETCH_SIZE/WRITE_SIZE")
@@ -245,9 +247,10 @@ def main():
 
     if not args.skip_extend:
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
-    result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
-    result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
-    result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
+    if not args.skip_components:
+        result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
+        result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
+        result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
@@ -510,6 +513,11 @@ def bench_mixed(torch, pkv, dev, args):
     def sample(i):
         pkv.sample(bufs[i % len(bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
 
+    d_mp = torch.full((rows,), 0.05, dtype=torch.float32, device=dev)
+
+    def sample_min_p(i):  # the same rows with min_p = 0.05 on top
+        pkv.sample(bufs[i % len(bufs)], d_T, d_K, d_P, d_u, min_p=d_mp, out=tokens, workspace=s_ws)
+
     def timed(fn, n):
         for i in range(3):
             fn(i)
@@ -526,6 +534,7 @@ def bench_mixed(torch, pkv, dev, args):
     dec_us = timed(lambda i: decode(), n)
     ext_us = timed(lambda i: extend(), n)
     smp_us = timed(sample, 4 * n)
+    smp_mp_us = timed(sample_min_p, 4 * n)
     step_us = timed(lambda i: (decode(), extend(), sample(i)), n)
     kv_bytes = dec_kv * HKV * HEAD_DIM * 2 * 2
     flops = 4.0 * HEAD_DIM * HQ * float(np.sum(E[ext] * C[ext] + E[ext] * (E[ext] + 1) / 2.0))
@@ -533,7 +542,7 @@ def bench_mixed(torch, pkv, dev, args):
     ext_tf = flops / (ext_us * 1e-6) / 1e12
     smp_gbs = rows * cfg.vocab * 2 / (smp_us * 1e-6) / 1e9
     log(f"mixed242: decode {dec_us:.1f} us ({dec_gbs:.0f} GB/s) | extend {ext_us:.1f} us ({ext_tf:.0f} TFLOP/s) "
-        f"| sample {smp_us:.1f} us ({smp_gbs:.0f} GB/s) | step {step_us:.1f} us")
+        f"| sample {smp_us:.1f} us ({smp_gbs:.0f} GB/s; {smp_mp_us:.1f} us with min_p 0.05) | step {step_us:.1f} us")
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the mixed batch")
     return {"mixed242_workload": f"240 decode rows (device_len {int(S[dec].min())}..{int(S[dec].max())}, "
@@ -545,6 +554,7 @@ def bench_mixed(torch, pkv, dev, args):
             "mixed242_extend_frac_mfma": round(ext_tf / BF16_MFMA_PEAK_TFLOPS, 4),
             "mixed242_sample_us": round(smp_us, 2), "mixed242_sampler_gbs": round(smp_gbs, 1),
             "mixed242_sampler_tokens_per_s": round(rows / (smp_us * 1e-6), 1),
+            "mixed242_sample_min_p_us": round(smp_mp_us, 2),
             "mixed242_step_us": round(step_us, 2)}
 
 

@@ -12,7 +12,7 @@
  *   2. pkv_paged_attention_decode   GQA attention of one new token per request
  *      pkv_paged_attention_extend   causal GQA attention of a chunk of new tokens
  *                                   over a cached prefix (prefill / extend);
- *   3. pkv_sample                   temperature -> top-k -> top-p -> draw per row,
+ *   3. pkv_sample                   temperature -> top-k -> top-p (-> min_p) -> draw per row,
  *                                   or argmax when the whole batch is greedy.
  *
  * Conventions shared by every entry point
@@ -239,6 +239,8 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  *   top_k     device int32 [bs] or NULL; top_k <= 0 or >= vocab: no top-k.
  *   top_p     device float [bs] or NULL; top_p >= 1: no top-p; else clamped
  *             to >= 1e-6.
+ *   min_p     device float [bs] or NULL ([ENG] 练习 and its answer); min_p <= 0:
+ *             no min_p; values above 1 act as 1.
  *   uniforms  device float [bs], u in [0, 1); may be NULL iff temperature is NULL.
  *   out_tokens device int32 [bs].
  * Row semantics when temperature is given: temperature <= 1e-6 -> argmax of
@@ -246,6 +248,11 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  * tokens ranked by logit (ties -> lower index first); top-k keeps ranks < k;
  * top-p keeps a ranked token iff the renormalised kept mass before it is
  * < top_p (the first token always survives); top-k is applied before top-p.
+ * min_p keeps a token iff its probability is at least min_p times the
+ * largest probability of the row (on the full tempered distribution, not the
+ * renormalised top-k set); the kept set is the intersection of that set with
+ * the top-k / top-p set (both are prefixes of the ranking, so the first
+ * token always survives).
  * The draw scans the kept tokens in vocabulary order and returns the first
  * whose running kept mass exceeds u * (total kept mass) (the last kept token
  * if rounding finds none).
@@ -261,8 +268,8 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  */
 int pkv_sample(const void* logits, int32_t logits_dtype, int32_t bs, int32_t vocab,
                int64_t row_stride, const float* temperature, const int32_t* top_k,
-               const float* top_p, const float* uniforms, int32_t* out_tokens,
-               void* ws, size_t ws_bytes, void* stream);
+               const float* top_p, const float* min_p, const float* uniforms,
+               int32_t* out_tokens, void* ws, size_t ws_bytes, void* stream);
 
 size_t pkv_sample_workspace_size(int32_t bs, int32_t vocab);
 

@@ -253,16 +253,18 @@ def sample_workspace(bs: int, vocab: int, device):
     return torch.empty(max(1, sample_workspace_size(bs, vocab)), dtype=torch.uint8, device=device)
 
 
-def sample(logits, temperature=None, top_k=None, top_p=None, uniforms=None, *, out=None, workspace=None,
-           stream=None):
-    """One token per row (pkv_sample). temperature None = all-greedy batch."""
+def sample(logits, temperature=None, top_k=None, top_p=None, uniforms=None, *, min_p=None, out=None,
+           workspace=None, stream=None):
+    """One token per row (pkv_sample). temperature None = all-greedy batch;
+    min_p None = no min_p."""
     torch = _torch()
     _cuda(logits, "logits")
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be [bs, vocab] with dense rows")
     bs, vocab = logits.shape
     for t, n, dt in ((temperature, "temperature", torch.float32), (top_k, "top_k", torch.int32),
-                     (top_p, "top_p", torch.float32), (uniforms, "uniforms", torch.float32)):
+                     (top_p, "top_p", torch.float32), (min_p, "min_p", torch.float32),
+                     (uniforms, "uniforms", torch.float32)):
         if t is not None:
             _cuda(t, n)
             if t.dtype != dt or t.dim() != 1 or t.shape[0] < bs or t.stride(0) != 1:
@@ -271,7 +273,8 @@ def sample(logits, temperature=None, top_k=None, top_p=None, uniforms=None, *, o
         out = torch.empty(bs, dtype=torch.int32, device=logits.device)
     ws = _workspace(sample_workspace_size(bs, vocab), logits.device, workspace)
     check(lib().pkv_sample(logits.data_ptr(), _dtype_code(logits), bs, vocab, logits.stride(0),
-                           _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(uniforms), out.data_ptr(),
+                           _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(min_p), _ptr(uniforms),
+                           out.data_ptr(),
                            _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
     return out
 

@@ -5,6 +5,9 @@
 // k most probable tokens; the kept mass is renormalised; top-p keeps a ranked
 // token iff the kept mass ranked before it is < p; one token is drawn from
 // the rest. Greedy rows (T <= 1e-6, or no temperature array) are argmax.
+// min_p ("Engine 与采样器", section 练习 and its answer) keeps a token iff its
+// probability is at least min_p times the largest, on the full tempered
+// distribution; that set is intersected with the top-k / top-p set.
 //
 // The pages' GPU path calls FlashInfer's rejection-sampling kernels; this is
 // a different, exact design. Ranking uses
@@ -18,18 +21,20 @@
 //   small batches). A slice reads its tokens once, turns them into
 //   order-preserving biased 16-bit keys with packed 16-bit integer ops (-0
 //   and +0 share a key) and hands over its maximum key and the first index
-//   of it, its mass relative to its maximum (rows without top-k) and a
-//   256-bin count histogram of the keys within 255 of its maximum (rows with
-//   top-k or top-p).
+//   of it, its mass relative to its maximum (rows that draw from the whole
+//   row or cut top-p over it) and a 256-bin count histogram of the keys
+//   within 255 of its maximum (rows with top-k, top-p or min_p).
 // * The finish kernel (one workgroup per row) takes the row maximum and
 //   shifts every slice histogram by the slice's distance to it, so the bins
 //   add into the row's window histogram. All tokens of a bin share one key
 //   and one weight: the top-k threshold and the top-p cut come from counts
 //   times weights, the ties at the cut keep the first n equal-key tokens in
 //   index order, and every slice's kept mass follows from its histogram.
-//   The draw (kept weights in index order, first running mass > u * W)
-//   picks one slice by those masses and scans its 8192 tokens. Cuts below
-//   the window take the generic path below over the row in memory.
+//   The min_p cut is the first bin whose weight is below min_p (a bin's
+//   tokens share one weight, so it never splits a bin). The draw (kept
+//   weights in index order, first running mass > u * W) picks one slice by
+//   those masses and scans its 8192 tokens. Cuts below the window take the
+//   generic path below over the row in memory.
 //
 // fp32 rows (the memory kernel) and the generic path: every
 // pass reads 16-byte chunks from memory (wave w owns a contiguous chunk range,
@@ -55,6 +60,7 @@ struct SampleArgs {
   const float* temperature;  // NULL = all greedy
   const int32_t* top_k;
   const float* top_p;
+  const float* min_p;        // NULL = no min_p
   const float* uniforms;
   int32_t* out;
 };
@@ -581,9 +587,9 @@ PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds<NW>& s, PF pred, WF
 
 // Per-row parameters (wave-uniform).
 struct SampleParams {
-  float c2, u, p;
+  float c2, u, p, mp;
   int32_t k;
-  bool greedy, use_k, use_p;
+  bool greedy, use_k, use_p, use_mp;
 
   PKV_INLINE void load(const SampleArgs& a, int row, int V) {
     const float temp = a.temperature ? a.temperature[row] : 0.f;
@@ -594,9 +600,17 @@ struct SampleParams {
     p = (!greedy && a.top_p) ? a.top_p[row] : 1.f;
     use_p = p < 1.f;
     if (use_p) p = fmaxf(p, 1e-6f);
+    mp = (!greedy && a.min_p) ? fminf(a.min_p[row], 1.f) : 0.f;  // above 1 acts as 1
+    use_mp = mp > 0.f;
     c2 = greedy ? 0.f : 1.4426950408889634f / temp;
     u = greedy ? 0.f : a.uniforms[row];
   }
+  // every token kept: the draw runs over the whole row's mass
+  PKV_INLINE bool plain() const { return !greedy && !use_k && !use_p && !use_mp; }
+  // the whole row's mass is needed: plain rows, and top-p over the whole row
+  PKV_INLINE bool need_mass() const { return !greedy && !use_k && (use_p || !use_mp); }
+  // a cut is needed
+  PKV_INLINE bool need_cut() const { return !greedy && (use_k || use_p || use_mp); }
 };
 
 // Cuts and draw over the row in memory (any cut depth, any number of kept
@@ -660,7 +674,9 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
         if (!kept_k(i, l)) return 0.f;
         const uint32_t key = E::key(l);
         if (sp.use_p && !(key > kp_key || (key == kp_key && i <= kp_last))) return 0.f;
-        return wt(l);
+        const float w = wt(l);
+        if (sp.use_mp && w < sp.mp) return 0.f;  // min_p: a whole key group at a time (one key, one weight)
+        return w;
       },
       [&](double total) { return (double)u * total; });
 }
@@ -697,7 +713,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a
   int32_t idx;
   if (sp.greedy) {
     idx = argmax;
-  } else if (!sp.use_k && !sp.use_p) {
+  } else if (sp.plain()) {
     const float u = sp.u, c2 = sp.c2;
     idx = find_crossing(row, s, [&](int, float l) { return row_weight(l, m, c2); },
                         [&](double total) { return (double)u * total; });
@@ -787,9 +803,9 @@ PKV_INLINE void wave_select_bins(AF amount, CF count, double goal, int* bin, dou
 // fastest, so greedy and sampled rows share every CU). Thread t holds
 // chunks t, t + 256, t + 512, t + 768 of the slice. The tokens become biased
 // 16-bit keys; the slice writes its maximum and the first index of it, its
-// mass relative to its maximum (rows without top-k) and a count histogram of
-// the keys within 255 of its maximum (bin d = kmax - key; rows with top-k or
-// top-p).
+// mass relative to its maximum (SampleParams::need_mass) and a count
+// histogram of the keys within 255 of its maximum (bin d = kmax - key;
+// SampleParams::need_cut).
 __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs a, SampleWs ws) {
   __shared__ uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
   __shared__ double wmass[kSliceWaves];
@@ -800,8 +816,8 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row, V);
-  const bool need_mass = !sp.greedy && !sp.use_k;
-  const bool need_hist = !sp.greedy && (sp.use_k || sp.use_p);
+  const bool need_mass = sp.need_mass();
+  const bool need_hist = sp.need_cut();
   const bool tail = slice == S - 1;  // the only slice with tokens at or past V
   const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
                                                      (int64_t)row * a.row_stride);
@@ -965,8 +981,8 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row, V);
-  const bool need_mass = !sp.greedy && !sp.use_k;
-  const bool plain = !sp.greedy && !sp.use_k && !sp.use_p;
+  const bool need_mass = sp.need_mass();
+  const bool plain = sp.plain();
   const float c2 = sp.c2;
   const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
                                                      (int64_t)row * a.row_stride);
@@ -1089,6 +1105,26 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
           double need = ceil((target - above) / (double)s.wtab[dstar]);
           if (!(need >= 1.0)) need = 1.0;
           tk2 = need >= (double)n_at ? n_at : (uint32_t)need;
+        }
+      }
+      if (sp.use_mp) {
+        // min_p keeps the bins whose weight (probability over the largest)
+        // is at least mp: bins d < dm, dm the first bin below it (-1 when
+        // every bin of the window is kept, i.e. its cut lies below the
+        // window). Both sets are prefixes of the ranking, so their
+        // intersection is the shorter one; bin dm keeps no token.
+        int dm = -1;
+#pragma unroll
+        for (int e = kHistBins / kWave - 1; e >= 0; --e) {
+          const uint64_t bl = __ballot(s.wtab[e * kWave + lane] < sp.mp);
+          if (bl) dm = e * kWave + __ffsll((unsigned long long)bl) - 1;
+        }
+        if (!sp.use_k && !sp.use_p) {
+          dc = dm;
+          tk2 = 0;
+        } else if (dc >= 0 && dm >= 0 && dm <= dc) {
+          dc = dm;
+          tk2 = 0;
         }
       }
       if (lane == 0) {

@@ -189,8 +189,8 @@ def test_decode_workspace_size_grows_with_batch(L):
 
 
 def _sample(L, logits=0x100000, dt=1, bs=4, V=1024, stride=1024, T=0x200000, K=None, P=None, u=0x300000,
-            out=0x400000, ws=0x500000, ws_bytes=1 << 30):
-    return L.pkv_sample(logits, dt, bs, V, stride, T, K, P, u, out, ws, ws_bytes, None)
+            out=0x400000, ws=0x500000, ws_bytes=1 << 30, MP=None):
+    return L.pkv_sample(logits, dt, bs, V, stride, T, K, P, MP, u, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -24,15 +24,15 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _run(logits, dtype, T, K, P, u, what, max_flag_frac=0.05):
-    """logits: numpy in kernel dtype ([bs, V]); T/K/P: prepared arrays or None."""
+def _run(logits, dtype, T, K, P, u, what, max_flag_frac=0.05, MP=None):
+    """logits: numpy in kernel dtype ([bs, V]); T/K/P/MP: prepared arrays or None."""
     print(f"sample case {what} shape={logits.shape} dtype={dtype}", flush=True)
     d = lambda x: None if x is None else to_dev(x)
-    tok = pkv.sample(to_dev(logits, dtype), d(T), d(K), d(P), d(u))
+    tok = pkv.sample(to_dev(logits, dtype), d(T), d(K), d(P), d(u), min_p=d(MP))
     torch.cuda.synchronize()
     got = to_host(tok)
     lf = oracle.widen(logits, dtype)
-    want, flagged = oracle.sample(lf, T, K, P, u)
+    want, flagged = oracle.sample(lf, T, K, P, u, min_p=MP)
     bad = np.nonzero((got != want) & ~flagged)[0]
     assert bad.size == 0, f"{what}: rows {bad[:10].tolist()} got {got[bad[:10]].tolist()} " \
                           f"want {want[bad[:10]].tolist()}"
@@ -256,3 +256,72 @@ def test_largest_bf16_vocabulary():
     with pytest.raises(pkv.PkvError):
         pkv.sample(torch.zeros((1, V + 8), dtype=torch.bfloat16, device="cuda"),
                    to_dev(T[:1]), None, None, to_dev(u[:1]))
+
+
+# ---------------------------------------------------------------- min_p
+# ("Engine 与采样器", section 练习 and its answer: keep a token iff its
+# probability is at least min_p times the largest, on the full tempered
+# distribution; intersected with the top-k / top-p set)
+
+
+@pytest.mark.parametrize("name,V,T,k,p,mp", [
+    ("mp-only", 151936, 1.0, -1, 1.0, 0.1),        # cut inside the 256-key window
+    ("mp-k50", 151936, 1.0, 50, 1.0, 0.05),
+    ("mp-p", 151936, 0.7, -1, 0.9, 0.2),           # top-p over the whole row's mass, then min_p
+    ("mp-k50-p95", 151936, 1.0, 50, 0.95, 0.1),
+    ("mp-loose-k", 151936, 1.0, 5, 1.0, 1e-4),     # top-k is the tighter cut
+    ("mp-1", 151936, 1.0, -1, 1.0, 1.0),           # only the largest key survives
+    ("mp-above-1", 151936, 0.8, 40, 0.9, 3.0),     # acts as 1
+    ("mp-deep", 1024, 1.5, -1, 1.0, 0.003),        # cut below the window -> generic path
+    ("mp-deep-bigk", 1024, 0.7, 600, 1.0, 0.01),   # top-k below the window, min_p inside -> generic path
+    ("mp-deep-p", 1024, 2.0, -1, 0.97, 0.004),
+])
+def test_min_p_paths(name, V, T, k, p, mp):
+    bs = 32
+    rng = _rng(name)
+    x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+    Ta = np.full(bs, T, np.float32)
+    Ka = None if k < 0 else np.full(bs, k, np.int32)
+    Pa = None if p >= 1.0 else np.full(bs, p, np.float32)
+    MP = np.full(bs, mp, np.float32)
+    MP[2] = 0.0                                   # rows without min_p in the same batch
+    MP[3] = -1.0
+    u = rng.random(bs, dtype=np.float32)
+    u[0], u[1] = 0.0, np.float32(0.99999994)
+    got, _, _ = _run(_bf16(x), "bf16", Ta, Ka, Pa, u, name, max_flag_frac=None, MP=MP)
+    _run(x, "f32", Ta, Ka, Pa, u, name + "-f32", max_flag_frac=None, MP=MP)
+    if mp >= 1.0:  # only the maximum's key group survives: on rows with one maximum, the argmax
+        xb = oracle.widen(_bf16(x), "bf16")
+        rows = (MP > 0) & ((xb == xb.max(axis=1, keepdims=True)).sum(axis=1) == 1)
+        assert rows.sum() >= bs // 2
+        assert np.array_equal(got[rows], np.argmax(xb, axis=1)[rows])
+
+
+def test_min_p_closed_form():
+    """Three tokens above a low floor at logits 0, -1, -2 (exact in bf16),
+    T = 1: their probabilities over the largest are 1, e^-1, e^-2; the
+    floor's e^-20 is below every min_p used and its total mass (4093 e^-20,
+    under 1e-5) moves no boundary. The kept set and the drawn
+    token follow by hand: min_p 0.2 keeps {10, 500} (W = 1 + e^-1),
+    min_p 0.1 keeps {10, 500, 700}; top-k 2 or top-p 0.5 cut it further."""
+    V = 4096
+    base = np.full(V, -20.0, np.float32)
+    base[[10, 500, 700]] = [0.0, -1.0, -2.0]
+    e1, e2 = np.exp(-1.0), np.exp(-2.0)
+    cases = [  # (min_p, top_k, top_p, u, token)
+        (0.2, 0, 1.0, 0.5, 10), (0.2, 0, 1.0, 0.9, 500), (0.2, 0, 1.0, 1 / (1 + e1) + 1e-3, 500),
+        (0.2, 0, 1.0, 1 / (1 + e1) - 1e-3, 10),
+        (0.1, 0, 1.0, 0.9, 500), (0.1, 0, 1.0, 0.95, 700), (0.1, 0, 1.0, (1 + e1) / (1 + e1 + e2) + 1e-3, 700),
+        (0.1, 2, 1.0, 0.95, 500), (0.1, 0, 0.5, 0.95, 10), (0.5, 0, 1.0, 0.99, 10), (0.3, 3, 0.9, 0.99, 500),
+    ]
+    bs = len(cases)
+    x = np.tile(base, (bs, 1))
+    MP = np.array([c[0] for c in cases], np.float32)
+    K = np.array([c[1] for c in cases], np.int32)
+    P = np.array([c[2] for c in cases], np.float32)
+    u = np.array([c[3] for c in cases], np.float32)
+    T = np.ones(bs, np.float32)
+    want = [c[4] for c in cases]
+    for dt, xx in (("bf16", _bf16(x)), ("f32", x)):
+        got, _, flagged = _run(xx, dt, T, K, P, u, f"min_p-closed-form-{dt}", max_flag_frac=0.0, MP=MP)
+        assert got.tolist() == want
