@@ -251,6 +251,7 @@ def main():
         result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
         result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
         result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
+        result["components"].update(bench_sampler_variants(torch, pkv, gen, dev, args))
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
@@ -389,6 +390,58 @@ def bench_embedding(torch, pkv, gen, dev, args):
         out[f"embedding_{name}_gbs"] = round(gbs, 1)
         out[f"embedding_{name}_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
     del W
+    return out
+
+
+def bench_sampler_variants(torch, pkv, gen, dev, args):
+    """The sampler on [256, 151936] logits, bf16 and fp32 (the dtype of an
+    fp32 logits buffer), one parameter mix per batch: all greedy, plain
+    (T = 1, no cut), top-k 50, top-p 0.9, top-k 50 + top-p 0.95, min_p 0.05,
+    and all three cuts. Logits ~ N(0, 3^2) drawn on the device, rotated over
+    311 MB of buffers so the Infinity Cache does not hold them. Algorithmic
+    bytes per call: one read of the logits."""
+    bs, V = 256, 151936
+    out = {}
+    tokens = torch.empty(bs, dtype=torch.int32, device=dev)
+    ws = pkv.sample_workspace(bs, V, dev)
+    u = torch.rand(bs, generator=gen, device=dev)
+    full = lambda v, dt=torch.float32: torch.full((bs,), v, dtype=dt, device=dev)
+    mixes = [("greedy", None, None, None, None), ("plain", full(1.0), None, None, None),
+             ("topk50", full(1.0), full(50, torch.int32), None, None),
+             ("topp09", full(1.0), None, full(0.9), None),
+             ("k50_p095", full(1.0), full(50, torch.int32), full(0.95), None),
+             ("minp005", full(1.0), None, None, full(0.05)),
+             ("k50_p095_minp005", full(1.0), full(50, torch.int32), full(0.95), full(0.05))]
+    ptr = lambda t: None if t is None else t.data_ptr()
+    fn = pkv.lib().pkv_sample
+    stream = torch.cuda.current_stream().cuda_stream
+    for dt, code, nbuf in ((torch.bfloat16, 1, 4), (torch.float32, 0, 2)):
+        tag = "bf16" if code else "f32"
+        bufs = [(torch.randn((bs, V), generator=gen, device=dev) * 3.0).to(dt) for _ in range(nbuf)]
+        for name, T, K, P, MP in mixes:
+            calls = [(b.data_ptr(), code, bs, V, V, ptr(T), ptr(K), ptr(P), ptr(MP), u.data_ptr(),
+                      tokens.data_ptr(), ws.data_ptr(), ws.numel(), stream) for b in bufs]
+            for c in calls:
+                if fn(*c) != 0:
+                    raise RuntimeError(pkv.lib().pkv_last_error().decode())
+            torch.cuda.synchronize()
+            reps = max(8, args.steps // 4) * nbuf
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(*calls[i % nbuf])
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            gbs = bs * V * bufs[0].element_size() / (us * 1e-6) / 1e9
+            key = f"sampler256_{tag}_{name}"
+            out[key + "_us"] = round(us, 2)
+            out[key + "_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        log(f"sampler [256, 151936] {tag}: " + ", ".join(f"{n} {out[f'sampler256_{tag}_{n}_us']:.1f} us"
+                                                          for n, *_ in mixes))
+        del bufs
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the sampler variants")
     return out
 
 

@@ -396,9 +396,20 @@ struct SampleRow {
     return x;
   }
   // f(c, x, ok) for every round c < rounds, in order (wave-uniform loop).
+  // The loads of four rounds are issued before the first is used, so each
+  // lane keeps four 16-byte reads in flight (one workgroup per row is
+  // otherwise bound by the latency of one read at a time).
   template <class F>
   PKV_INLINE void for_rounds(F f) const {
-    for (int c = 0; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
+    int c = 0;
+    for (; c + 4 <= rounds; c += 4) {
+      const u32x4 x0 = fetch(c), x1 = fetch(c + 1), x2 = fetch(c + 2), x3 = fetch(c + 3);
+      f(c, x0, chunk_ok(c));
+      f(c + 1, x1, chunk_ok(c + 1));
+      f(c + 2, x2, chunk_ok(c + 2));
+      f(c + 3, x3, chunk_ok(c + 3));
+    }
+    for (; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
   }
   // f(i, l) for every element (index, logit) of chunk x of round c.
   template <class F>
