@@ -396,8 +396,8 @@ def bench_embedding(torch, pkv, gen, dev, args):
 def bench_sampler_variants(torch, pkv, gen, dev, args):
     """The sampler on [256, 151936] logits, bf16 and fp32 (the dtype of an
     fp32 logits buffer), one parameter mix per batch: all greedy, plain
-    (T = 1, no cut), top-k 50, top-p 0.9, top-k 50 + top-p 0.95, min_p 0.05,
-    and all three cuts. Logits ~ N(0, 3^2) drawn on the device, rotated over
+    (T = 1, no cut), top-k 50, top-p 0.9 (at T = 1 and at T = 0.7), top-k 50
+    + top-p 0.95, min_p 0.05, and all three cuts; T = 1 unless stated. Logits ~ N(0, 3^2) drawn on the device, rotated over
     311 MB of buffers so the Infinity Cache does not hold them. Algorithmic
     bytes per call: one read of the logits."""
     bs, V = 256, 151936
@@ -409,6 +409,7 @@ def bench_sampler_variants(torch, pkv, gen, dev, args):
     mixes = [("greedy", None, None, None, None), ("plain", full(1.0), None, None, None),
              ("topk50", full(1.0), full(50, torch.int32), None, None),
              ("topp09", full(1.0), None, full(0.9), None),
+             ("t07_topp09", full(0.7), None, full(0.9), None),
              ("k50_p095", full(1.0), full(50, torch.int32), full(0.95), None),
              ("minp005", full(1.0), None, None, full(0.05)),
              ("k50_p095_minp005", full(1.0), full(50, torch.int32), full(0.95), full(0.05))]

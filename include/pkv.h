@@ -257,9 +257,10 @@ size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_
  * whose running kept mass exceeds u * (total kept mass) (the last kept token
  * if rounding finds none).
  *   ws        device workspace of pkv_sample_workspace_size(bs, vocab) bytes,
- *             16-byte aligned; required for bf16 logits (per-slice records,
- *             slice masses and key histograms, written by the first of the
- *             two kernels and read by the second), unused for fp32. Its
+ *             16-byte aligned; required (per-slice records and masses, and
+ *             the key histograms of bf16 rows or the candidate lists of fp32
+ *             rows, written by the first of two kernels and read by the
+ *             second; the size covers both dtypes). Its
  *             contents need no initialisation and are not kept between
  *             calls; calls that share a workspace must not overlap in time
  *             (different streams race). PKV_ERR_WORKSPACE if missing or

@@ -103,8 +103,6 @@ struct SampleElem<float> {
   }
 };
 
-constexpr int kSampleThreads = 512;
-constexpr int kSampleWaves = kSampleThreads / kWave;
 constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave with a group-mass slot
 
 // ---------------------------------------------------------------- wave helpers
@@ -426,6 +424,86 @@ struct SampleRow {
   }
 };
 
+constexpr int kCandCap = 1024;  // fp32 rows: listed tokens per slice at most
+constexpr int kMaxSlicesPow2 = 128;  // a power of two >= the slices of a row (binary search)
+
+// fp32 rows: the slices' candidate lists read as one row. Entry j of slice
+// s's list is (logit bits, vocabulary index) of the j-th token the slice
+// listed, in index order, so the lists one after another are in index order
+// too. The lists are packed: chunk q (two entries, 16 bytes) is chunk
+// q - beg[s] of slice s, the last slice with beg[s] <= q (beg = exclusive
+// prefix of the slices' chunk counts, found by a binary search). An entry
+// past its list's end reads as the NaN pattern 0xffffffff, whose key is 0;
+// every token whose key is below `floor` (>= 1) is absent, so what remains
+// is exactly the row's tokens with key >= floor (each slice lists all of its
+// tokens at or above its own floor, and floor is the largest of those).
+template <int NW>
+struct CandRow {
+  using E = SampleElem<float>;
+  static constexpr int kPerChunk = 2;
+  const uint2* lists;
+  const int32_t* beg;  // [slices] first packed chunk of each list
+  const int32_t* cnt;  // [slices] list lengths
+  int slices;
+  uint32_t floor;
+  int nchunks, cpw, rounds, wave, lane;
+
+  PKV_INLINE void init(const uint2* l, const int32_t* b, const int32_t* n, int S, int chunks, uint32_t floor_key,
+                       int w, int ln) {
+    lists = l;
+    beg = b;
+    cnt = n;
+    slices = S;
+    floor = floor_key;
+    nchunks = chunks;
+    cpw = (nchunks + NW - 1) / NW;
+    rounds = (cpw + kWave - 1) / kWave;
+    wave = w;
+    lane = ln;
+  }
+  PKV_INLINE int chunk_id(int c) const { return wave * cpw + c * kWave + lane; }
+  PKV_INLINE bool chunk_ok(int c) const { return c * kWave + lane < cpw && chunk_id(c) < nchunks; }
+  PKV_INLINE u32x4 fetch(int c) const {
+    u32x4 x = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    if (chunk_ok(c)) {
+      const int q = chunk_id(c);
+      int sl = 0;
+#pragma unroll
+      for (int step = kMaxSlicesPow2 / 2; step > 0; step >>= 1)
+        if (sl + step < slices && beg[sl + step] <= q) sl += step;
+      const int j = kPerChunk * (q - beg[sl]);
+      x = *reinterpret_cast<const u32x4*>(lists + (int64_t)sl * kCandCap + j);
+      if (j + 1 >= cnt[sl]) x[2] = 0xffffffffu;
+    }
+    return x;
+  }
+  template <class F>
+  PKV_INLINE void for_rounds(F f) const {
+    int c = 0;
+    for (; c + 4 <= rounds; c += 4) {
+      const u32x4 x0 = fetch(c), x1 = fetch(c + 1), x2 = fetch(c + 2), x3 = fetch(c + 3);
+      f(c, x0, chunk_ok(c));
+      f(c + 1, x1, chunk_ok(c + 1));
+      f(c + 2, x2, chunk_ok(c + 2));
+      f(c + 3, x3, chunk_ok(c + 3));
+    }
+    for (; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
+  }
+  template <class F>
+  PKV_INLINE void elements(int c, const u32x4& x, bool ok, F f) const {
+    if (!ok) return;
+#pragma unroll
+    for (int e = 0; e < kPerChunk; ++e) {
+      const float l = __uint_as_float(x[2 * e]);
+      if (E::key(l) >= floor) f((int)x[2 * e + 1], l);
+    }
+  }
+  template <class F>
+  PKV_INLINE void for_each(F f) const {
+    for_rounds([&](int c, const u32x4& x, bool ok) { elements(c, x, ok, f); });
+  }
+};
+
 // w(l) = exp2((l - l_max) * c2)
 PKV_INLINE float row_weight(float l, float lmax, float c2) { return fast_exp2((l - lmax) * c2); }
 
@@ -627,11 +705,36 @@ struct SampleParams {
 // Cuts and draw over the row in memory (any cut depth, any number of kept
 // tokens): radix descents for the top-k threshold and the top-p cut,
 // group-mass scans for the ties at each cut and for the draw.
+//
+// Over a part of the row that holds every token at or above some key (the
+// candidate lists), `covered` is given: the result is the whole row's iff
+// every cut falls inside that part, which holds when it has at least k
+// tokens (top-k), when its mass reaches the top-p target (top-p without
+// top-k, whose target is p times the whole row's mass w_row), and, for
+// min_p alone, when every token outside it (logits <= below_max) or one of
+// its own falls below min_p; *covered is false (and the result
+// meaningless) otherwise. Block-uniform.
 template <class RowT, int NW>
-PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const SampleParams& sp, float lmax) {
+PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const SampleParams& sp, float lmax,
+                                  const double* w_row = nullptr, bool* covered = nullptr,
+                                  float below_max = INFINITY) {
   using E = typename RowT::E;
   const float c2 = sp.c2;
   auto wt = [&](float l) { return row_weight(l, lmax, c2); };
+  if (covered) {
+    *covered = true;
+    if (sp.use_k && row_sum(row, s, [](int, float) { return 1.f; }) < (double)sp.k) {
+      *covered = false;
+      return -1;
+    }
+    // min_p alone: covered when every token below the part weighs below
+    // min_p (below_max: the largest logit below it), or one of its own does
+    if (sp.use_mp && !sp.use_k && !sp.use_p && !(wt(below_max) < sp.mp) &&
+        row_sum(row, s, [&](int, float l) { return wt(l) < sp.mp ? 1.f : 0.f; }) == 0.0) {
+      *covered = false;
+      return -1;
+    }
+  }
 
   // top-k: threshold key kk_key; equal keys kept up to index kk_last
   uint32_t kk_key = 0, kk_eq = 0, kk_take = 0;
@@ -657,7 +760,16 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
   uint32_t kp_key = 0;
   int32_t kp_last = 0x7fffffff;
   if (sp.use_p) {
-    const double Wk = row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
+    double Wk;
+    if (covered && !sp.use_k) {  // top-p over the whole row: its mass, and the part must reach the target
+      Wk = *w_row;
+      if (row_sum(row, s, [&](int, float l) { return wt(l); }) < (double)sp.p * Wk) {
+        *covered = false;
+        return -1;
+      }
+    } else {
+      Wk = row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
+    }
     const double target = (double)sp.p * Wk;
     double above;
     uint32_t n_at;
@@ -692,48 +804,6 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
       [&](double total) { return (double)u * total; });
 }
 
-// ---------------------------------------------------------------- memory kernel (fp32; long bf16 rows)
-
-template <typename T>
-__global__ void __launch_bounds__(kSampleThreads) sample_mem_kernel(SampleArgs a) {
-  __shared__ SampleLds<kSampleWaves> s;
-  const int row_id = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  SampleParams sp;
-  sp.load(a, row_id, a.vocab);
-  SampleRow<T, kSampleWaves> row;
-  row.init(reinterpret_cast<const T*>(a.logits) + (int64_t)row_id * a.row_stride, a.vocab, wave, lane);
-
-  // maximum and the first index of it (-0 == +0 compare equal)
-  float vmax = -INFINITY;
-  int32_t imax = 0x7fffffff;
-  row.for_each([&](int i, float l) {
-    if (l > vmax) {
-      vmax = l;
-      imax = i;
-    }
-  });
-  float m = wave_max_f32(vmax);
-  __syncthreads();
-  if (lane == 0) s.wave_f[wave] = m;
-  __syncthreads();
-  m = (float)s.wave_f[0];
-  for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, (float)s.wave_f[w]);
-  const int32_t am = block_reduce_i32(s, vmax == m ? imax : 0x7fffffff, false);
-  const int32_t argmax = am == 0x7fffffff ? 0 : am;
-  int32_t idx;
-  if (sp.greedy) {
-    idx = argmax;
-  } else if (sp.plain()) {
-    const float u = sp.u, c2 = sp.c2;
-    idx = find_crossing(row, s, [&](int, float l) { return row_weight(l, m, c2); },
-                        [&](double total) { return (double)u * total; });
-  } else {
-    idx = sample_generic(row, s, sp, m);
-  }
-  if (tid == 0) a.out[row_id] = idx >= 0 ? idx : argmax;
-}
-
 // ---------------------------------------------------------------- bf16: slice kernel + finish kernel
 
 constexpr int kSliceThreads = 256;                                // 4 waves: many workgroups per CU
@@ -749,15 +819,18 @@ constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kDrawChunks = kSliceTokens / (8 * kFinishThreads);  // 1: 8 tokens per finishing thread
 
 __host__ __device__ inline int sample_slices(int V) { return (V + kSliceTokens - 1) / kSliceTokens; }
-static_assert((int64_t)kMaxSlices * kSliceTokens <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves * 8,
-              "the generic path covers every row the slices cover");
+static_assert((int64_t)kMaxSlices * kSliceTokens <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves * 4,
+              "the generic path covers every row the slices cover (fp32: four tokens per chunk)");
 static_assert(kMaxSlices <= kFinishThreads, "one slice per finishing thread");
+static_assert(kMaxSlices <= kMaxSlicesPow2 && kMaxSlices <= 2 * kWave, "slices of a row: two per lane, binary search");
 
 // What the slices leave for the finish kernel.
 struct SampleWs {
   uint64_t* recs;      // [bs * S]: slice maximum key | first index of it << 32
   double* masses;      // [bs * S]: slice mass relative to the slice maximum
-  uint32_t* hists;     // [bs * S * kHistWords]: slice window histograms (16-bit counts)
+  uint32_t* hists;     // bf16: [bs * S * kHistWords]: slice window histograms (16-bit counts)
+  uint2* cands;        // fp32: [bs * S * kCandCap]: candidate lists (logit bits, index)
+  uint2* meta;         // fp32: [bs * S]: (list floor key, list length)
 };
 
 // First of NB bins (ascending) whose running amount reaches goal, by one
@@ -1326,6 +1399,320 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   __syncthreads();  // 8
   const int32_t r = s.result >= 0 ? s.result : lk;
   if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
+}
+
+// ---------------------------------------------------------------- fp32: slice kernel + finish kernel
+
+constexpr int kSlice32Rounds = kSliceTokens / (4 * kSliceThreads);  // 8 chunks of 4 floats per thread
+
+// fp32 slice kernel: workgroup b reads slice b / bs of row b % bs (thread t:
+// chunks t + 256i, i < 8). It writes the slice maximum (32-bit key) and the
+// first index of it, the mass relative to it (SampleParams::need_mass) and,
+// for rows with a cut, a candidate list: every token of the slice whose key
+// is at or above a floor, in index order. The floor comes from a count
+// histogram of the keys' upper 16 bits within 255 of the slice maximum's:
+// the deepest bin whose running count stays within kCandCap (for top-k, the
+// first bin where it reaches k, if that fits: no deeper token of this slice
+// can be among the row's k largest; for min_p alone, no deeper than the
+// first bin that weighs below min_p).
+__global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArgs a, SampleWs ws) {
+  using E = SampleElem<float>;
+  constexpr int R = kSlice32Rounds;
+  __shared__ uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
+  __shared__ double wmass[kSliceWaves];
+  __shared__ uint32_t wave_k[kSliceWaves];
+  __shared__ int32_t wave_i[kSliceWaves];
+  __shared__ int32_t rtot[R][kSliceWaves];
+  __shared__ uint32_t floor_sh;
+  const int V = a.vocab, S = sample_slices(V);
+  const int row = blockIdx.x % a.bs, slice = blockIdx.x / a.bs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  SampleParams sp;
+  sp.load(a, row, V);
+  const bool need_mass = sp.need_mass();
+  const bool need_list = sp.need_cut();
+  const bool tail = slice == S - 1;  // the only slice with tokens at or past V
+  const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.logits) +
+                                                     (int64_t)row * a.row_stride);
+  const int last_chunk = (V - 1) / 4;
+  const int t0s = slice * kSliceTokens;
+  u32x4 raw[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)  // indices clamped to the row's last chunk: reads stay in the row
+    raw[i] = __builtin_nontemporal_load(crow + min(t0s / 4 + i * kSliceThreads + tid, last_chunk));
+  if (need_list)  // ordered before the atomics by the barrier of the block maximum
+    for (int b = tid; b < kHistBins + kWave; b += kSliceThreads) hist[b] = 0;
+  // key of token e of chunk round i; 0 (below every real key) at or past V
+  auto key = [&](int i, int e) -> uint32_t {
+    const uint32_t k = E::key(__uint_as_float(raw[i][e]));
+    return (tail && t0s + 4 * (i * kSliceThreads + tid) + e >= V) ? 0u : k;
+  };
+  uint32_t tk = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tk = max(tk, key(i, e));
+  double mass = 0.0;  // relative to this thread's maximum: fp32 within a chunk, fp64 above
+  if (need_mass) {
+    const float c2 = sp.c2, off = -fmaxf(E::key_value(tk), -1e30f) * c2;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float cs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w = fast_exp2(fmaf(__uint_as_float(raw[i][e]), c2, off));
+        cs += key(i, e) ? w : 0.f;
+      }
+      mass += (double)cs;
+    }
+  }
+  // unsigned maximum through the signed one: flipping the top bit keeps the order
+  const uint32_t wk = (uint32_t)wave_max_i32((int32_t)(tk ^ 0x80000000u)) ^ 0x80000000u;
+  if (lane == 0) wave_k[wave] = wk;
+  __syncthreads();
+  uint32_t kmax = wave_k[0];
+#pragma unroll
+  for (int w = 1; w < kSliceWaves; ++w) kmax = max(kmax, wave_k[w]);
+  if (need_mass) {
+    const double sc =
+        (double)fast_exp2((fmaxf(E::key_value(tk), -1e30f) - fmaxf(E::key_value(kmax), -1e30f)) * sp.c2);
+    const double m = wave_sum_f64(mass * sc);
+    if (lane == 0) wmass[wave] = m;
+  }
+  int32_t found = 0x7fffffff;  // first index holding the maximum
+  if (tk == kmax) {
+#pragma unroll
+    for (int i = R - 1; i >= 0; --i)
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (key(i, e) == kmax) found = t0s + 4 * (i * kSliceThreads + tid) + e;
+  }
+  found = wave_min_i32(found);
+  if (lane == 0) wave_i[wave] = found;
+  const uint32_t cmax = kmax >> 16;
+  if (need_list) {  // bin d = cmax - (key >> 16); a token outside the window, or none, to a discard bin
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = key(i, e), d = cmax - (k >> 16);
+        atomicAdd(&hist[(k != 0u && d < (uint32_t)kHistBins) ? d : (uint32_t)(kHistBins + lane)], 1u);
+      }
+  }
+  __syncthreads();
+  if (need_list) {
+    if (wave == 0) {  // the list's floor: lane l holds bins 4l .. 4l + 3
+      uint32_t c[4], run = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hist[4 * lane + e];
+        run += c[e];
+      }
+      const int32_t incl = wave_incl_scan_i32((int32_t)run, lane);
+      int32_t cum = incl - (int32_t)run, d_cap = -1, d_k = 0x7fffffff;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cum += (int32_t)c[e];
+        if (cum <= kCandCap) d_cap = 4 * lane + e;
+        if (cum >= sp.k && d_k == 0x7fffffff) d_k = 4 * lane + e;
+      }
+      d_cap = wave_max_i32(d_cap);
+      d_k = wave_min_i32(d_k);
+      // use_k: a bin whose running count reaches k and fits is deep enough
+      int d = (sp.use_k && d_k <= d_cap) ? d_k : d_cap;
+      if (sp.use_mp && !sp.use_k && !sp.use_p) {
+        // min_p alone: a bin whose largest logit weighs below min_p against
+        // this slice's maximum weighs below it against the row's too: it and
+        // every deeper bin are never kept (the finish kernel checks that the
+        // lists' floor lies below the cut)
+        const float ls = E::key_value(kmax);
+        int d_mp = 0x7fffffff;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = 4 * lane + e;
+          if (b >= 1 && (uint32_t)b <= cmax &&
+              row_weight(E::key_value(((cmax - (uint32_t)b) << 16) | 0xffffu), ls, sp.c2) < sp.mp)
+            d_mp = min(d_mp, b);
+        }
+        d_mp = wave_min_i32(d_mp);
+        if (d_mp != 0x7fffffff) d = min(d, d_mp - 1);
+      }
+      if (lane == 0) floor_sh = d < 0 ? 0xffffffffu : ((uint32_t)d >= cmax ? 1u : (cmax - (uint32_t)d) << 16);
+    }
+    __syncthreads();
+  }
+  const int64_t slot = (int64_t)row * S + slice;  // the row's slices in index order
+  if (need_list) {
+    // listed tokens (key >= floor) in index order: round-major, then thread, then element
+    const uint32_t fl = floor_sh;
+    int32_t n[R], incl[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      n[i] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n[i] += key(i, e) >= fl ? 1 : 0;
+      incl[i] = wave_incl_scan_i32(n[i], lane);
+      if (lane == 63) rtot[i][wave] = incl[i];
+    }
+    __syncthreads();
+    int32_t run = 0, off[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int w = 0; w < kSliceWaves; ++w) {
+        if (w == wave) off[i] = run + incl[i] - n[i];
+        run += rtot[i][w];
+      }
+    uint2* list = ws.cands + slot * kCandCap;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      int32_t pos = off[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (key(i, e) >= fl) {
+          if (pos < kCandCap) list[pos] = make_uint2(raw[i][e], (uint32_t)(t0s + 4 * (i * kSliceThreads + tid) + e));
+          ++pos;
+        }
+    }
+    if (tid == 0) ws.meta[slot] = make_uint2(fl, (uint32_t)min(run, kCandCap));
+  }
+  if (tid == 0) {
+    int32_t am = wave_i[0];
+    double m = 0.0;
+    for (int w = 0; w < kSliceWaves; ++w) {
+      am = min(am, wave_i[w]);
+      if (need_mass) m += wmass[w];
+    }
+    ws.recs[slot] = (uint64_t)kmax | ((uint64_t)(uint32_t)am << 32);
+    if (need_mass) ws.masses[slot] = m;
+  }
+}
+
+// fp32 finish kernel: one workgroup per row. Greedy rows take the argmax
+// from the slice records. Rows without a cut pick the slice holding the draw
+// by the slice masses and scan that slice in memory. Rows with a cut run the
+// generic cuts and draw over the candidate lists (tokens at or above the
+// largest list floor); when a cut falls outside them, over the row in memory.
+__global__ void __launch_bounds__(kFinishThreads) sample_finish32_kernel(SampleArgs a, SampleWs ws) {
+  using E = SampleElem<float>;
+  __shared__ SampleLds<kFinishWaves> s;
+  __shared__ int32_t sl_cnt[kMaxSlices];
+  __shared__ int32_t sl_beg[kMaxSlices];
+  __shared__ double sl_mass[kMaxSlices];
+  __shared__ uint32_t h_u[5];
+  __shared__ double h_f[2];
+  const int V = a.vocab, S = sample_slices(V);
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  SampleParams sp;
+  sp.load(a, row, V);
+  const bool plain = sp.plain();
+  const float c2 = sp.c2;
+  const float* lrow = reinterpret_cast<const float*>(a.logits) + (int64_t)row * a.row_stride;
+  const int64_t slot0 = (int64_t)row * S;
+
+  if (wave == 0) {  // slice records: lane l holds slices l and l + 64
+    const bool in0 = lane < S, in1 = lane + 64 < S;
+    const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull, r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
+    const uint32_t k0 = (uint32_t)r0, k1 = (uint32_t)r1;  // 0 for no slice: below every real key
+    const uint32_t mk = (uint32_t)wave_max_i32((int32_t)(max(k0, k1) ^ 0x80000000u)) ^ 0x80000000u;
+    const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
+                                        (in1 && k1 == mk) ? (int32_t)(r1 >> 32) : 0x7fffffff));
+    const int32_t argmax = am == 0x7fffffff ? 0 : am;  // slices are in index order
+    if (sp.greedy) {
+      if (lane == 0) a.out[row] = argmax;
+    } else {
+      const float lmax = E::key_value(mk);
+      double m0 = 0.0, m1 = 0.0, wall = 0.0;
+      if (sp.need_mass()) {
+        if (in0) m0 = ws.masses[slot0 + lane] * (double)fast_exp2((fmaxf(E::key_value(k0), -1e30f) - lmax) * c2);
+        if (in1) m1 = ws.masses[slot0 + lane + 64] * (double)fast_exp2((fmaxf(E::key_value(k1), -1e30f) - lmax) * c2);
+        wall = wave_sum_f64(m0 + m1);
+      }
+      uint32_t fl = 0;
+      if (plain) {
+        sl_mass[lane] = m0;
+        sl_mass[lane + 64] = m1;
+      } else {
+        const uint2 me0 = in0 ? ws.meta[slot0 + lane] : make_uint2(0u, 0u);
+        const uint2 me1 = in1 ? ws.meta[slot0 + lane + 64] : make_uint2(0u, 0u);
+        fl = (uint32_t)wave_max_i32((int32_t)(max(me0.x, me1.x) ^ 0x80000000u)) ^ 0x80000000u;
+        sl_cnt[lane] = (int32_t)me0.y;
+        sl_cnt[lane + 64] = (int32_t)me1.y;
+        // packed chunks: exclusive prefix of the lists' chunk counts, slices in order
+        const int32_t c0 = ((int32_t)me0.y + 1) / 2, c1 = ((int32_t)me1.y + 1) / 2;
+        const int32_t i0 = wave_incl_scan_i32(c0, lane);
+        const int32_t i1 = lane_i32(i0, 63) + wave_incl_scan_i32(c1, lane);
+        sl_beg[lane] = i0 - c0;
+        sl_beg[lane + 64] = i1 - c1;
+        if (lane == 0) h_u[4] = (uint32_t)lane_i32(i1, 63);
+      }
+      if (lane == 0) {
+        h_u[0] = mk;
+        h_u[1] = (uint32_t)argmax;
+        h_u[2] = fl;
+        h_f[0] = wall;
+      }
+    }
+  }
+  if (sp.greedy) return;
+  __syncthreads();
+  const float lmax = E::key_value(h_u[0]);
+  const int32_t argmax = (int32_t)h_u[1];
+  int32_t idx;
+  if (plain) {
+    if (wave == 0) {  // the slice holding the draw: running mass over the slices in index order
+      const double ms0 = lane < S ? sl_mass[lane] : 0.0, ms1 = lane + 64 < S ? sl_mass[lane + 64] : 0.0;
+      double ex0, ex1;
+      const double in_0 = wave_scan_f64(ms0, lane, &ex0);
+      const double t0 = lane_f64(in_0, 63);
+      const double in_1 = wave_scan_f64(ms1, lane, &ex1) + t0;
+      ex1 += t0;
+      const double target = (double)sp.u * lane_f64(in_1, 63);
+      const uint64_t b0 = __ballot(ms0 > 0.0 && ex0 <= target && target < in_0);
+      const uint64_t b1 = __ballot(ms1 > 0.0 && ex1 <= target && target < in_1);
+      int32_t psl;
+      double rem;
+      if (b0) {
+        const int l = __ffsll((unsigned long long)b0) - 1;
+        psl = l;
+        rem = target - lane_f64(ex0, l);
+      } else if (b1) {
+        const int l = __ffsll((unsigned long long)b1) - 1;
+        psl = 64 + l;
+        rem = target - lane_f64(ex1, l);
+      } else {  // rounding left the target past every slice: the last slice with mass
+        psl = max(wave_max_i32(max(ms0 > 0.0 ? lane : -1, ms1 > 0.0 ? lane + 64 : -1)), 0);
+        rem = INFINITY;
+      }
+      if (lane == 0) {
+        h_u[3] = (uint32_t)psl;
+        h_f[1] = rem;
+      }
+    }
+    __syncthreads();
+    const int psl = (int)h_u[3];
+    const double rem = h_f[1];
+    SampleRow<float, kFinishWaves> srow;
+    srow.init(lrow + (int64_t)psl * kSliceTokens, min(kSliceTokens, V - psl * kSliceTokens), wave, lane);
+    idx = find_crossing(srow, s, [&](int, float l) { return row_weight(l, lmax, c2); },
+                        [&](double) { return rem; });
+    if (idx >= 0) idx += psl * kSliceTokens;
+  } else {
+    const double wall = h_f[0];
+    CandRow<kFinishWaves> crow;
+    crow.init(ws.cands + slot0 * kCandCap, sl_beg, sl_cnt, S, (int)h_u[4], h_u[2], wave, lane);
+    bool covered;
+    const uint32_t fl = h_u[2];  // the largest logit below the lists' floor (none: -inf)
+    const float below = fl > 1u ? E::key_value(fl - 1u) : -INFINITY;
+    idx = sample_generic(crow, s, sp, lmax, &wall, &covered, below);
+    if (!covered) {
+      SampleRow<float, kFinishWaves> frow;
+      frow.init(lrow, V, wave, lane);
+      idx = sample_generic(frow, s, sp, lmax);
+    }
+  }
+  if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
 }
 
 }  // namespace pkv

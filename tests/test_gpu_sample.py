@@ -131,6 +131,9 @@ def test_sample_paths(name, V, T, k, p):
     u = rng.random(bs, dtype=np.float32)
     u[0], u[1] = 0.0, np.float32(0.99999994)
     _run(_bf16(x), "bf16", Ta, Ka, Pa, u, name, max_flag_frac=None)
+    # fp32 rows: candidate lists of at most 1024 tokens per slice; big-k, the
+    # flat and deep top-p cases and k9000 cut below them (the row in memory)
+    _run(x, "f32", Ta, Ka, Pa, u, name + "-f32", max_flag_frac=None)
 
 
 def test_sample_fp32_large_vocab_and_odd_sizes():
@@ -325,3 +328,21 @@ def test_min_p_closed_form():
     for dt, xx in (("bf16", _bf16(x)), ("f32", x)):
         got, _, flagged = _run(xx, dt, T, K, P, u, f"min_p-closed-form-{dt}", max_flag_frac=0.0, MP=MP)
         assert got.tolist() == want
+
+
+def test_fp32_candidate_lists_and_fallback_mix():
+    """fp32 rows of one batch, each with its own cut: some inside the slices'
+    candidate lists, some below them (top-k beyond the lists, a nucleus
+    larger than the lists, min_p alone with every listed token above it),
+    plain and greedy rows, on a vocabulary with a ragged last slice."""
+    V, bs = 50000, 40
+    rng = _rng("f32-mix")
+    x = (rng.standard_normal((bs, V)) * rng.choice([1.0, 3.0, 6.0], (bs, 1))).astype(np.float32)
+    x[5, 100:400] = 2.5                               # many equal logits at a top-k threshold
+    x[6, :] = np.round(x[6, :])                       # few distinct values: large tie groups
+    T = rng.choice([0.0, 0.6, 1.0, 2.0, 8.0], bs).astype(np.float32)
+    K = rng.choice([0, 1, 20, 300, 2000], bs).astype(np.int32)
+    P = rng.choice([1.0, 0.5, 0.9, 0.99], bs).astype(np.float32)
+    MP = rng.choice([0.0, 0.0, 0.001, 0.1], bs).astype(np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    _run(x, "f32", T, K, P, u, "f32-mix", max_flag_frac=None, MP=MP)
