@@ -371,6 +371,7 @@ template <typename T, int NW>
 struct SampleRow {
   using E = SampleElem<T>;
   static constexpr int EPC = E::kPerChunk;
+  static constexpr int kPerChunk = EPC;
   const T* base;
   int V, nchunks, cpw, rounds, wave, lane;
 
@@ -417,6 +418,13 @@ struct SampleRow {
 #pragma unroll
     for (int e = 0; e < EPC; ++e)
       if (i0 + e < V) f(i0 + e, E::value(x, e));
+  }
+  // g(e, valid, i, l) for every element slot e of chunk x of round c
+  template <class G>
+  PKV_INLINE void elements_all(int c, const u32x4& x, bool ok, G g) const {
+    const int i0 = chunk_id(c) * EPC;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) g(e, ok && i0 + e < V, i0 + e, E::value(x, e));
   }
   template <class F>
   PKV_INLINE void for_each(F f) const {
@@ -496,6 +504,14 @@ struct CandRow {
     for (int e = 0; e < kPerChunk; ++e) {
       const float l = __uint_as_float(x[2 * e]);
       if (E::key(l) >= floor) f((int)x[2 * e + 1], l);
+    }
+  }
+  template <class G>
+  PKV_INLINE void elements_all(int c, const u32x4& x, bool ok, G g) const {
+#pragma unroll
+    for (int e = 0; e < kPerChunk; ++e) {
+      const float l = __uint_as_float(x[2 * e]);
+      g(e, ok && E::key(l) >= floor, (int)x[2 * e + 1], l);
     }
   }
   template <class F>
@@ -629,12 +645,44 @@ PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds<NW>& s, PF pred, WF
       s.rmass[b] = 0.0;
     }
     __syncthreads();
-    row.for_each([&](int i, float l) {
-      const uint32_t key = E::key(l);
-      if ((key & mask) == prefix && pred(i, l)) {
-        const uint32_t dgt = (key >> shift) & 0xffu;
-        atomicAdd(&s.rcnt[dgt], 1u);
-        if (by_mass) atomicAdd(&s.rmass[dgt], (double)weight(l));
+    // Near the top of a ranking most tokens share the leading digits, and
+    // LDS atomics on one address serialise: a wave first adds each digit
+    // that at least 8 of its lanes hold as one combined update (up to two
+    // such digits per element slot), then the rest one by one.
+    row.for_rounds([&](int c, const u32x4& x, bool ok) {
+      constexpr int EPC = RowT::kPerChunk;
+      bool act[EPC];
+      uint32_t dg[EPC];
+      double wv[EPC];
+      row.elements_all(c, x, ok, [&](int e, bool valid, int i, float l) {
+        const uint32_t key = E::key(l);
+        act[e] = valid && (key & mask) == prefix && pred(i, l);
+        dg[e] = (key >> shift) & 0xffu;
+        wv[e] = (by_mass && act[e]) ? (double)weight(l) : 0.0;
+      });
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const uint64_t pend = __ballot(act[e]);
+          if (!pend) break;  // uniform
+          const int leader = __ffsll((unsigned long long)pend) - 1;
+          const uint32_t ld = (uint32_t)lane_i32((int32_t)dg[e], leader);
+          const bool mine = act[e] && dg[e] == ld;
+          const uint64_t m = __ballot(mine);
+          if (__popcll(m) < 8) break;  // uniform: few lanes share it
+          const double ms = by_mass ? wave_sum_f64(mine ? wv[e] : 0.0) : 0.0;
+          if (lane == leader) {
+            atomicAdd(&s.rcnt[ld], (uint32_t)__popcll(m));
+            if (by_mass) atomicAdd(&s.rmass[ld], ms);
+          }
+          act[e] = act[e] && !mine;
+        }
+        if (act[e]) {
+          atomicAdd(&s.rcnt[dg[e]], 1u);
+          if (by_mass) atomicAdd(&s.rmass[dg[e]], wv[e]);
+        }
       }
     });
     // bin b of the scan is digit 255 - b (descending keys)
