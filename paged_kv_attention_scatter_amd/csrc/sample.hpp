@@ -1466,7 +1466,7 @@ constexpr int kSlice32Rounds = kSliceTokens / (4 * kSliceThreads);  // 8 chunks 
 __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArgs a, SampleWs ws) {
   using E = SampleElem<float>;
   constexpr int R = kSlice32Rounds;
-  __shared__ uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
+  __shared__ uint32_t hist[kHistBins];
   __shared__ double wmass[kSliceWaves];
   __shared__ uint32_t wave_k[kSliceWaves];
   __shared__ int32_t wave_i[kSliceWaves];
@@ -1489,12 +1489,24 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
   for (int i = 0; i < R; ++i)  // indices clamped to the row's last chunk: reads stay in the row
     raw[i] = __builtin_nontemporal_load(crow + min(t0s / 4 + i * kSliceThreads + tid, last_chunk));
   if (need_list)  // ordered before the atomics by the barrier of the block maximum
-    for (int b = tid; b < kHistBins + kWave; b += kSliceThreads) hist[b] = 0;
-  // key of token e of chunk round i; 0 (below every real key) at or past V
-  auto key = [&](int i, int e) -> uint32_t {
-    const uint32_t k = E::key(__uint_as_float(raw[i][e]));
-    return (tail && t0s + 4 * (i * kSliceThreads + tid) + e >= V) ? 0u : k;
-  };
+    for (int b = tid; b < kHistBins; b += kSliceThreads) hist[b] = 0;
+  // the tokens become their keys in place (0, below every real key, at or
+  // past V); a key gives its logit back (-0 as +0, which weighs the same)
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = E::key(__uint_as_float(raw[i][e]));
+        raw[i][e] = t0s + 4 * (i * kSliceThreads + tid) + e >= V ? 0u : k;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[i][e] = E::key(__uint_as_float(raw[i][e]));
+  }
+  auto key = [&](int i, int e) -> uint32_t { return raw[i][e]; };
   uint32_t tk = 0;
 #pragma unroll
   for (int i = 0; i < R; ++i)
@@ -1508,7 +1520,7 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
       float cs = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float w = fast_exp2(fmaf(__uint_as_float(raw[i][e]), c2, off));
+        const float w = fast_exp2(fmaf(E::key_value(key(i, e)), c2, off));
         cs += key(i, e) ? w : 0.f;
       }
       mass += (double)cs;
@@ -1538,13 +1550,13 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
   found = wave_min_i32(found);
   if (lane == 0) wave_i[wave] = found;
   const uint32_t cmax = kmax >> 16;
-  if (need_list) {  // bin d = cmax - (key >> 16); a token outside the window, or none, to a discard bin
+  if (need_list) {  // bin d = cmax - (key >> 16); most tokens lie below the window and add nothing
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t k = key(i, e), d = cmax - (k >> 16);
-        atomicAdd(&hist[(k != 0u && d < (uint32_t)kHistBins) ? d : (uint32_t)(kHistBins + lane)], 1u);
+        if (k != 0u && d < (uint32_t)kHistBins) atomicAdd(&hist[d], 1u);
       }
   }
   __syncthreads();
@@ -1618,7 +1630,9 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (key(i, e) >= fl) {
-          if (pos < kCandCap) list[pos] = make_uint2(raw[i][e], (uint32_t)(t0s + 4 * (i * kSliceThreads + tid) + e));
+          if (pos < kCandCap)
+            list[pos] = make_uint2(__float_as_uint(E::key_value(key(i, e))),
+                                   (uint32_t)(t0s + 4 * (i * kSliceThreads + tid) + e));
           ++pos;
         }
     }
