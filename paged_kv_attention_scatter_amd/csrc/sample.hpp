@@ -103,7 +103,7 @@ struct SampleElem<float> {
   }
 };
 
-constexpr int kSampleMaxRounds = 512;   // memory passes: chunk rounds per wave with a group-mass slot
+constexpr int kSampleMaxRounds = 256;   // memory passes: chunk rounds per wave with a group-mass slot
 
 // ---------------------------------------------------------------- wave helpers
 
@@ -520,6 +520,56 @@ struct CandRow {
   }
 };
 
+// fp32 rows: candidates packed in LDS (logit bits, vocabulary index), in
+// index order; two entries per 16-byte chunk.
+constexpr int kLdsCands = 4096;
+template <int NW>
+struct LdsRow {
+  using E = SampleElem<float>;
+  static constexpr int kPerChunk = 2;
+  const uint2* ents;
+  int n, nchunks, cpw, rounds, wave, lane;
+
+  PKV_INLINE void init(const uint2* e, int count, int w, int l) {
+    ents = e;
+    n = count;
+    nchunks = (count + kPerChunk - 1) / kPerChunk;
+    cpw = (nchunks + NW - 1) / NW;
+    rounds = (cpw + kWave - 1) / kWave;
+    wave = w;
+    lane = l;
+  }
+  PKV_INLINE int chunk_id(int c) const { return wave * cpw + c * kWave + lane; }
+  PKV_INLINE bool chunk_ok(int c) const { return c * kWave + lane < cpw && chunk_id(c) < nchunks; }
+  PKV_INLINE u32x4 fetch(int c) const {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (chunk_ok(c)) x = *reinterpret_cast<const u32x4*>(ents + kPerChunk * chunk_id(c));
+    return x;
+  }
+  template <class F>
+  PKV_INLINE void for_rounds(F f) const {
+    for (int c = 0; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
+  }
+  template <class F>
+  PKV_INLINE void elements(int c, const u32x4& x, bool ok, F f) const {
+    if (!ok) return;
+    const int j = kPerChunk * chunk_id(c);
+#pragma unroll
+    for (int e = 0; e < kPerChunk; ++e)
+      if (j + e < n) f((int)x[2 * e + 1], __uint_as_float(x[2 * e]));
+  }
+  template <class G>
+  PKV_INLINE void elements_all(int c, const u32x4& x, bool ok, G g) const {
+    const int j = kPerChunk * chunk_id(c);
+#pragma unroll
+    for (int e = 0; e < kPerChunk; ++e) g(e, ok && j + e < n, (int)x[2 * e + 1], __uint_as_float(x[2 * e]));
+  }
+  template <class F>
+  PKV_INLINE void for_each(F f) const {
+    for_rounds([&](int c, const u32x4& x, bool ok) { elements(c, x, ok, f); });
+  }
+};
+
 // w(l) = exp2((l - l_max) * c2)
 PKV_INLINE float row_weight(float l, float lmax, float c2) { return fast_exp2((l - lmax) * c2); }
 
@@ -749,6 +799,49 @@ struct SampleParams {
   // a cut is needed
   PKV_INLINE bool need_cut() const { return !greedy && (use_k || use_p || use_mp); }
 };
+
+// Copies the elements of `row` into out[] in index order when there are at
+// most cap of them; returns their count, or -1 (nothing written) if more.
+// Group counts per (wave, round) go through s.gsum (exact in fp32), an
+// exclusive scan over the groups in order gives each group's start, and a
+// second pass writes. Block-uniform; all threads call it.
+template <class RowT, int NW>
+PKV_INLINE int compact_row(const RowT& row, SampleLds<NW>& s, uint2* out, int cap) {
+  const int wave = row.wave, lane = row.lane, R = row.rounds;
+  __syncthreads();
+  row.for_rounds([&](int c, const u32x4& x, bool ok) {
+    int m = 0;
+    row.elements(c, x, ok, [&](int, float) { ++m; });
+    const int t = wave_sum_i32(m);
+    if (lane == 0) s.gsum[wave * R + c] = (float)t;
+  });
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefix over the groups in index order; each lane a contiguous run
+    const int G = NW * R, per = (G + kWave - 1) / kWave;
+    const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
+    int own = 0;
+    for (int g = g0; g < g1; ++g) own += (int)s.gsum[g];
+    const int incl = wave_incl_scan_i32(own, lane);
+    int run = incl - own;
+    for (int g = g0; g < g1; ++g) {
+      const int v = (int)s.gsum[g];
+      s.gsum[g] = (float)run;
+      run += v;
+    }
+    if (lane == 63) s.pick_cnt = (uint32_t)incl;
+  }
+  __syncthreads();
+  const int total = (int)s.pick_cnt;
+  if (total > cap) return -1;
+  row.for_rounds([&](int c, const u32x4& x, bool ok) {
+    int m = 0;
+    row.elements(c, x, ok, [&](int, float) { ++m; });
+    int pos = (int)s.gsum[wave * R + c] + wave_incl_scan_i32(m, lane) - m;
+    row.elements(c, x, ok, [&](int i, float l) { out[pos++] = make_uint2(__float_as_uint(l), (uint32_t)i); });
+  });
+  __syncthreads();
+  return total;
+}
 
 // Cuts and draw over the row in memory (any cut depth, any number of kept
 // tokens): radix descents for the top-k threshold and the top-p cut,
@@ -1658,6 +1751,7 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
 __global__ void __launch_bounds__(kFinishThreads) sample_finish32_kernel(SampleArgs a, SampleWs ws) {
   using E = SampleElem<float>;
   __shared__ SampleLds<kFinishWaves> s;
+  __shared__ __align__(16) uint2 lcands[kLdsCands];
   __shared__ int32_t sl_cnt[kMaxSlices];
   __shared__ int32_t sl_beg[kMaxSlices];
   __shared__ double sl_mass[kMaxSlices];
@@ -1767,7 +1861,17 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish32_kernel(SampleA
     bool covered;
     const uint32_t fl = h_u[2];  // the largest logit below the lists' floor (none: -inf)
     const float below = fl > 1u ? E::key_value(fl - 1u) : -INFINITY;
-    idx = sample_generic(crow, s, sp, lmax, &wall, &covered, below);
+    // the candidates into LDS when they fit (every later pass then reads
+    // LDS); not tried when the lists are far longer than LDS holds (full
+    // lists, as for top-p over the whole row, keep nearly every entry)
+    const int nl = 2 * (int)h_u[4] <= 4 * kLdsCands ? compact_row(crow, s, lcands, kLdsCands) : -1;
+    if (nl >= 0) {
+      LdsRow<kFinishWaves> lrow;
+      lrow.init(lcands, nl, wave, lane);
+      idx = sample_generic(lrow, s, sp, lmax, &wall, &covered, below);
+    } else {
+      idx = sample_generic(crow, s, sp, lmax, &wall, &covered, below);
+    }
     if (!covered) {
       SampleRow<float, kFinishWaves> frow;
       frow.init(lrow, V, wave, lane);
