@@ -36,11 +36,20 @@
 //   those masses and scans its 8192 tokens. Cuts below the window take the
 //   generic path below over the row in memory.
 //
-// fp32 rows (the memory kernel) and the generic path: every
-// pass reads 16-byte chunks from memory (wave w owns a contiguous chunk range,
-// lane l reads chunk w * CPW + 64c + l in round c). Cuts by radix descent over
-// the full key (8 bits per pass, count and fp64 mass histograms); ties and the
-// draw by per-(wave, round) group masses that locate one chunk round.
+// fp32 rows (slice kernel + finish kernel): the slices are the same 8192
+// tokens with 32-bit keys. A slice hands over its maximum, its mass and, for
+// rows with a cut, a candidate list: every token of the slice at or above a
+// floor picked from a histogram of the keys' upper 16 bits (the bins of an
+// fp32 row do not share one weight, so the cuts are not taken from counts).
+// The finish kernel runs the generic cuts and draw over the lists, which
+// hold exactly the row's tokens at or above the largest floor; when a cut
+// lies below them, over the row in memory.
+//
+// The generic path: every pass reads 16-byte chunks (wave w owns a
+// contiguous chunk range, lane l reads chunk w * CPW + 64c + l in round c).
+// Cuts by radix descent over the full key (8 bits per pass, count and fp64
+// mass histograms); ties and the draw by per-(wave, round) group masses that
+// locate one chunk round.
 //
 // Mass sums are fp32 over at most 8 tokens (a 16-byte chunk, or one round of
 // a thread) or one wave's group, and fp64 above.
