@@ -346,3 +346,20 @@ def test_fp32_candidate_lists_and_fallback_mix():
     MP = rng.choice([0.0, 0.0, 0.001, 0.1], bs).astype(np.float32)
     u = rng.random(bs, dtype=np.float32)
     _run(x, "f32", T, K, P, u, "f32-mix", max_flag_frac=None, MP=MP)
+
+
+def test_largest_fp32_vocabulary():
+    """fp32 rows at the 2^20-token limit: 128 slices, so the finish kernel's
+    two slices per lane and the lists' binary search reach their last slice;
+    top-k, top-k + top-p, min_p, top-p alone and plain rows."""
+    V, bs = 1 << 20, 5
+    rng = _rng("max-vocab-f32")
+    x = (rng.standard_normal((bs, V)) * 3).astype(np.float32)
+    x[1, V - 3] = 40.0                                # the maximum in the last slice
+    T = np.array([0.7, 1.0, 1.0, 0.8, 1.0], np.float32)
+    K = np.array([50, 30, 0, 0, 0], np.int32)
+    P = np.array([1.0, 0.95, 1.0, 0.9, 1.0], np.float32)
+    MP = np.array([0.0, 0.0, 0.05, 0.0, 0.0], np.float32)
+    u = rng.random(bs, dtype=np.float32)
+    got, _, _ = _run(x, "f32", T, K, P, u, "max-vocab-f32", max_flag_frac=None, MP=MP)
+    assert got[1] == V - 3                            # e^(40 - ~15) dwarfs the rest
