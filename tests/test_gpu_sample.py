@@ -191,6 +191,7 @@ def test_vocab_boundaries_and_masked_tokens(V):
     x[0, -1] = 50.0
     x[1, -2:] = 50.0
     x[2:5, ::3] = -np.inf
+    x[6, :V // 2] = -np.inf                             # whole slices masked
     T = np.array([0.0, 0.0, 0.8, 1.0, 0.5, 0.9, 0.9, 1.2], np.float32)
     K = np.array([0, 0, 0, 40, 5, 30, 0, 0], np.int32)
     P = np.array([1.0, 1.0, 0.9, 1.0, 0.5, 0.9, 0.95, 1.0], np.float32)
@@ -203,6 +204,15 @@ def test_vocab_boundaries_and_masked_tokens(V):
     want, flagged = oracle.sample(oracle.widen(xb, "bf16")[:, :V], T, K, P, u)
     bad = np.nonzero((got != want) & ~flagged)[0]
     assert bad.size == 0, (V, bad.tolist(), got[bad].tolist(), want[bad].tolist())
+    assert got[0] == V - 1 and got[1] == V - 2
+    xf = np.pad(x, ((0, 0), (0, (-V) % 4)))             # fp32 rows padded to 16 bytes
+    print(f"sample case edge-V{V} fp32", flush=True)
+    tok = pkv.sample(to_dev(xf)[:, :V], to_dev(T), to_dev(K), to_dev(P), to_dev(u))
+    torch.cuda.synchronize()
+    got = to_host(tok)
+    want, flagged = oracle.sample(xf[:, :V].astype(np.float64), T, K, P, u)
+    bad = np.nonzero((got != want) & ~flagged)[0]
+    assert bad.size == 0, (V, "fp32", bad.tolist(), got[bad].tolist(), want[bad].tolist())
     assert got[0] == V - 1 and got[1] == V - 2
 
 
