@@ -480,31 +480,45 @@ struct CandRow {
   }
   PKV_INLINE int chunk_id(int c) const { return wave * cpw + c * kWave + lane; }
   PKV_INLINE bool chunk_ok(int c) const { return c * kWave + lane < cpw && chunk_id(c) < nchunks; }
-  PKV_INLINE u32x4 fetch(int c) const {
+  // the slice holding chunk q: the last with beg <= q
+  PKV_INLINE int locate(int q) const {
+    int sl = 0;
+#pragma unroll
+    for (int step = kMaxSlicesPow2 / 2; step > 0; step >>= 1)
+      if (sl + step < slices && beg[sl + step] <= q) sl += step;
+    return sl;
+  }
+  // chunk c, its slice sl found from a slice at or before it
+  PKV_INLINE u32x4 fetch_from(int c, int& sl) const {
     u32x4 x = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (chunk_ok(c)) {
       const int q = chunk_id(c);
-      int sl = 0;
-#pragma unroll
-      for (int step = kMaxSlicesPow2 / 2; step > 0; step >>= 1)
-        if (sl + step < slices && beg[sl + step] <= q) sl += step;
+      while (sl + 1 < slices && beg[sl + 1] <= q) ++sl;
       const int j = kPerChunk * (q - beg[sl]);
       x = *reinterpret_cast<const u32x4*>(lists + (int64_t)sl * kCandCap + j);
       if (j + 1 >= cnt[sl]) x[2] = 0xffffffffu;
     }
     return x;
   }
+  PKV_INLINE u32x4 fetch(int c) const {
+    int sl = chunk_ok(c) ? locate(chunk_id(c)) : 0;
+    return fetch_from(c, sl);
+  }
+  // a lane's chunks rise with the round, so its slice is carried forward
+  // (one binary search per pass, then a step or two per round)
   template <class F>
   PKV_INLINE void for_rounds(F f) const {
+    int sl = chunk_ok(0) ? locate(chunk_id(0)) : 0;
     int c = 0;
     for (; c + 4 <= rounds; c += 4) {
-      const u32x4 x0 = fetch(c), x1 = fetch(c + 1), x2 = fetch(c + 2), x3 = fetch(c + 3);
+      const u32x4 x0 = fetch_from(c, sl), x1 = fetch_from(c + 1, sl), x2 = fetch_from(c + 2, sl),
+                  x3 = fetch_from(c + 3, sl);
       f(c, x0, chunk_ok(c));
       f(c + 1, x1, chunk_ok(c + 1));
       f(c + 2, x2, chunk_ok(c + 2));
       f(c + 3, x3, chunk_ok(c + 3));
     }
-    for (; c < rounds; ++c) f(c, fetch(c), chunk_ok(c));
+    for (; c < rounds; ++c) f(c, fetch_from(c, sl), chunk_ok(c));
   }
   template <class F>
   PKV_INLINE void elements(int c, const u32x4& x, bool ok, F f) const {
