@@ -346,7 +346,7 @@ PKV_INLINE double block_scan_f64(SampleLds<NW>& s, double v, double* incl_out, d
 // reaches `goal` (-1 if none), the amount strictly before it and count(bin).
 template <int NW, class AF, class CF>
 PKV_INLINE void window_select(SampleLds<NW>& s, AF amount, CF count, double goal, int* bin, double* before,
-                              uint32_t* cnt) {
+                              uint32_t* cnt, double* total = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __syncthreads();
   if (tid == 0) s.pick_bin = -1;
@@ -357,6 +357,7 @@ PKV_INLINE void window_select(SampleLds<NW>& s, AF amount, CF count, double goal
     if (lane == 63) s.scan_f[wave] = incl;
   }
   __syncthreads();
+  if (total) *total = (s.scan_f[0] + s.scan_f[1]) + (s.scan_f[2] + s.scan_f[3]);  // all 256 bins
   if (wave < 4) {
     double off = 0.0;
     for (int w = 0; w < wave; ++w) off += s.scan_f[w];
@@ -706,7 +707,7 @@ PKV_INLINE int32_t find_crossing(const RowT& row, SampleLds<NW>& s, VF v, TF tar
 // *eq = the group's count.
 template <class RowT, int NW, class PF, class WF>
 PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds<NW>& s, PF pred, WF weight, bool by_mass, double goal,
-                                  double* above_out, uint32_t* eq_out) {
+                                  double* above_out, uint32_t* eq_out, double* total_out = nullptr) {
   using E = typename RowT::E;
   uint32_t prefix = 0, mask = 0;
   double above = 0.0;
@@ -764,7 +765,8 @@ PKV_INLINE uint32_t radix_descend(const RowT& row, SampleLds<NW>& s, PF pred, WF
     uint32_t cnt;
     window_select(
         s, [&](int b) { return by_mass ? s.rmass[255 - b] : (double)s.rcnt[255 - b]; },
-        [&](int b) { return s.rcnt[255 - b]; }, goal - above, &bin, &before, &cnt);
+        [&](int b) { return s.rcnt[255 - b]; }, goal - above, &bin, &before, &cnt,
+        shift == E::kKeyBits - 8 ? total_out : nullptr);  // the first digit's bins hold everything
     if (bin < 0) {  // rounding: goal beyond everything -> the lowest non-empty digit
       if (threadIdx.x == 0) {
         int lo = -1;
@@ -887,10 +889,6 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
   auto wt = [&](float l) { return row_weight(l, lmax, c2); };
   if (covered) {
     *covered = true;
-    if (sp.use_k && row_sum(row, s, [](int, float) { return 1.f; }) < (double)sp.k) {
-      *covered = false;
-      return -1;
-    }
     // min_p alone: covered when every token below the part weighs below
     // min_p (below_max: the largest logit below it), or one of its own does
     if (sp.use_mp && !sp.use_k && !sp.use_p && !(wt(below_max) < sp.mp) &&
@@ -904,9 +902,13 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
   uint32_t kk_key = 0, kk_eq = 0, kk_take = 0;
   int32_t kk_last = 0x7fffffff;
   if (sp.use_k) {
-    double ab;
+    double ab, n_all;
     kk_key = radix_descend(row, s, [](int, float) { return true; }, [](float) { return 0.f; }, false,
-                           (double)sp.k, &ab, &kk_eq);
+                           (double)sp.k, &ab, &kk_eq, &n_all);
+    if (covered && n_all < (double)sp.k) {  // fewer than k tokens: the threshold lies below them
+      *covered = false;
+      return -1;
+    }
     kk_take = (uint32_t)sp.k - (uint32_t)ab;
     if (kk_take < kk_eq) {
       const double goal = (double)kk_take - 0.5;
@@ -924,20 +926,17 @@ PKV_INLINE int32_t sample_generic(const RowT& row, SampleLds<NW>& s, const Sampl
   uint32_t kp_key = 0;
   int32_t kp_last = 0x7fffffff;
   if (sp.use_p) {
-    double Wk;
-    if (covered && !sp.use_k) {  // top-p over the whole row: its mass, and the part must reach the target
-      Wk = *w_row;
-      if (row_sum(row, s, [&](int, float l) { return wt(l); }) < (double)sp.p * Wk) {
-        *covered = false;
-        return -1;
-      }
-    } else {
-      Wk = row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
-    }
+    // top-p over the whole row (a part of it given): the whole row's mass
+    const bool whole = covered && !sp.use_k;
+    const double Wk = whole ? *w_row : row_sum(row, s, [&](int i, float l) { return kept_k(i, l) ? wt(l) : 0.f; });
     const double target = (double)sp.p * Wk;
-    double above;
+    double above, m_all;
     uint32_t n_at;
-    kp_key = radix_descend(row, s, kept_k, wt, true, target, &above, &n_at);
+    kp_key = radix_descend(row, s, kept_k, wt, true, target, &above, &n_at, &m_all);
+    if (whole && m_all < target) {  // the part's mass falls short: the cut lies below it
+      *covered = false;
+      return -1;
+    }
     // equal-key tokens at the cut: token j of the group (0-based) is kept iff above + j * w < target
     const double w = (double)wt(E::key_value(kp_key));
     double need = ceil((target - above) / w);
