@@ -448,17 +448,16 @@ def bench_sampler_variants(torch, pkv, gen, dev, args):
 
 def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
     """A decode step (store_kv, decode attention, sampler) of the first bs
-    requests of the 256-request batch, bs = 1, 8 and 64, over layer 0 of the
-    pool: issued eagerly through the Python binding, and replayed from a HIP
-    graph captured once (torch.cuda.CUDAGraph over the same calls). Small
-    steps are bound by the host's launch rate; the replay is not."""
+    requests of the 256-request batch, bs = 1, 8, 64 and 256, over layer 0
+    of the pool: issued eagerly through the Python binding, and replayed from
+    a HIP graph captured once (torch.cuda.CUDAGraph over the same calls)."""
     from workloads import HEAD_DIM, HKV, HQ, config, draw_sampling_params
     V = config(3).vocab
     rows = draw_sampling_params(config(3))
     T_all, K_all, P_all = pkv.prepare_sampling(*zip(*rows), vocab=V)
     kp, vp = pool[0, 0], pool[1, 0]
     out = {}
-    for bs in (1, 8, 64):
+    for bs in (1, 8, 64, 256):
         s_q = q[:bs].clone()
         s_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
         s_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
