@@ -984,6 +984,9 @@ constexpr int kDrawChunks = kSliceTokens / (8 * kFinishThreads);  // 1: 8 tokens
 __host__ __device__ inline int sample_slices(int V) { return (V + kSliceTokens - 1) / kSliceTokens; }
 static_assert((int64_t)kMaxSlices * kSliceTokens <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves * 4,
               "the generic path covers every row the slices cover (fp32: four tokens per chunk)");
+static_assert((int64_t)kMaxSlices * kCandCap / 2 <= (int64_t)kSampleMaxRounds * kWave * kFinishWaves &&
+                  kLdsCands / 2 <= kSampleMaxRounds * kWave * kFinishWaves,
+              "candidate passes fit the group table (two entries per chunk)");
 static_assert(kMaxSlices <= kFinishThreads, "one slice per finishing thread");
 static_assert(kMaxSlices <= kMaxSlicesPow2 && kMaxSlices <= 2 * kWave, "slices of a row: two per lane, binary search");
 
