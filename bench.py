@@ -1,6 +1,6 @@
 """Benchmark of the paged-KV hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 3|2|5] [--skip-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 3|2] [--skip-cpu]
 
 A step is one decode step of the whole path over one synthetic batch, on the
 current HIP stream: store_kv of the batch's new K/V rows, decode attention
@@ -112,6 +112,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
+    cpu_pools = None if args.skip_cpu else CpuPools()  # before anything touches the GPU
     import torch
     import paged_kv_attention_scatter_amd as pkv
     from workloads import (HEAD_DIM, HKV, HQ, LAYERS, config, draw_lengths, draw_logits, draw_page_table,
@@ -245,6 +246,8 @@ def main():
         },
     }
 
+    if args.config == 3:
+        result["components"].update(bench_decode64(torch, pkv, pool, num_pages, gen, dev, args))
     if not args.skip_extend:
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
     if not args.skip_components:
@@ -253,14 +256,86 @@ def main():
         result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
         result["components"].update(bench_sampler_variants(torch, pkv, gen, dev, args))
 
-    if not args.skip_cpu:
-        result["cpu_baseline"] = cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg)
+    if cpu_pools is not None:
+        result["cpu_baseline"] = cpu_baseline(cpu_pools)
+        cpu_pools.close()
     if not args.skip_mixed:
         del pool, kp, vp, logit_bufs, step
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         result["components"].update(bench_mixed(torch, pkv, dev, args))
     print(json.dumps(result), flush=True)
+
+
+def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
+    """The 64-request decode batch (device_len ~ U[256, 2048], bf16, page_size
+    1, same 28-layer pool) with an all-greedy sampler (no temperature array:
+    the argmax path) over [64, 151936] logits: store_kv, decode attention and
+    argmax timed apart with HIP events on the launch stream, and as one step.
+    Rotates over the filled layers and four logits buffers."""
+    from workloads import (HEAD_DIM, HKV, HQ, config, draw_lengths, draw_logits, draw_page_table, draw_q,
+                           draw_sampling_params)
+    cfg = config(2)
+    C, S = draw_lengths(cfg)
+    bs = len(S)
+    table = draw_page_table(cfg, S, num_pages)
+    q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
+    d_table = torch.from_numpy(table).to(dev)
+    d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
+    d_loc = torch.from_numpy(table[np.arange(bs), S - 1].astype(np.int32)).to(dev)
+    new_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+    new_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+    total_kv = int(S.sum())
+    ws = torch.empty(pkv.decode_workspace_size(bs, HQ, total_kv), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    T, K, P = pkv.prepare_sampling(*zip(*draw_sampling_params(cfg)), vocab=cfg.vocab)
+    assert T is None  # all greedy: the argmax path
+    bufs = [torch.from_numpy(draw_logits(cfg).view(np.int16)).to(dev).view(torch.bfloat16)]
+    for _ in range(3):
+        bufs.append((torch.randn((bs, cfg.vocab), generator=gen, device=dev) * cfg.logit_sigma).to(torch.bfloat16))
+    tokens = torch.empty(bs, dtype=torch.int32, device=dev)
+    s_ws = pkv.sample_workspace(bs, cfg.vocab, dev)
+    ops = [lambda i: pkv.store_kv(pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_loc, new_k, new_v),
+           lambda i: pkv.paged_attention_decode(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_table,
+                                                d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws),
+           lambda i: pkv.sample(bufs[i % len(bufs)], None, None, None, None, out=tokens, workspace=s_ws)]
+    for i in range(5):
+        for op in ops:
+            op(i)
+    torch.cuda.synchronize()
+    n = max(20, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    for i in range(n):
+        for j, op in enumerate(ops):
+            ev[i][j].record()
+            op(i)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(n)])
+    st_us, dec_us, am_us = (float(np.mean(ms[:, j])) * 1e3 for j in range(3))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        for op in ops:
+            op(i)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / n * 1e3
+    kv = total_kv * HKV * HEAD_DIM * 2 * 2
+    lg = bs * cfg.vocab * 2
+    log(f"decode64: store {st_us:.1f} us | decode {dec_us:.1f} us ({kv / dec_us / 1e3:.0f} GB/s) | "
+        f"argmax {am_us:.1f} us ({lg / am_us / 1e3:.0f} GB/s) | step {step_us:.1f} us")
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the decode64 timing")
+    return {"decode64_workload": f"bs=64, device_len {int(S.min())}..{int(S.max())}, sum {total_kv}, "
+                                 f"page_size 1, all greedy (argmax) over [64, {cfg.vocab}] bf16",
+            "decode64_store_us": round(st_us, 2), "decode64_decode_us": round(dec_us, 2),
+            "decode64_decode_kv_gbs": round(kv / dec_us / 1e3, 1),
+            "decode64_decode_frac_hbm": round(kv / dec_us / 1e3 / HBM_PEAK_GBS, 4),
+            "decode64_argmax_us": round(am_us, 2), "decode64_argmax_gbs": round(lg / am_us / 1e3, 1),
+            "decode64_argmax_frac_hbm": round(lg / am_us / 1e3 / HBM_PEAK_GBS, 4),
+            "decode64_argmax_tokens_per_s": round(bs / (am_us * 1e-6), 1),
+            "decode64_step_us": round(step_us, 2)}
 
 
 def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
@@ -611,31 +686,169 @@ def bench_mixed(torch, pkv, dev, args):
             "mixed242_step_us": round(step_us, 2)}
 
 
-def cpu_baseline(torch, pool, table, C, S, q, logits0, T, K, P, cfg):
-    """The oracle, as it stands, on the GPU machine's host cores: decode attention
-    for as many requests as fit in ~10 s of CPU time (their K/V rows copied
-    from layer 0 of the pool), reported as KV GB/s like the GPU figure."""
+# ---------------------------------------------------------------- CPU baseline (the oracle on the host cores)
+#
+# Worker processes are started with the "spawn" method before the GPU is
+# initialised and import only NumPy, the seeded generators and the oracle.
+# Each worker draws its share of the inputs with the workloads generators
+# (untimed), waits at a barrier, then runs the oracle on them; the time is
+# from the first worker's start to the last worker's end.
+
+_CPU_BARRIER = None
+
+
+def _cpu_worker_init(barrier, cpu):
+    global _CPU_BARRIER
+    _CPU_BARRIER = barrier
+    if cpu is not None:
+        os.sched_setaffinity(0, {cpu.get()})
+
+
+def _cpu_worker_task(job):
     import oracle
-    k0 = pool[0, 0]
-    v0 = pool[1, 0]
-    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
-    done, kv_bytes, elapsed = 0, 0, 0.0
-    budget = 10.0
-    while done < len(S) and elapsed < budget:
-        r = done
-        s = int(S[r])
-        slots = torch.from_numpy(table[r, :s].astype(np.int64)).to(k0.device)
-        K = k0.index_select(0, slots).view(torch.int16).cpu().numpy().view(np.uint16)
-        V = v0.index_select(0, slots).view(torch.int16).cpu().numpy().view(np.uint16)
-        tab = np.arange(s, dtype=np.int64)[None, :]
+    from workloads import config, draw_logits, draw_lengths, draw_q, draw_request_kv, draw_sampling_params, \
+        draw_uniforms, f32_to_bf16_bits
+    kind, items = job
+    if kind == "decode":  # items: request ids of the 256-request decode batch
+        cfg = config(3)
+        C, S = draw_lengths(cfg)
+        q = draw_q(cfg, C, S)
+        data = []
+        for r in items:
+            K, V = draw_request_kv(cfg, r, int(S[r]))
+            data.append((r, f32_to_bf16_bits(K), f32_to_bf16_bits(V)))
+        _CPU_BARRIER.wait(timeout=300)
         t0 = time.perf_counter()
-        oracle.attention_decode(qh[r:r + 1], K, V, tab, C[r:r + 1], S[r:r + 1], "bf16")
-        elapsed += time.perf_counter() - t0
-        kv_bytes += s * 8 * 128 * 2 * 2
-        done += 1
-    return {"value": round(kv_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"decode attention of the first {done} of {len(S)} requests (fp64 NumPy, one thread, "
-                      f"{elapsed:.1f} s)", "host_cpus_available": len(os.sched_getaffinity(0))}
+        nbytes = 0
+        for r, K, V in data:
+            tab = np.arange(int(S[r]), dtype=np.int64)[None, :]
+            oracle.attention_decode(q[r:r + 1], K, V, tab, C[r:r + 1], S[r:r + 1], "bf16")
+            nbytes += int(S[r]) * 8 * 128 * 2 * 2
+        return t0, time.perf_counter(), nbytes
+    if kind == "extend":  # items: (request, t0, t1) query-row spans of the 8-request prefill
+        cfg = config(4)
+        C, S = draw_lengths(cfg)
+        q = draw_q(cfg, C, S)
+        cu = np.concatenate([[0], np.cumsum(S - C)])
+        data = []
+        for r, a, b in items:
+            K, V = draw_request_kv(cfg, r, int(S[r]))
+            n = int(C[r]) + b
+            data.append((r, a, b, f32_to_bf16_bits(K[:n]), f32_to_bf16_bits(V[:n])))
+        _CPU_BARRIER.wait(timeout=300)
+        t0 = time.perf_counter()
+        flops = 0.0
+        for r, a, b, K, V in data:
+            c = int(C[r])
+            tab = np.arange(c + b, dtype=np.int64)[None, :]
+            oracle.attention_extend(q[cu[r] + a:cu[r] + b], K, V, tab, np.array([c + a], np.int32),
+                                    np.array([c + b], np.int32), "bf16")
+            flops += 4.0 * 128 * 16 * float(sum(c + t + 1 for t in range(a, b)))
+        return t0, time.perf_counter(), flops
+    if kind == "sample":  # items: row ids of the 256-row mixed sampler batch
+        cfg = config(3)
+        lf = oracle.widen(draw_logits(cfg)[list(items)], "bf16")
+        T, K, P = oracle.prepare([oracle.SamplingParams(*p) for p in draw_sampling_params(cfg)], cfg.vocab)
+        u = draw_uniforms(cfg)
+        sel = lambda x: None if x is None else x[list(items)]
+        _CPU_BARRIER.wait(timeout=300)
+        t0 = time.perf_counter()
+        oracle.sample(lf, sel(T), sel(K), sel(P), sel(u))
+        return t0, time.perf_counter(), len(items)
+    raise ValueError(kind)
+
+
+def host_cpus():
+    """(logical CPUs this process may use, one logical CPU per physical core
+    among them, CPU model name)."""
+    cpus = sorted(os.sched_getaffinity(0))
+    cores = {}
+    for c in cpus:
+        try:
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/core_id") as f:
+                core = f.read().strip()
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/physical_package_id") as f:
+                pkg = f.read().strip()
+        except OSError:
+            core, pkg = str(c), "0"
+        cores.setdefault((pkg, core), c)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cpus, sorted(cores.values()), model
+
+
+class CpuPools:
+    """Two oracle pools: every logical CPU of this process's share (at most
+    16, the host share of one GPU), and one logical CPU per physical core.
+    Created before the GPU is initialised."""
+
+    def __init__(self):
+        import multiprocessing as mp
+        self.ctx = mp.get_context("spawn")
+        cpus, phys, self.model = host_cpus()
+        self.sets = {"logical": cpus[:16]}
+        if len(phys) < len(cpus):
+            self.sets["physical"] = phys[:16]
+        self.pools = {}
+        for name, cs in self.sets.items():
+            barrier = self.ctx.Barrier(len(cs))
+            q = self.ctx.Queue()
+            for c in cs:
+                q.put(c)
+            self.pools[name] = (self.ctx.Pool(len(cs), initializer=_cpu_worker_init, initargs=(barrier, q)), len(cs))
+
+    def run(self, name, kind, items):
+        """Splits items into one job per worker; returns (seconds, summed result)."""
+        pool, n = self.pools[name]
+        jobs = [(kind, items[i::n]) for i in range(n)]
+        res = pool.map(_cpu_worker_task, jobs, chunksize=1)
+        return max(r[1] for r in res) - min(r[0] for r in res), sum(r[2] for r in res)
+
+    def close(self):
+        for pool, _ in self.pools.values():
+            pool.terminate()
+
+
+def cpu_baseline(pools):
+    """The oracle, as it stands (fp64 NumPy, one process per core), on the GPU
+    box's host cores, with all logical CPUs and with physical cores only (the
+    faster is reported): decode attention of the whole 256-request batch (KV
+    GB/s, the unit of the GPU figure), the last 64 query rows of every request
+    of the 8-request prefill (causal TFLOP/s) and the 256-row mixed sampler
+    batch (tokens/s)."""
+    from workloads import config, draw_lengths
+    C4, S4 = draw_lengths(config(4))
+    ext_items = []
+    for r in range(len(S4)):
+        E = int(S4[r] - C4[r])
+        ext_items += [(r, E - 64, E - 32), (r, E - 32, E)]
+    runs = {}
+    for name in pools.sets:
+        d_s, d_bytes = pools.run(name, "decode", list(range(256)))
+        e_s, e_flops = pools.run(name, "extend", ext_items)
+        s_s, s_rows = pools.run(name, "sample", list(range(256)))
+        runs[name] = {"cores": len(pools.sets[name]), "decode_s": round(d_s, 3),
+                      "decode_kv_gbs": round(d_bytes / d_s / 1e9, 4), "extend_s": round(e_s, 3),
+                      "extend_tflops": round(e_flops / e_s / 1e12, 6), "sample_s": round(s_s, 3),
+                      "sampler_tokens_per_s": round(s_rows / s_s, 2)}
+        log(f"cpu baseline ({name}, {len(pools.sets[name])} processes): decode {runs[name]['decode_kv_gbs']:.3f} GB/s, "
+            f"extend {runs[name]['extend_tflops'] * 1e3:.3f} GFLOP/s, sampler {runs[name]['sampler_tokens_per_s']:.1f} tokens/s")
+    best = max(runs, key=lambda n: runs[n]["decode_kv_gbs"])
+    b = runs[best]
+    return {"value": b["decode_kv_gbs"], "unit": "GB/s", "cores": b["cores"], "kind": "oracle",
+            "sample": f"decode attention of all 256 requests of the decode batch ({b['decode_s']:.1f} s), plus "
+                      f"the last 64 query rows of each of the 8 prefill requests ({b['extend_s']:.1f} s) and the "
+                      f"256-row mixed sampler batch ({b['sample_s']:.1f} s); fp64 NumPy, one process per core, "
+                      f"{best} cores (the faster of {', '.join(runs)})",
+            "extend_tflops": b["extend_tflops"], "sampler_tokens_per_s": b["sampler_tokens_per_s"],
+            "cpu_model": pools.model, "runs": runs}
 
 
 if __name__ == "__main__":

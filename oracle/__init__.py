@@ -41,7 +41,7 @@ from .pages import bytes_per_page, num_pages
 from .sampling_params import SamplingParams, is_greedy, prepare
 from .store_kv import store_kv
 from .attention import gather_kv, attention_request, attention_decode, attention_extend
-from .sampler import sample, sample_row, DELTA
+from .sampler import sample, sample_row, admissible, admissible_row, DELTA
 from .qk_norm_rope import rmsnorm, rope, rope_angles, rope_inv_freq, qk_norm_rope
 from .embedding import embedding_gather
 
@@ -49,6 +49,6 @@ __all__ = [
     "widen", "bf16_bits_to_f64", "Req", "bytes_per_page", "num_pages",
     "SamplingParams", "is_greedy", "prepare", "store_kv", "gather_kv",
     "attention_request", "attention_decode", "attention_extend", "sample",
-    "sample_row", "DELTA", "rmsnorm", "rope", "rope_angles", "rope_inv_freq", "qk_norm_rope",
+    "sample_row", "admissible", "admissible_row", "DELTA", "rmsnorm", "rope", "rope_angles", "rope_inv_freq", "qk_norm_rope",
     "embedding_gather",
 ]

@@ -120,6 +120,79 @@ def sample_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
     return i, flagged
 
 
+def admissible_row(logits: np.ndarray, T: float, top_k: int, top_p: float, u: float,
+                   delta: float = DELTA, min_p: float = 0.0) -> set:
+    """Every token the sampling rule can return for this row when each
+    rounding-sensitive decision is moved within its margin: the top-p
+    threshold anywhere in [p - delta, p + delta], the min_p threshold anywhere
+    in [min_p (1 - delta), min_p (1 + delta)] (capped at 1), and the draw
+    target anywhere in [u W - delta W, u W + delta W] for the kept mass W of
+    the resulting kept set. These are exactly the decisions whose margins the
+    flag of ``sample_row`` measures, so an unflagged row's set is the single
+    token ``sample_row`` returns. Argmax and top-k are exact order decisions
+    and do not move."""
+    l = np.asarray(logits, dtype=np.float64)
+    V = l.shape[0]
+    if np.float32(T) <= np.float32(MIN_T):
+        return {int(np.argmax(l))}
+    z = l / np.float64(np.float32(T))
+    e = np.exp(z - z.max())
+    order = np.lexsort((np.arange(V), -l))
+    k = V if (top_k <= 0 or top_k >= V) else int(top_k)
+    ranked = order[:k]
+    # kept-set sizes reachable by the top-p threshold (a prefix of the ranking)
+    n_p = [k, k]
+    p = np.float64(np.float32(top_p))
+    if p < 1.0:
+        p = max(p, MIN_P)
+        q = e[ranked] / e[ranked].sum()
+        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+        n_p = [int(np.count_nonzero(before < p - delta)), int(np.count_nonzero(before < p + delta))]
+    # ... and by the min_p threshold (a prefix again: ranked is descending in e)
+    n_m = [k, k]
+    mp = min(np.float64(np.float32(min_p)), 1.0)
+    if mp > 0.0:
+        er = e[ranked]
+        at_max = l[ranked] == l.max()                      # ratio exactly 1: never moves
+        hi_thr, lo_thr = min(mp * (1.0 + delta), 1.0), mp * (1.0 - delta)
+        n_m = [int(np.count_nonzero(at_max | (er >= hi_thr))), int(np.count_nonzero(at_max | (er >= lo_thr)))]
+    n_lo = max(1, min(n_p[0], n_m[0]))
+    n_hi = max(1, min(n_p[1], n_m[1]))
+    out = set()
+    for n in range(n_lo, n_hi + 1):
+        kept = ranked[:n]
+        w = np.zeros(V, dtype=np.float64)
+        w[kept] = e[kept]
+        c = np.cumsum(w)
+        W = c[-1]
+        target = np.float64(np.float32(u)) * W
+        i_lo = int(np.searchsorted(c, target - delta * W, side="right"))
+        i_hi = int(np.searchsorted(c, target + delta * W, side="right"))
+        last = int(kept.max())
+        for i in kept:
+            if i_lo <= i <= i_hi:
+                out.add(int(i))
+        if i_hi >= V or i_lo > last:
+            out.add(last)
+    return out
+
+
+def admissible(logits: np.ndarray, temperature, top_k, top_p, uniforms, rows, delta: float = DELTA,
+               min_p=None) -> dict:
+    """admissible_row for each row in ``rows`` of a batch (arguments as for
+    ``sample``). Returns {row: set of tokens}."""
+    out = {}
+    for r in rows:
+        if temperature is None:
+            out[r] = {int(np.argmax(logits[r]))}
+            continue
+        k = -1 if top_k is None else int(top_k[r])
+        p = 1.0 if top_p is None else float(top_p[r])
+        mp = 0.0 if min_p is None else float(min_p[r])
+        out[r] = admissible_row(logits[r], float(temperature[r]), k, p, float(uniforms[r]), delta, min_p=mp)
+    return out
+
+
 def sample(logits: np.ndarray, temperature, top_k, top_p, uniforms, delta: float = DELTA,
            rows=None, min_p=None):
     """logits: f64 [bs, V]; temperature / top_k / top_p / min_p: per-row

@@ -1110,14 +1110,17 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
   // a chunk, fp64 above
   double mass = 0.0;
   if (need_mass) {
-    const float c2 = sp.c2, off = -fmaxf(key16_value(tk), -1e30f) * c2;
+    // weights exp2((l - t_max) * c2): the difference first (exact for two
+    // bf16 values), then one rounding of the product, so the thread's
+    // reference carries no rounding of its own
+    const float c2 = sp.c2, tmaxv = fmaxf(key16_value(tk), -1e30f);
     auto chunk_mass = [&](const u32x4& x, const u32x4& k, bool masked) {
       float cs = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = x[j];
-        float w0 = fast_exp2(fmaf(__uint_as_float(w << 16), c2, off));
-        float w1 = fast_exp2(fmaf(__uint_as_float(w & 0xffff0000u), c2, off));
+        float w0 = fast_exp2((__uint_as_float(w << 16) - tmaxv) * c2);
+        float w1 = fast_exp2((__uint_as_float(w & 0xffff0000u) - tmaxv) * c2);
         if (masked) {  // key 0: no token
           if ((k[j] & 0xffffu) == 0u) w0 = 0.f;
           if ((k[j] >> 16) == 0u) w1 = 0.f;
@@ -1632,13 +1635,15 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice32_kernel(SampleArg
     for (int e = 0; e < 4; ++e) tk = max(tk, key(i, e));
   double mass = 0.0;  // relative to this thread's maximum: fp32 within a chunk, fp64 above
   if (need_mass) {
-    const float c2 = sp.c2, off = -fmaxf(E::key_value(tk), -1e30f) * c2;
+    // weights exp2((l - t_max) * c2), the difference taken first (see the
+    // bf16 slice kernel)
+    const float c2 = sp.c2, tmaxv = fmaxf(E::key_value(tk), -1e30f);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       float cs = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float w = fast_exp2(fmaf(E::key_value(key(i, e)), c2, off));
+        const float w = fast_exp2((E::key_value(key(i, e)) - tmaxv) * c2);
         cs += key(i, e) ? w : 0.f;
       }
       mass += (double)cs;

@@ -12,3 +12,10 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # GPU runs start the oracle's worker pool now, before any test initialises
+    # the GPU in this process (the full-size parity tests use it)
+    expr = (config.option.markexpr or "").replace(" ", "")
+    if "gpu" in expr and "notgpu" not in expr:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle_pool
+        oracle_pool.start()

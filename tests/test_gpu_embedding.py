@@ -68,11 +68,11 @@ def test_shards_zero_rows_and_strides():
     assert np.array_equal(total, oracle.widen(oracle.embedding_gather(W, ids, 0, V), "bf16"))
 
 
-def test_vocabulary_table_full_size_sampled():
+def test_vocabulary_table_full_size_every_row():
     """The Qwen3-0.6B table (151936 x 1024 bf16, drawn on the device) gathered
     for the 8-request prefill's 19,892 token ids in the launch configuration
-    the benchmark times; 500 seeded rows are checked bit for bit against the
-    oracle on the rows read back."""
+    the benchmark times; every output row is checked bit for bit against the
+    oracle's gather of the table read back."""
     V, H = 151936, 1024
     gen = torch.Generator(device="cuda").manual_seed(11)
     W = torch.randn((V, H), generator=gen, device="cuda").to(torch.bfloat16)
@@ -81,9 +81,5 @@ def test_vocabulary_table_full_size_sampled():
     print("embedding full-size case", flush=True)
     out = pkv.embedding_gather(W, to_dev(ids))
     torch.cuda.synchronize()
-    pick = np.sort(rng.choice(len(ids), 500, replace=False))
-    rows = np.unique(ids[pick])
-    Wh = np.zeros((V, H), dtype=np.uint16)
-    Wh[rows] = to_host(W[torch.from_numpy(rows.astype(np.int64)).cuda()])
-    want = oracle.embedding_gather(Wh, ids[pick], 0, V)
-    assert np.array_equal(_bits(to_host(out)[pick]), _bits(want))
+    want = oracle.embedding_gather(to_host(W), ids, 0, V)
+    assert np.array_equal(_bits(to_host(out)), _bits(want))

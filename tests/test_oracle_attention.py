@@ -177,3 +177,41 @@ def test_bf16_widening_is_exact():
     back = oracle.bf16_bits_to_f64(bits)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(back, ref)
+
+
+def test_ragged_extend_offsets_several_requests():
+    """attention_extend over four requests that each have several query rows
+    (E > 1, unequal) and cached prefixes: request r's rows of the ragged
+    output are SDPA brute force ("Mini-SGLang 完整剖析" section 4.6.5: q is
+    laid end to end, request r starting at the sum of the earlier extend
+    lengths; "第 0 步" section 这份代码在做什么: query t of a request sits at
+    absolute position cached + t). The offsets, the gather and the reference
+    are built here with plain loops, not with the oracle's helpers, so a
+    padded layout, an off-by-one offset or a request mix-up fails."""
+    rng = np.random.default_rng(41)
+    HQ, HKV, D = 8, 4, 32
+    C = [3, 0, 11, 6]
+    E = [5, 2, 7, 4]
+    S = [c + e for c, e in zip(C, E)]
+    n_slots = sum(S) + 10
+    perm = rng.permutation(n_slots)
+    kp = rng.standard_normal((n_slots, HKV, D)).astype(np.float32).astype(np.float64)  # fp32 values
+    vp = rng.standard_normal((n_slots, HKV, D)).astype(np.float32).astype(np.float64)
+    width = max(S) + 3
+    table = np.full((len(S), width), n_slots - 1, np.int64)
+    pos = 0
+    for r, s in enumerate(S):
+        for j in range(s):
+            table[r, j] = perm[pos]
+            pos += 1
+    q = rng.standard_normal((sum(E), HQ, D)).astype(np.float32).astype(np.float64)
+    got = oracle.attention_extend(q, kp, vp, table, np.array(C, np.int32), np.array(S, np.int32), "f32")
+    start = 0
+    for r in range(len(S)):
+        rows = list(range(start, start + E[r]))
+        K = np.stack([kp[table[r, j]] for j in range(S[r])])
+        V = np.stack([vp[table[r, j]] for j in range(S[r])])
+        want = _sdpa(q[rows], K, V, C[r])
+        np.testing.assert_allclose(got[rows], want, rtol=1e-12, atol=1e-12)
+        start += E[r]
+    assert start == got.shape[0]

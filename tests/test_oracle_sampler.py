@@ -294,3 +294,91 @@ def test_min_p_one_at_the_maximum_is_exact():
             assert not flagged
     _, flagged = oracle.sample_row(np.array([3.0, 3.0 - 1e-9]), 1.0, -1, 1.0, 0.2, min_p=1.0)
     assert flagged
+
+
+# ---------------------------------------------------------------- admissible sets of flagged rows
+
+def test_admissible_of_an_unflagged_row_is_its_token():
+    rng = np.random.default_rng(31)
+    n_checked = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 400))
+        logits = np.round(rng.standard_normal(V) * rng.choice([0.5, 2.0, 4.0]), 2)
+        T = float(np.float32(rng.choice([0.3, 0.7, 1.0, 2.5])))
+        k = int(rng.choice([-1, 1, 3, 20, V]))
+        p = float(np.float32(rng.choice([1.0, 0.2, 0.5, 0.9, 0.99])))
+        mp = float(np.float32(rng.choice([0.0, 0.0, 0.05, 0.3])))
+        u = float(rng.random(dtype=np.float32))
+        tok, flagged = oracle.sample_row(logits, T, k, p, u, min_p=mp)
+        if flagged:
+            continue
+        assert oracle.admissible_row(logits, T, k, p, u, min_p=mp) == {tok}
+        n_checked += 1
+    assert n_checked > 250
+
+
+def test_admissible_at_the_pages_top_p_boundary():
+    """[0.66, 0.24, 0.10] with p = 0.9 puts the third token's prior mass on
+    the cut ("源码解析（四）" section 14.4's worked example): kept {0, 1} or
+    {0, 1, 2}. With u = 0.95 the draw gives token 1 (target 0.855 of 0.9) or
+    token 2 (target 0.95 of 1.0); both are admissible, token 0 is not."""
+    g = _golden()["topp_boundary"]
+    logits = np.log(np.array(g["probs"]))
+    tok, flagged = oracle.sample_row(logits, 1.0, -1, g["top_p"], 0.95)
+    assert flagged
+    assert oracle.admissible_row(logits, 1.0, -1, g["top_p"], 0.95) == {1, 2}
+
+
+def test_admissible_covers_perturbed_thresholds():
+    """Rows built to sit on a top-p, min_p or draw boundary: the token drawn
+    with every threshold moved by less than the margin is in the set, and the
+    set stays small."""
+    rng = np.random.default_rng(32)
+    d = oracle.DELTA
+    for trial in range(60):
+        V = int(rng.integers(3, 60))
+        logits = rng.standard_normal(V) * 1.5
+        e = np.exp(logits - logits.max())
+        order = np.lexsort((np.arange(V), -logits))
+        q = e[order] / e.sum()
+        kind = trial % 3
+        p, mp, u = 1.0, 0.0, float(rng.random())
+        if kind == 0:                                   # top-p threshold on a prior mass
+            j = int(rng.integers(1, V))
+            p = float(np.sum(q[:j]))
+        elif kind == 1:                                 # min_p threshold on a ratio
+            j = int(rng.integers(1, V))
+            mp = float(e[order[j]])
+        else:                                           # draw target on a running-mass boundary
+            c = np.cumsum(e) / e.sum()
+            u = float(c[int(rng.integers(0, V - 1))])
+        adm = oracle.admissible_row(logits, 1.0, -1, p, np.float32(u), min_p=mp)
+        assert 1 <= len(adm) <= 4
+        for _ in range(20):
+            e1, e2, e3 = rng.uniform(-0.9, 0.9, 3) * d
+            pp = p + e1 if p < 1.0 else 1.0
+            mm = mp * (1.0 + e3) if mp > 0.0 else 0.0
+            uu = float(np.float32(u)) + e2
+            tok, _ = _sample_exact(logits, pp, mm, uu)
+            assert tok in adm, (trial, kind, tok, adm)
+
+
+def _sample_exact(logits, p, mp, u):
+    """sample_row's rule with thresholds taken as given (no float32 rounding
+    of p, min_p or u): the perturbed reference for the test above."""
+    l = np.asarray(logits, np.float64)
+    V = len(l)
+    e = np.exp(l - l.max())
+    ranked = np.lexsort((np.arange(V), -l))
+    if p < 1.0:
+        q = e[ranked] / e[ranked].sum()
+        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+        ranked = ranked[:max(1, int(np.count_nonzero(before < p)))]
+    if mp > 0.0:
+        keep = (e[ranked] >= min(mp, 1.0)) | (l[ranked] == l.max())
+        ranked = ranked[:int(np.count_nonzero(keep))]
+    w = np.zeros(V)
+    w[ranked] = e[ranked]
+    c = np.cumsum(w)
+    i = int(np.searchsorted(c, u * c[-1], side="right"))
+    return (int(ranked.max()) if i >= V else i), False
