@@ -204,6 +204,31 @@ int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_st
 size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv);
 
 /*
+ * Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, kernels and
+ * results as pkv_paged_attention_decode, without ws / ws_bytes: the split-K
+ * partials go to a scratch array inside the library, one per GPU, of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes, held from the library's first call on that
+ * GPU until the process ends. A call whose pkv_decode_workspace_size(bs,
+ * num_q_heads, max_total_kv) exceeds it returns PKV_ERR_WORKSPACE before
+ * anything is enqueued (16 MiB covers bs <= 768 at 16 query heads with any
+ * max_total_kv). The call itself allocates nothing and calls no allocating
+ * routine. Every call on one GPU shares that GPU's scratch: calls that can
+ * overlap in time on one GPU (different streams, or concurrent host threads
+ * on different streams) race and give wrong results; calls ordered on one
+ * stream are safe. The scratch needs no initialisation (every byte a call
+ * reads was written earlier in the same call).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pkv_paged_attention_decode_noalloc(const pkv_pool* pool, const void* q, int64_t q_stride,
+                                       void* o, int64_t o_stride, int32_t bs, int32_t num_q_heads,
+                                       const int32_t* page_table, int32_t pt_rows, int64_t pt_stride,
+                                       const int32_t* table_idx, const int32_t* cached_len,
+                                       const int32_t* device_len, int64_t max_total_kv, float sm_scale,
+                                       void* stream);
+
+/*
  * Extend (causal prefill over a cached prefix; [TINY] attention with its
  * absolute-position causal mask; [DISS] 4.6.5 cu_seqlens_q as the exclusive
  * prefix sum of extend_len). Request r has C_r = cached_len[r] cached tokens

@@ -210,6 +210,35 @@ def paged_attention_decode(q, k_pool, v_pool, page_table, cached_len, device_len
     return out
 
 
+def paged_attention_decode_noalloc(q, k_pool, v_pool, page_table, cached_len, device_len, *, table_idx=None,
+                                   max_total_kv=None, sm_scale: float = 0.0, page_size: int = 1, out=None,
+                                   stream=None):
+    """Decode attention without a workspace (pkv_paged_attention_decode_noalloc):
+    the library's per-GPU scratch holds the partials. `out` must be given to
+    keep the call free of allocations (else it is created here). Calls that
+    overlap in time on one GPU race."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool, page_size)
+    bs, hq = q.shape[0], q.shape[1]
+    qs = _rows(q, "q", hq * HEAD_DIM)
+    if q.dtype != k_pool.dtype:
+        raise ValueError("q must have the pool's dtype")
+    if out is None:
+        out = torch.empty((bs, hq, HEAD_DIM), dtype=q.dtype, device=q.device)
+    os_ = _rows(out, "out", hq * HEAD_DIM)
+    rows, pts = _table(page_table)
+    _lengths(device_len, "device_len", bs)
+    if table_idx is not None:
+        _lengths(table_idx, "table_idx", bs)
+    if max_total_kv is None:
+        max_total_kv = bs * pts
+    check(lib().pkv_paged_attention_decode_noalloc(
+        byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
+        _ptr(table_idx), _ptr(cached_len), device_len.data_ptr(), int(max_total_kv), sm_scale,
+        _stream(stream)))
+    return out
+
+
 def extend_workspace_size(bs: int, num_q_heads: int, total_q: int) -> int:
     return int(lib().pkv_extend_workspace_size(bs, num_q_heads, total_q))
 

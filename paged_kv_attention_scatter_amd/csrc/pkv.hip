@@ -25,6 +25,14 @@
 // Kernels OR PKV_FAULT_* bits into this word when they meet out-of-range data.
 __device__ uint32_t pkv_fault_word;
 
+// Device scratch of the entry points that allocate nothing (the *_noalloc
+// variants): one copy per GPU, held until the process ends. On the host this
+// name is only a stand-in, not a device address: kernels get the per-device
+// address that hipGetSymbolAddress returns (DeviceState::scratch) instead.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch regions are 256-byte aligned");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -50,6 +58,7 @@ struct DeviceState {
   bool init = false;
   int status = PKV_OK;
   uint32_t* faults = nullptr;  // device address of pkv_fault_word on this device
+  void* scratch = nullptr;     // device address of `scratch` on this device
   int num_cus = 0;
 };
 
@@ -79,6 +88,12 @@ int device_state(DeviceState** out) {
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(pkv_fault_word));
       if (e != hipSuccess) s.status = PKV_ERR_HIP;
       else s.faults = static_cast<uint32_t*>(p);
+      void* sp = nullptr;
+      if (s.status == PKV_OK) {
+        e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !sp) s.status = PKV_ERR_HIP;
+        else s.scratch = sp;
+      }
     }
   }
   if (s.status != PKV_OK)
