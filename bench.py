@@ -54,6 +54,9 @@ def parse():
                     help="skip the mixed chunked-prefill + decode batch (page_size 16) timed after the main step")
     ap.add_argument("--skip-components", action="store_true",
                     help="skip the q/k norm + RoPE + store, embedding and graph-replay timings")
+    ap.add_argument("--small-steps", type=str, default=None, metavar="BS[,BS...]",
+                    help="only time eager decode steps (store_kv, decode, sampler) of the first BS requests of "
+                         "the 256-request batch over a one-layer pool, for kernel traces; prints per-size times")
     ap.add_argument("--copy-calib", action="store_true",
                     help="before warm-up, run plain 1 GiB device copies (untimed) whose counter "
                          "readings calibrate FETCH_SIZE/WRITE_SIZE")
@@ -112,6 +115,8 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
+    if args.small_steps:
+        return small_steps(args)
     cpu_pools = None if args.skip_cpu else CpuPools()  # before anything touches the GPU
     import torch
     import paged_kv_attention_scatter_amd as pkv
@@ -265,6 +270,69 @@ def main():
         torch.cuda.empty_cache()
         result["components"].update(bench_mixed(torch, pkv, dev, args))
     print(json.dumps(result), flush=True)
+
+
+def small_steps(args):
+    """Eager decode steps of the first bs requests of the 256-request batch
+    (store_kv of their new rows, decode attention, the sampler with their
+    mixed parameters), over one layer's pool with the 28-layer page count, so
+    the slots are as scattered as in the full pool. For kernel traces of the
+    small-batch path; prints one line per batch size."""
+    import torch
+    import paged_kv_attention_scatter_amd as pkv
+    from workloads import HEAD_DIM, HKV, HQ, LAYERS, config, draw_lengths, draw_page_table, draw_q, \
+        draw_sampling_params
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1003)
+    cfg = config(3)
+    free, _ = torch.cuda.mem_get_info()
+    num_pages = pkv.num_pages(HEAD_DIM, HKV, 1, 2, LAYERS, free, 0, 0.9)
+    kp = torch.empty((num_pages + 1, HKV, HEAD_DIM), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    vp = torch.empty_like(kp).normal_(generator=gen)
+    C, S = draw_lengths(cfg)
+    table = draw_page_table(cfg, S, num_pages)
+    q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
+    T_all, _, P_all = pkv.prepare_sampling(*zip(*draw_sampling_params(cfg)), vocab=cfg.vocab)
+    res = {}
+    for bs in (int(x) for x in args.small_steps.split(",")):
+        s_q = q[:bs].clone()
+        s_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        s_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        s_loc = torch.from_numpy(table[np.arange(bs), S[:bs] - 1].astype(np.int32)).to(dev)
+        s_table = torch.from_numpy(np.ascontiguousarray(table[:bs])).to(dev)
+        s_C, s_S = torch.from_numpy(C[:bs].copy()).to(dev), torch.from_numpy(S[:bs].copy()).to(dev)
+        logits = [(torch.randn((bs, cfg.vocab), generator=gen, device=dev) * 3).to(torch.bfloat16)
+                  for _ in range(4)]
+        T, P = torch.from_numpy(T_all[:bs].copy()).to(dev), torch.from_numpy(P_all[:bs].copy()).to(dev)
+        u = torch.rand(bs, generator=gen, device=dev)
+        max_kv = int(S[:bs].sum())
+        o = torch.empty_like(s_q)
+        tok = torch.empty(bs, dtype=torch.int32, device=dev)
+        ws_d = torch.empty(pkv.decode_workspace_size(bs, HQ, max_kv), dtype=torch.uint8, device=dev)
+        ws_s = pkv.sample_workspace(bs, cfg.vocab, dev)
+
+        def step(i):
+            pkv.store_kv(kp, vp, s_loc, s_k, s_v)
+            pkv.paged_attention_decode(s_q, kp, vp, s_table, s_C, s_S, max_total_kv=max_kv, out=o, workspace=ws_d)
+            pkv.sample(logits[i % 4], T, None, P, u, out=tok, workspace=ws_s)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        res[f"step_bs{bs}_us"] = round(us, 2)
+        log(f"small-batch decode step bs={bs} (sum device_len {max_kv}): {us:.1f} us")
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the small-batch steps")
+    print(json.dumps({"small_steps": res}), flush=True)
 
 
 def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
@@ -522,65 +590,75 @@ def bench_sampler_variants(torch, pkv, gen, dev, args):
 
 
 def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
-    """A decode step (store_kv, decode attention, sampler) of the first bs
-    requests of the 256-request batch, bs = 1, 8, 64 and 256, over layer 0
-    of the pool: issued eagerly through the Python binding, and replayed from
-    a HIP graph captured once (torch.cuda.CUDAGraph over the same calls)."""
+    """Decode steps (store_kv, decode attention, sampler) of the first bs
+    requests of the 256-request batch over layer 0 of the pool, through the
+    graph runner: sizes 1, 2, 4, 8, 16, ..., 256 captured largest first into
+    one pool, a batch padded to the next captured size with the dummy
+    request. For bs = 1, 5, 8, 60, 64 and 256: the step issued eagerly through
+    the Python binding (unpadded), the padded graph replay with its inputs
+    already in the runner's buffers, and run() (copying the batch in, then
+    the replay)."""
+    from paged_kv_attention_scatter_amd.graph import DecodeGraphRunner
     from workloads import HEAD_DIM, HKV, HQ, config, draw_sampling_params
     V = config(3).vocab
     rows = draw_sampling_params(config(3))
-    T_all, K_all, P_all = pkv.prepare_sampling(*zip(*rows), vocab=V)
+    T_all, _, P_all = pkv.prepare_sampling(*zip(*rows), vocab=V)
     kp, vp = pool[0, 0], pool[1, 0]
-    out = {}
-    for bs in (1, 8, 64, 256):
-        s_q = q[:bs].clone()
-        s_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
-        s_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
-        s_loc = torch.from_numpy(table[np.arange(bs), S[:bs] - 1].astype(np.int32)).to(dev)
-        s_table = torch.from_numpy(np.ascontiguousarray(table[:bs])).to(dev)
-        s_C, s_S = torch.from_numpy(C[:bs].copy()).to(dev), torch.from_numpy(S[:bs].copy()).to(dev)
-        s_logits = (torch.randn((bs, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
-        T, P = torch.from_numpy(T_all[:bs].copy()).to(dev), torch.from_numpy(P_all[:bs].copy()).to(dev)
-        u = torch.rand(bs, generator=gen, device=dev)
+    dummy_slot = kp.shape[0] - 1                         # the dummy page (page_size 1)
+    tab = np.full((table.shape[0] + 1, table.shape[1]), dummy_slot, np.int32)
+    tab[:-1] = table
+    d_tab = torch.from_numpy(tab).to(dev)
+    runner = DecodeGraphRunner(kp, vp, d_tab, dummy_slot, max_bs=256, vocab=V, num_q_heads=HQ,
+                               max_context=table.shape[1])
+    out = {"graph_capture_sizes": len(runner.sizes)}
+    reps = max(50, args.steps)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    for bs in (1, 5, 8, 60, 64, 256):
+        n = runner.size_for(bs)
+        b_q = q[:bs].clone()
+        b_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        b_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        b_loc = torch.from_numpy(table[np.arange(bs), S[:bs] - 1].astype(np.int32)).to(dev)
+        b_idx = torch.arange(bs, dtype=torch.int32, device=dev)
+        b_C, b_S = torch.from_numpy(C[:bs].copy()).to(dev), torch.from_numpy(S[:bs].copy()).to(dev)
+        b_lg = (torch.randn((bs, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
+        b_T, b_P = torch.from_numpy(T_all[:bs].copy()).to(dev), torch.from_numpy(P_all[:bs].copy()).to(dev)
+        b_u = torch.rand(bs, generator=gen, device=dev)
         max_kv = int(S[:bs].sum())
-        o = torch.empty_like(s_q)
+        o = torch.empty_like(b_q)
         tok = torch.empty(bs, dtype=torch.int32, device=dev)
         ws_d = torch.empty(pkv.decode_workspace_size(bs, HQ, max_kv), dtype=torch.uint8, device=dev)
         ws_s = pkv.sample_workspace(bs, V, dev)
 
-        def step():
-            pkv.store_kv(kp, vp, s_loc, s_k, s_v)
-            pkv.paged_attention_decode(s_q, kp, vp, s_table, s_C, s_S, max_total_kv=max_kv, out=o, workspace=ws_d)
-            pkv.sample(s_logits, T, None, P, u, out=tok, workspace=ws_s)
+        def eager():
+            pkv.store_kv(kp, vp, b_loc, b_k, b_v)
+            pkv.paged_attention_decode(b_q, kp, vp, d_tab, b_C, b_S, table_idx=b_idx, max_total_kv=max_kv, out=o,
+                                       workspace=ws_d)
+            pkv.sample(b_lg, b_T, None, b_P, b_u, out=tok, workspace=ws_s)
 
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(3):
-                step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        reps = max(50, args.steps)
-        times = {}
-        for name, fn in (("eager", step), ("graph", graph.replay)):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            times[name] = e0.elapsed_time(e1) / reps * 1e3
-        log(f"decode step bs={bs}: eager {times['eager']:.1f} us, graph replay {times['graph']:.1f} us")
-        out[f"step_bs{bs}_eager_us"] = round(times["eager"], 2)
-        out[f"step_bs{bs}_graph_us"] = round(times["graph"], 2)
-        del graph
+        args_run = (b_q, b_k, b_v, b_loc, b_idx, b_C, b_S, b_lg, b_T, b_P, b_u)
+        runner.run(*args_run)                            # stage this batch (and pad it) once
+        t_eager = timed(eager)
+        t_replay = timed(runner.graphs[n].replay)
+        t_run = timed(lambda: runner.run(*args_run))
+        log(f"decode step bs={bs} (graph size {n}): eager {t_eager:.1f} us, graph replay {t_replay:.1f} us, "
+            f"copy-in + replay {t_run:.1f} us")
+        out[f"step_bs{bs}_eager_us"] = round(t_eager, 2)
+        out[f"step_bs{bs}_graph_us"] = round(t_replay, 2)
+        out[f"step_bs{bs}_graph_run_us"] = round(t_run, 2)
+    del runner
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the graph timing")
     return out

@@ -70,36 +70,52 @@ __device__ __forceinline__ void raise_fault(uint32_t* faults, uint32_t bit) {
   if (faults) atomicOr(faults, bit);
 }
 
+// 32-bit DPP move; a lane without a source in its row reads 0.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i32(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int32_t lane_i32(int32_t x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// Inclusive scan over the 64 lanes of a wave: Kogge-Stone inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then the totals of the rows before added to
+// every lane of a row. Every lane of the wave must be active.
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v, int lane) {
+  v += dpp_i32<0x111>(v);
+  v += dpp_i32<0x112>(v);
+  v += dpp_i32<0x114>(v);
+  v += dpp_i32<0x118>(v);
+  const int32_t o1 = lane_i32(v, 15);
+  const int32_t o2 = o1 + lane_i32(v, 31);
+  const int32_t o3 = o2 + lane_i32(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0 : (row == 1 ? o1 : (row == 2 ? o2 : o3)));
+}
+
 // Exclusive prefix sums of per-request values, computed by a whole
 // workgroup into LDS: on return cu[0] = 0 and cu[i + 1] = cu[i] + val(i)
-// for i < n.
-// `val` is evaluated once per element by the thread that owns it.
+// for i < n. `val` is evaluated once per element by the thread that owns it.
+// Each thread owns a contiguous run of ceil(n / NT) elements; the threads'
+// sums are scanned by wave DPP scans and one exchange of wave totals.
 template <int NT, typename F>
 __device__ void block_exclusive_scan(int32_t* cu, int n, F val) {
-  // Each thread owns a contiguous run of ceil(n / NT) elements.
-  const int t = threadIdx.x;
+  static_assert(NT % kWave == 0 && NT <= 1024, "whole waves");
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int per = (n + NT - 1) / NT;
   const int b = min(n, t * per), e = min(n, b + per);
   int32_t s = 0;
   for (int i = b; i < e; ++i) {
-    int32_t v = val(i);
+    const int32_t v = val(i);
     cu[i + 1] = v;
     s += v;
   }
-  __shared__ int32_t part[NT];
-  part[t] = s;
+  __shared__ int32_t wave_tot[NW];
+  const int32_t incl = wave_incl_scan_i32(s, lane);
+  if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
-  // NT is small (<= 1024): a serial scan by one wave is cheap and exact.
-  if (t == 0) {
-    int32_t acc = 0;
-    for (int i = 0; i < NT; ++i) {
-      int32_t v = part[i];
-      part[i] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  int32_t acc = part[t];
+  int32_t acc = incl - s;
+  for (int w = 0; w < wave; ++w) acc += wave_tot[w];
   for (int i = b; i < e; ++i) {
     acc += cu[i + 1];
     cu[i + 1] = acc;

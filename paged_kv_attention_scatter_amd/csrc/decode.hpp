@@ -43,7 +43,7 @@ struct DecodeArgs {
   void* o;
   int64_t o_stride;
   int32_t bs;
-  int32_t num_items;    // P
+  int32_t num_items;    // workgroups launched: the plan's items for max_total_kv
   const int32_t* page_table;
   int32_t pt_rows;
   int64_t pt_stride;
@@ -66,6 +66,27 @@ template <>
 struct ElemTraits<float> {
   static constexpr int kPerWord = 1;
 };
+
+// The split plan: 256-key items, at most kMaxItems; a batch too small to fill
+// the chip that way gets up to kSmallItems smaller items of at least
+// kMinKeys keys, so one long request spreads over many CUs. The host sizes
+// the grid with it from its bound on the total; the kernels recompute it from
+// the actual total (never more than the grid), so a loose bound -- a graph
+// captured for the largest batch it replays -- still splits the real keys.
+constexpr int kDecodeMaxItems = 1024;     // 256 CUs x 4 resident workgroups
+constexpr int kDecodeKeysPerItem = 256;
+constexpr int kDecodeSmallItems = 512;
+constexpr int kDecodeMinKeysPerItem = 32;
+
+__host__ __device__ inline int decode_num_items(int64_t total, int cap) {
+  int64_t p = (total + kDecodeKeysPerItem - 1) / kDecodeKeysPerItem;
+  int64_t small = (total + kDecodeMinKeysPerItem - 1) / kDecodeMinKeysPerItem;
+  if (small > kDecodeSmallItems) small = kDecodeSmallItems;
+  if (p < small) p = small;
+  if (p > cap) p = cap;
+  if (p < 1) p = 1;
+  return (int)p;
+}
 
 // Item containing flattened key position p (largest i with floor(i*T/P) <= p).
 __device__ __forceinline__ int item_of(int64_t p, int64_t T, int P) {
@@ -166,9 +187,9 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
     for (int i = threadIdx.x; i <= bs; i += NT) a.cu_out[i] = cu[i];
 
   const int64_t total = cu[bs];
-  const int P = a.num_items;
+  const int P = decode_num_items(total, a.num_items);
   const int item = blockIdx.x;
-  if (total == 0) return;
+  if (total == 0 || item >= P) return;
   const int64_t b0 = item_begin(item, total, P), b1 = item_begin(item + 1, total, P);
   if (b0 >= b1) return;
 
@@ -315,62 +336,78 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 
 // Merge the partials of every request that was cut by item boundaries; zero
 // the output of requests whose lengths were invalid. One workgroup per
-// request; every pass over the request's items issues its loads four at a
-// time, so the merge costs a few memory round trips, not one per item.
-// Threads [16h, 16h + 16) handle head h, eight consecutive dims each
-// (HQ * 16 threads).
+// (request, query head), 512 threads: thread t takes the request's items
+// i0 + g, i0 + g + 32, ... (g = t / 16) for dims [8 (t % 16), 8 (t % 16) + 8)
+// and merges them online (four items' loads in flight per step); the 32 item
+// groups then meet in LDS. A request cut into many items (small batches use
+// small items) costs a few memory round trips, not one per item.
+constexpr int kCombineThreads = 512;
+
 template <typename T, int HQ>
-__global__ void __launch_bounds__(HQ * 16) decode_combine_kernel(DecodeArgs a) {
-  static_assert(HQ * 16 <= 1024, "16 threads per query head");
-  constexpr int kU = 4;  // loads in flight per thread per pass
-  const int r = blockIdx.x;
+__global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeArgs a) {
+  constexpr int kGroups = kCombineThreads / 16;  // item groups
+  constexpr int kU = 4;                          // items in flight per thread per step
+  const int r = blockIdx.x, h = blockIdx.y;
   const int32_t* cu = a.cu_out;
   const int64_t total = cu[a.bs];
   const int32_t c0 = cu[r], c1 = cu[r + 1];
-  T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride;
+  T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride + (int64_t)h * kHeadDim;
+  const int t = threadIdx.x, grp = t >> 4, d0 = (t & 15) * 8;
   if (c1 == c0) {  // invalid request: skipped by the main kernel
-    for (int idx = threadIdx.x; idx < HQ * kHeadDim; idx += blockDim.x) store_out<T>(ob + idx, 0.f);
+    if (t < kHeadDim) store_out<T>(ob + t, 0.f);
     return;
   }
-  const int P = a.num_items;
+  const int P = decode_num_items(total, a.num_items);
   const int i0 = item_of(c0, total, P), i1 = item_of(c1 - 1, total, P);
   if (i0 == i1) return;  // finished in place
-  const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
   // An item that holds no key of the request wrote nothing: it is skipped.
   auto live = [&](int i) { return i <= i1 && item_begin(i, total, P) != item_begin(i + 1, total, P); };
-  auto ml = [&](int i) { return reinterpret_cast<const float2*>(a.part_ml)[(int64_t)(i + r) * HQ + h]; };
-
-  float M = -INFINITY;
-  for (int i = i0; i <= i1; i += kU) {
-    float2 v[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = live(i + u) ? ml(i + u) : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) M = fmaxf(M, v[u].x);
-  }
-  float L = 0.f, A[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = i0; i <= i1; i += kU) {
+  float m = -INFINITY, l = 0.f, A[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = i0 + grp; i <= i1; i += kGroups * kU) {
     float2 v[kU];
     u32x4 x[kU][2];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool ok = live(i + u);
-      v[u] = ok ? ml(i + u) : make_float2(-INFINITY, 0.f);
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.part_acc + ((int64_t)(i + u + r) * HQ + h) * kHeadDim + d0);
+      const int it = i + u * kGroups;
+      const bool ok = live(it);
+      v[u] = ok ? reinterpret_cast<const float2*>(a.part_ml)[(int64_t)(it + r) * HQ + h] : make_float2(-INFINITY, 0.f);
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.part_acc + ((int64_t)(it + r) * HQ + h) * kHeadDim + d0);
       x[u][0] = ok ? src[0] : u32x4{0u, 0u, 0u, 0u};
       x[u][1] = ok ? src[1] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float c = (v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - M);
-      L += v[u].y * c;
+      if (v[u].x == -INFINITY) continue;
+      const float mn = fmaxf(m, v[u].x);
+      const float co = fast_exp2(m - mn), cn = fast_exp2(v[u].x - mn);  // m = -inf gives co = 0
+      l = l * co + v[u].y * cn;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) A[e] += __uint_as_float(x[u][e >> 2][e & 3]) * c;
+      for (int e = 0; e < 8; ++e) A[e] = A[e] * co + __uint_as_float(x[u][e >> 2][e & 3]) * cn;
+      m = mn;
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __shared__ float sm_m[kGroups], sm_l[kGroups];
+  __shared__ float sm_a[kGroups][kHeadDim];
+  if ((t & 15) == 0) {
+    sm_m[grp] = m;
+    sm_l[grp] = l;
+  }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) store_out<T>(ob + (int64_t)h * kHeadDim + d0 + e, A[e] * inv);
+  for (int e = 0; e < 8; ++e) sm_a[grp][d0 + e] = A[e];
+  __syncthreads();
+  if (t < kHeadDim) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) M = fmaxf(M, sm_m[g]);
+    float L = 0.f, Ad = 0.f;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const float c = sm_m[g] == -INFINITY ? 0.f : fast_exp2(sm_m[g] - M);
+      L += sm_l[g] * c;
+      Ad += sm_a[g][t] * c;
+    }
+    store_out<T>(ob + t, L > 0.f ? Ad / L : 0.f);
+  }
 }
 
 }  // namespace pkv

@@ -6,6 +6,7 @@
 // the only device state it owns is the 4-byte fault word below.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>

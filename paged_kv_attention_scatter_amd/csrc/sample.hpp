@@ -119,11 +119,6 @@ constexpr int kSampleMaxRounds = 256;   // memory passes: chunk rounds per wave 
 // Wave-wide reductions and scans on DPP row moves and readlane (no LDS
 // round trips). Every lane of the wave must be active.
 
-// 32-bit DPP move; a lane without a source in its row reads 0.
-template <int CTRL>
-PKV_INLINE int32_t dpp_i32(int32_t x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
-}
 template <int CTRL>
 PKV_INLINE double dpp_f64(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
@@ -131,7 +126,6 @@ PKV_INLINE double dpp_f64(double x) {
   const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int32_t)(uint32_t)(u >> 32));
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-PKV_INLINE int32_t lane_i32(int32_t x, int l) { return __builtin_amdgcn_readlane(x, l); }
 PKV_INLINE double lane_f64(double x, int l) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)u, l);
@@ -204,17 +198,6 @@ PKV_INLINE double wave_scan_f64(double v, int lane, double* excl) {
   const double prev = dpp_f64<0x111>(incl);
   *excl = (lane & 15) ? prev : off;
   return incl;
-}
-PKV_INLINE int32_t wave_incl_scan_i32(int32_t v, int lane) {
-  v += dpp_i32<0x111>(v);
-  v += dpp_i32<0x112>(v);
-  v += dpp_i32<0x114>(v);
-  v += dpp_i32<0x118>(v);
-  const int32_t o1 = lane_i32(v, 15);
-  const int32_t o2 = o1 + lane_i32(v, 31);
-  const int32_t o3 = o2 + lane_i32(v, 47);
-  const int row = lane >> 4;
-  return v + (row == 0 ? 0 : (row == 1 ? o1 : (row == 2 ? o2 : o3)));
 }
 // Sum over the wave, returned in every lane (fp32 tree).
 PKV_INLINE float wave_total_f32(float v) {

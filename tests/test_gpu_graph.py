@@ -136,3 +136,81 @@ def test_decode_step_graph_replays_match_eager():
             tok = to_host(t_g)[:bs]
             assert np.array_equal(tok[~flagged], want[~flagged])
     assert pkv.read_faults() == 0
+
+
+# ---------------------------------------------------------------- the capture set and padded replay
+
+def test_graph_runner_capture_set_and_padding():
+    """DecodeGraphRunner with max_bs 24: sizes 1, 2, 4, 8, 16, 24 captured
+    largest first into one pool. Batches of 3, 5, 13, 24, 1 and 9 requests
+    run padded to 4, 8, 16, 24, 1 and 16 with the dummy request. Every replay
+    (after eager work and a synchronisation) must equal the same padded step
+    launched eagerly by a twin runner on a twin pool, bit for bit (outputs,
+    tokens, the pool outside the dummy slot); the real rows must match the oracle (attention
+    bounds; tokens exact on unflagged rows, admissible on flagged ones); only
+    the real rows' slots and the dummy slot may change in the pool."""
+    from paged_kv_attention_scatter_amd.graph import DecodeGraphRunner, capture_sizes
+    assert capture_sizes(256) == [1, 2, 4] + list(range(8, 257, 8))
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(77)
+    n_req, max_ctx = 40, 1536
+    num_slots = n_req * max_ctx + 1
+    dummy = num_slots - 1
+    slots = rng.permutation(num_slots - 1)
+    table = np.full((n_req + 1, max_ctx), dummy, np.int32)          # last row: the dummy request
+    for r in range(n_req):
+        table[r] = slots[r * max_ctx:(r + 1) * max_ctx]
+    gen = torch.Generator(device=dev).manual_seed(78)
+    pool_g = torch.randn((2, num_slots, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
+    pool_e = pool_g.clone()
+    tab_g, tab_e = to_dev(table), to_dev(table)
+    kw = dict(max_bs=24, vocab=V, num_q_heads=HQ, max_context=max_ctx)
+    run_g = DecodeGraphRunner(pool_g[0], pool_g[1], tab_g, dummy, **kw)
+    run_e = DecodeGraphRunner(pool_e[0], pool_e[1], tab_e, dummy, **kw)
+    assert run_g.sizes == [1, 2, 4, 8, 16, 24]
+    lens = rng.integers(200, max_ctx - 10, n_req).astype(np.int32)   # device_len before this run
+    for bs, want_n in ((3, 4), (5, 8), (13, 16), (24, 24), (1, 1), (9, 16)):
+        reqs = np.sort(rng.choice(n_req, bs, replace=False)).astype(np.int32)
+        lens[reqs] += 1                                                # one new token each
+        S = lens[reqs].copy()
+        C = S - 1
+        loc = table[reqs, S - 1]
+        q = torch.randn((bs, HQ, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((bs, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((bs, HKV, D), generator=gen, device=dev).to(torch.bfloat16)
+        lg = (torch.randn((bs, V), generator=gen, device=dev) * 3).to(torch.bfloat16)
+        T = np.where(rng.random(bs) < 0.5, 0.0, 0.7).astype(np.float32)
+        T = np.maximum(T, np.float32(1e-6)).astype(np.float32)
+        P = np.where(T > 1e-6, 0.9, 1.0).astype(np.float32)
+        u = rng.random(bs, dtype=np.float32)
+        args = (q, k, v, to_dev(loc), to_dev(reqs), to_dev(C), to_dev(S), lg, to_dev(T), to_dev(P), to_dev(u))
+        assert run_g.size_for(bs) == want_n
+        before = to_host(pool_g[0]).copy() if bs == 5 else None
+        torch.cuda.synchronize()
+        print(f"graph runner: batch {bs} -> captured size {want_n}", flush=True)
+        o_g, t_g = run_g.run(*args)
+        torch.cuda.synchronize()
+        o_e, t_e = run_e.run(*args, replay=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)), f"bs {bs}: decode output differs"
+        assert torch.equal(t_g, t_e), f"bs {bs}: tokens differ"
+        # the dummy slot takes every padding row's write: its content is unspecified
+        assert torch.equal(pool_g[:, :dummy].view(torch.int16), pool_e[:, :dummy].view(torch.int16)), \
+            f"bs {bs}: pools differ"
+        got, q_h = to_host(o_g), to_host(q)
+        kp_h, vp_h = to_host(pool_g[0]), to_host(pool_g[1])
+        refs = [attention_request(oracle.widen(q_h[i:i + 1], "bf16"), oracle.widen(kp_h[table[r, :S[i]]], "bf16"),
+                                  oracle.widen(vp_h[table[r, :S[i]]], "bf16"), int(C[i]))[0]
+                for i, r in enumerate(reqs)]
+        check_attention(got, np.stack(refs), "bf16", f"graph runner bs {bs}")
+        assert np.array_equal(kp_h[loc], to_host(k)), "the new K rows are at out_loc"
+        if before is not None:  # nothing but the real rows' slots and the dummy slot changed
+            changed = np.nonzero(np.any(kp_h != before, axis=(1, 2)))[0]
+            assert set(changed.tolist()) <= set(loc.tolist()) | {dummy}
+        lf = oracle.widen(to_host(lg), "bf16")
+        want, flagged = oracle.sample(lf, T, None, P, u.astype(np.float64))
+        tok = to_host(t_g)
+        assert np.array_equal(tok[~flagged], want[~flagged]), f"bs {bs}: tokens differ from the oracle"
+        adm = oracle.admissible(lf, T, None, P, u, np.nonzero(flagged)[0].tolist())
+        assert all(int(tok[i]) in adm[i] for i in np.nonzero(flagged)[0])
+    assert pkv.read_faults() == 0
