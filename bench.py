@@ -257,6 +257,7 @@ def main():
         result["components"].update(bench_extend(torch, pkv, pool, num_pages, gen, dev, args))
     if not args.skip_components:
         result["components"].update(bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
+        result["components"].update(bench_q_prologue(torch, pkv, pool, num_pages, table, C, S, gen, dev, args))
         result["components"].update(bench_embedding(torch, pkv, gen, dev, args))
         result["components"].update(bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args))
         result["components"].update(bench_sampler_variants(torch, pkv, gen, dev, args))
@@ -497,6 +498,69 @@ def bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the qk norm/rope/store timing")
     return cases
+
+
+def bench_q_prologue(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
+    """q's RMSNorm + RoPE in the attention prologue against the unfused chain,
+    over layer 0 of the pool: the 8-request prefill (19,892 new tokens: the
+    store call normalises, rotates and stores k; extend normalises and
+    rotates q itself) and the 256-request decode step. Unfused: the store
+    call also writes q_out (q read, q_out written, read again by attention)."""
+    from workloads import HEAD_DIM, HKV, HQ, config, draw_lengths, draw_page_table
+    kp, vp = pool[0, 0], pool[1, 0]
+    wq = (torch.rand(HEAD_DIM, generator=gen, device=dev) + 0.5).to(torch.bfloat16)
+    wk = (torch.rand(HEAD_DIM, generator=gen, device=dev) + 0.5).to(torch.bfloat16)
+    C4, S4 = draw_lengths(config(4))
+    t4 = draw_page_table(config(4), S4, num_pages)
+    out = {}
+    for name, Cc, Sc, tab in (("prefill8", C4, S4, t4), ("decode256", C, S, table)):
+        pos = np.concatenate([np.arange(c, s) for c, s in zip(Cc, Sc)]).astype(np.int32)
+        loc = np.concatenate([tab[r, Cc[r]:Sc[r]] for r in range(len(Sc))]).astype(np.int32)
+        n = len(pos)
+        q = torch.randn((n, HQ, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((n, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((n, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
+        qo, o = torch.empty_like(q), torch.empty_like(q)
+        d_pos, d_loc = torch.from_numpy(pos).to(dev), torch.from_numpy(loc).to(dev)
+        d_tab = torch.from_numpy(tab).to(dev)
+        d_C, d_S = torch.from_numpy(Cc).to(dev), torch.from_numpy(Sc).to(dev)
+        E = Sc - Cc
+        if name == "prefill8":
+            attn = lambda qq, **kw: pkv.paged_attention_extend(qq, kp, vp, d_tab, d_C, d_S, max_extend=int(E.max()),
+                                                              out=o, **kw)
+        else:
+            ws = torch.empty(pkv.decode_workspace_size(len(Sc), HQ, int(Sc.sum())), dtype=torch.uint8, device=dev)
+            attn = lambda qq, **kw: pkv.paged_attention_decode(qq, kp, vp, d_tab, d_C, d_S,
+                                                              max_total_kv=int(Sc.sum()), out=o, workspace=ws, **kw)
+
+        def unfused():
+            pkv.qk_norm_rope_store_kv(kp, vp, d_loc, q, k, v, d_pos, wq, wk, q_out=qo)
+            attn(qo)
+
+        def fused():
+            pkv.qk_norm_rope_store_kv(kp, vp, d_loc, None, k, v, d_pos, None, wk)
+            attn(q, q_norm_weight=wq)
+
+        times = {}
+        for label, fn in (("unfused", unfused), ("fused", fused)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            reps = max(20, args.steps // 2)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[label] = e0.elapsed_time(e1) / reps * 1e3
+        log(f"q prologue {name}: store + attention unfused {times['unfused']:.1f} us, q norm/rope folded into "
+            f"attention {times['fused']:.1f} us (q round trip {n * HQ * HEAD_DIM * 2 * 2 / 1e6:.1f} MB)")
+        out[f"q_prologue_{name}_unfused_us"] = round(times["unfused"], 2)
+        out[f"q_prologue_{name}_fused_us"] = round(times["fused"], 2)
+    if pkv.read_faults():
+        raise RuntimeError("device fault word set during the q prologue timing")
+    return out
 
 
 def bench_embedding(torch, pkv, gen, dev, args):

@@ -159,7 +159,10 @@ int pkv_embedding_gather(const void* weight, int32_t dtype, int64_t weight_rows,
  *             (PKV_FAULT_STORE_SLOT); its q_out row is still written.
  *   q, q_out  device, [n, num_q_heads, 128] in pool.dtype, token rows
  *             q_stride / q_out_stride elements apart (0 = dense). q_out may
- *             be q (in place); otherwise they must not overlap.
+ *             be q (in place); otherwise they must not overlap. Both NULL:
+ *             the k side only (q then goes through the attention call's own
+ *             prologue, pkv_q_norm_rope); num_q_heads and q_norm_weight are
+ *             then ignored.
  *   k, v      device, [n, kv_heads, 128] in pool.dtype, rows k_stride / v_stride apart.
  *   positions device, int32 [n], absolute token positions (cached_len + t for
  *             the t-th new token of a request).
@@ -202,6 +205,34 @@ int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_st
                                void* ws, size_t ws_bytes, void* stream);
 
 size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv);
+
+/*
+ * Qwen3's q prologue folded into attention ([TINY] its rmsnorm and rope
+ * operators and the layer function, which normalise each q head with q_norm
+ * and rotate it right before attention; [DISS] 4.6.7). With it, the attention
+ * entry points below take the raw projected q and compute, for each query
+ * head vector x of a token at absolute position p,
+ *   y = w * x / sqrt(mean(x^2) + eps),  then the rotation of
+ *   pkv_qk_norm_rope_store_kv (pairs j, j + 64 turned by fp32(p) * f_j),
+ * in fp32, rounded to the pool dtype, before the dot products. p is
+ * device_len - 1 for a decode row and cached_len + t for extend row t. The k
+ * side goes through pkv_qk_norm_rope_store_kv with q = q_out = NULL.
+ *   q_norm_weight  device, [128] in the pool dtype, 16-byte aligned.
+ *   eps >= 0, rope_theta > 1.
+ */
+typedef struct {
+  const void* q_norm_weight;
+  float eps;
+  float rope_theta;
+} pkv_q_norm_rope;
+
+/* pkv_paged_attention_decode with the q prologue (qnr must not be NULL). */
+int pkv_paged_attention_decode_qnr(const pkv_pool* pool, const void* q, int64_t q_stride,
+                                   void* o, int64_t o_stride, int32_t bs, int32_t num_q_heads,
+                                   const int32_t* page_table, int32_t pt_rows, int64_t pt_stride,
+                                   const int32_t* table_idx, const int32_t* cached_len,
+                                   const int32_t* device_len, int64_t max_total_kv, float sm_scale,
+                                   const pkv_q_norm_rope* qnr, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode attention that allocates nothing, for callers that cannot allocate
@@ -254,6 +285,15 @@ int pkv_paged_attention_extend(const pkv_pool* pool, const void* q, int64_t q_st
                                float sm_scale, void* ws, size_t ws_bytes, void* stream);
 
 size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_q);
+
+/* pkv_paged_attention_extend with the q prologue (qnr must not be NULL). */
+int pkv_paged_attention_extend_qnr(const pkv_pool* pool, const void* q, int64_t q_stride,
+                                   void* o, int64_t o_stride, int32_t bs, int32_t num_q_heads,
+                                   const int32_t* page_table, int32_t pt_rows, int64_t pt_stride,
+                                   const int32_t* table_idx, const int32_t* cached_len,
+                                   const int32_t* device_len, int64_t total_q, int32_t max_extend,
+                                   float sm_scale, const pkv_q_norm_rope* qnr, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * Batched sampler ([ENG] 采样器; [SRC4] 14.3-14.4; [DISS] 4.8.4-4.8.6).

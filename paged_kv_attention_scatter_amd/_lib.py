@@ -33,6 +33,10 @@ class PkvPool(ctypes.Structure):
     ]
 
 
+class PkvQNormRope(ctypes.Structure):
+    _fields_ = [("q_norm_weight", c_void_p), ("eps", c_float), ("rope_theta", c_float)]
+
+
 _P_i32 = POINTER(c_int32)
 _P_f32 = POINTER(c_float)
 
@@ -50,6 +54,14 @@ SIGNATURES = {
                                              c_void_p, c_void_p, c_int64, c_float, c_void_p, c_size_t,
                                              c_void_p]),
     "pkv_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int64]),
+    "pkv_paged_attention_decode_qnr": (c_int32, [POINTER(PkvPool), c_void_p, c_int64, c_void_p, c_int64,
+                                                 c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
+                                                 c_void_p, c_void_p, c_int64, c_float, POINTER(PkvQNormRope),
+                                                 c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attention_extend_qnr": (c_int32, [POINTER(PkvPool), c_void_p, c_int64, c_void_p, c_int64,
+                                                 c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
+                                                 c_void_p, c_void_p, c_int64, c_int32, c_float,
+                                                 POINTER(PkvQNormRope), c_void_p, c_size_t, c_void_p]),
     "pkv_paged_attention_decode_noalloc": (c_int32, [POINTER(PkvPool), c_void_p, c_int64, c_void_p, c_int64,
                                                      c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
                                                      c_void_p, c_void_p, c_int64, c_float, c_void_p]),

@@ -13,7 +13,7 @@ from ctypes import byref, c_float, c_int32, c_uint32
 import numpy as np
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F32, PKV_I32, PKV_I64, PkvPool, check, lib
+from ._lib import PKV_BF16, PKV_F32, PKV_I32, PKV_I64, PkvPool, PkvQNormRope, check, lib
 
 HEAD_DIM = 128
 
@@ -119,11 +119,32 @@ def qk_norm_rope_store_kv(k_pool, v_pool, out_loc, q, k, v, positions, q_norm_we
                           stream=None):
     """Per-head RMSNorm of q and k, rotary embedding at `positions`, then the
     K/V store (pkv_qk_norm_rope_store_kv). Returns q_out ([n, num_q_heads,
-    128], the normalised and rotated q; pass q_out=q to work in place)."""
+    128], the normalised and rotated q; pass q_out=q to work in place).
+    q=None: the k side only (q then goes through the attention call's own
+    prologue, q_norm_weight=...); returns None."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool, page_size)
     width = pool.kv_heads * HEAD_DIM
     n = out_loc.shape[0]
+    if q is None:
+        for t, name in ((out_loc, "out_loc"), (positions, "positions"), (k, "k"), (v, "v"),
+                        (k_norm_weight, "k_norm_weight")):
+            _cuda(t, name)
+        if k.dtype != k_pool.dtype or v.dtype != k_pool.dtype or k.shape[0] != n or v.shape[0] != n:
+            raise ValueError("k, v must have the pool dtype and len(out_loc) rows")
+        if positions.dtype != torch.int32 or positions.shape[0] != n or positions.stride(0) != 1:
+            raise ValueError("positions must be a dense int32 tensor of len(out_loc) entries")
+        if out_loc.dtype not in (torch.int32, torch.int64) or out_loc.dim() != 1 or out_loc.stride(0) != 1:
+            raise ValueError("out_loc must be a dense 1-D int32 or int64 tensor")
+        if k_norm_weight.dtype != k_pool.dtype or k_norm_weight.numel() != HEAD_DIM:
+            raise ValueError(f"k_norm_weight must be a dense [{HEAD_DIM}] tensor of the pool dtype")
+        ks, vs = _rows(k, "k", width), _rows(v, "v", width)
+        loc_t = PKV_I32 if out_loc.dtype == torch.int32 else PKV_I64
+        check(lib().pkv_qk_norm_rope_store_kv(byref(pool), _ptr(out_loc), loc_t, n, None, 0, None, 0, 0,
+                                              k.data_ptr(), ks, v.data_ptr(), vs, _ptr(positions), None,
+                                              k_norm_weight.data_ptr(), float(eps), float(rope_theta),
+                                              _stream(stream)))
+        return None
     for t, name in ((out_loc, "out_loc"), (positions, "positions"), (q, "q"), (k, "k"), (v, "v"),
                     (q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
         _cuda(t, name)
@@ -182,11 +203,23 @@ def _workspace(nbytes, device, workspace):
     return workspace
 
 
+def _qnr(q_norm_weight, eps, rope_theta, pool_dtype):
+    if q_norm_weight is None:
+        return None
+    _cuda(q_norm_weight, "q_norm_weight")
+    if q_norm_weight.dtype != pool_dtype or q_norm_weight.numel() != HEAD_DIM or not q_norm_weight.is_contiguous():
+        raise ValueError(f"q_norm_weight must be a dense [{HEAD_DIM}] tensor of the pool dtype")
+    return PkvQNormRope(q_norm_weight.data_ptr(), float(eps), float(rope_theta))
+
+
 def paged_attention_decode(q, k_pool, v_pool, page_table, cached_len, device_len, *, table_idx=None,
                            max_total_kv=None, sm_scale: float = 0.0, page_size: int = 1, out=None,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, q_norm_weight=None, eps: float = 1e-6,
+                           rope_theta: float = 1_000_000.0):
     """GQA decode attention over the paged pool (pkv_paged_attention_decode).
-    q: [bs, num_q_heads, 128]. Returns o with q's shape and dtype."""
+    q: [bs, num_q_heads, 128]. Returns o with q's shape and dtype.
+    With q_norm_weight, q is the raw projection and the call normalises and
+    rotates it first (pkv_paged_attention_decode_qnr)."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool, page_size)
     bs, hq = q.shape[0], q.shape[1]
@@ -203,10 +236,14 @@ def paged_attention_decode(q, k_pool, v_pool, page_table, cached_len, device_len
     if max_total_kv is None:
         max_total_kv = bs * pts
     ws = _workspace(decode_workspace_size(bs, hq, max_total_kv), q.device, workspace)
-    check(lib().pkv_paged_attention_decode(
-        byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
-        _ptr(table_idx), _ptr(cached_len), device_len.data_ptr(), int(max_total_kv), sm_scale,
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    qnr = _qnr(q_norm_weight, eps, rope_theta, k_pool.dtype)
+    common = (byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
+              _ptr(table_idx), _ptr(cached_len), device_len.data_ptr(), int(max_total_kv), sm_scale)
+    wsa = (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if qnr is None:
+        check(lib().pkv_paged_attention_decode(*common, *wsa))
+    else:
+        check(lib().pkv_paged_attention_decode_qnr(*common, byref(qnr), *wsa))
     return out
 
 
@@ -245,10 +282,13 @@ def extend_workspace_size(bs: int, num_q_heads: int, total_q: int) -> int:
 
 def paged_attention_extend(q, k_pool, v_pool, page_table, cached_len, device_len, *, max_extend: int,
                            table_idx=None, sm_scale: float = 0.0, page_size: int = 1, out=None,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, q_norm_weight=None, eps: float = 1e-6,
+                           rope_theta: float = 1_000_000.0):
     """Causal extend attention over a cached prefix (pkv_paged_attention_extend).
     q: ragged [total_q, num_q_heads, 128] in request order; max_extend bounds
-    every request's extend_len. Returns o with q's shape and dtype."""
+    every request's extend_len. Returns o with q's shape and dtype.
+    With q_norm_weight, q is the raw projection and the call normalises and
+    rotates it first (pkv_paged_attention_extend_qnr)."""
     torch = _torch()
     pool = make_pool(k_pool, v_pool, page_size)
     total_q, hq = q.shape[0], q.shape[1]
@@ -265,10 +305,14 @@ def paged_attention_extend(q, k_pool, v_pool, page_table, cached_len, device_len
     if table_idx is not None:
         _lengths(table_idx, "table_idx", bs)
     ws = _workspace(extend_workspace_size(bs, hq, total_q), q.device, workspace)
-    check(lib().pkv_paged_attention_extend(
-        byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
-        _ptr(table_idx), cached_len.data_ptr(), device_len.data_ptr(), total_q, int(max_extend), sm_scale,
-        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    qnr = _qnr(q_norm_weight, eps, rope_theta, k_pool.dtype)
+    common = (byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
+              _ptr(table_idx), cached_len.data_ptr(), device_len.data_ptr(), total_q, int(max_extend), sm_scale)
+    wsa = (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if qnr is None:
+        check(lib().pkv_paged_attention_extend(*common, *wsa))
+    else:
+        check(lib().pkv_paged_attention_extend_qnr(*common, byref(qnr), *wsa))
     return out
 
 

@@ -54,6 +54,10 @@ struct DecodeArgs {
   float* part_acc;      // [P + bs][HQ][128]
   int32_t* cu_out;      // [bs + 1] prefix of valid lengths (written by block 0)
   uint32_t* faults;
+  // q prologue (Qwen3's q_norm + rotary embedding), or q_w == nullptr
+  const void* q_w;      // [128] norm weight, element type T
+  float q_eps;
+  float inv_freq[64];   // fp32 rotary frequencies 1 / theta^(2j / 128)
 };
 
 template <typename T>
@@ -67,9 +71,9 @@ struct ElemTraits<float> {
   static constexpr int kPerWord = 1;
 };
 
-// The split plan: 256-key items, at most kMaxItems; a batch too small to fill
-// the chip that way gets up to kSmallItems smaller items of at least
-// kMinKeys keys, so one long request spreads over many CUs. The host sizes
+// The split plan: 256-key items, at most kDecodeMaxItems; a batch too small
+// to fill the chip that way gets up to kDecodeSmallItems smaller items of at
+// least kDecodeMinKeysPerItem keys, so one long request spreads over many CUs. The host sizes
 // the grid with it from its bound on the total; the kernels recompute it from
 // the actual total (never more than the grid), so a loose bound -- a graph
 // captured for the largest batch it replays -- still splits the real keys.
@@ -152,6 +156,53 @@ __device__ __forceinline__ void store_out<float>(float* o, float x) {
   *o = x;
 }
 
+// The q prologue of the fused path ("第 0 步：一个能跑的最小推理引擎": the
+// layer's q_norm, then rope at the token's position; "Mini-SGLang 完整剖析"
+// section 4.6.7): this lane's DPL dims of one query head, normalised over the
+// head (a sum over its LPH lanes), times the norm weight, then rotated: dims
+// j < 64 and j + 64 form a pair turned by pos * inv_freq[j], the other
+// member held by the lane LPH / 2 away. Arithmetic in fp32, the result in T.
+template <typename T, int LPH, int DPL, int NWD>
+__device__ __forceinline__ void q_norm_rope(uint32_t (&qw)[NWD], const DecodeArgs& a, int dofs, float pos) {
+  constexpr int EPW = ElemTraits<T>::kPerWord;
+  float x[DPL], w[DPL];
+#pragma unroll
+  for (int i = 0; i < NWD; ++i) {
+    if constexpr (EPW == 2) {
+      x[2 * i] = bf16_lo(qw[i]);
+      x[2 * i + 1] = bf16_hi(qw[i]);
+    } else {
+      x[i] = __uint_as_float(qw[i]);
+    }
+  }
+  const T* wp = reinterpret_cast<const T*>(a.q_w) + dofs;
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    if constexpr (EPW == 2) w[d] = bf16_to_f32(wp[d]);
+    else w[d] = reinterpret_cast<const float*>(wp)[d];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) ss = fmaf(x[d], x[d], ss);
+  ss = group_sum<LPH>(ss);
+  const float rn = 1.0f / sqrtf(fmaf(ss, 1.0f / (float)kHeadDim, a.q_eps));
+  const bool first = dofs < kHeadDim / 2;
+  float y[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    const float u = x[d] * rn * w[d];
+    const float up = __shfl_xor(u, LPH / 2, 64);  // the pair's other member
+    float sn, cs;
+    sincosf(pos * a.inv_freq[(dofs + d) & (kHeadDim / 2 - 1)], &sn, &cs);
+    y[d] = first ? u * cs - up * sn : up * sn + u * cs;
+  }
+#pragma unroll
+  for (int i = 0; i < NWD; ++i) {
+    if constexpr (EPW == 2) qw[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+    else qw[i] = __float_as_uint(y[i]);
+  }
+}
+
 template <typename T, int HKV, int G, int NWAVE, int KB>
 __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a) {
   constexpr int HQ = HKV * G;
@@ -221,6 +272,10 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 #pragma unroll
       for (int hh = 0; hh < G; ++hh)
         load_lane_row<T, NWD>(qw[hh], qb + (int64_t)(g * G + hh) * kHeadDim + dofs);
+      if (a.q_w) {  // fused q prologue: the new token sits at position S - 1
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) q_norm_rope<T, LPH, DPL, NWD>(qw[hh], a, dofs, (float)(S - 1));
+      }
     }
 
     float m[G], l[G], acc[G][DPL];

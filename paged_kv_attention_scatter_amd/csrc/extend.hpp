@@ -72,6 +72,10 @@ struct ExtendArgs {
   int32_t max_extend;
   float scale_log2;      // sm_scale * log2(e)
   uint32_t* faults;
+  // q prologue (Qwen3's q_norm + rotary embedding), or q_w == nullptr
+  const void* q_w;       // [128] bf16 norm weight
+  float q_eps;
+  float inv_freq[64];    // fp32 rotary frequencies 1 / theta^(2j / 128)
 };
 
 constexpr int kExtBlockQ = 128;  // query positions per workgroup
@@ -173,6 +177,64 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (t_ok) w = *reinterpret_cast<const u32x4*>(qrow + ks * 32 + lg * 8);
       qreg[hh][ks] = __builtin_bit_cast(bf16x8_v, w);
+    }
+  }
+  if (a.q_w) {
+    // Fused q prologue ("第 0 步" layer function: q_norm, then rope at the
+    // query's absolute position C + t; "Mini-SGLang 完整剖析" section 4.6.7).
+    // The lane holds dims 32 ks + 8 lg + i of its query: the row's norm is a
+    // sum over the four lanes lq + 16 lg, and dims j and j + 64 of a rotated
+    // pair sit in k-steps ks and ks + 2 of the same lane. fp32, then bf16.
+    const float pos = (float)(C + t_eff);
+    float w[4][8], cs[2][8], sn[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 wr = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.q_w) + ks * 32 + lg * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[ks][2 * i] = bf16_lo(wr[i]);
+        w[ks][2 * i + 1] = bf16_hi(wr[i]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sincosf(pos * a.inv_freq[ks * 32 + lg * 8 + i], &sn[ks][i], &cs[ks][i]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      float x[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 raw = __builtin_bit_cast(u32x4, qreg[hh][ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[ks][2 * i] = bf16_lo(raw[i]);
+          x[ks][2 * i + 1] = bf16_hi(raw[i]);
+        }
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(x[ks][i], x[ks][i], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float rn = t_ok ? 1.0f / sqrtf(fmaf(ss, 1.0f / (float)kHeadDim, a.q_eps)) : 0.f;
+      float y[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u = x[ks][i] * rn * w[ks][i], v = x[ks + 2][i] * rn * w[ks + 2][i];
+          y[ks][i] = u * cs[ks][i] - v * sn[ks][i];
+          y[ks + 2][i] = u * sn[ks][i] + v * cs[ks][i];
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 packed = {pack_bf16x2(y[ks][0], y[ks][1]), pack_bf16x2(y[ks][2], y[ks][3]),
+                              pack_bf16x2(y[ks][4], y[ks][5]), pack_bf16x2(y[ks][6], y[ks][7])};
+        qreg[hh][ks] = __builtin_bit_cast(bf16x8_v, packed);
+      }
     }
   }
 

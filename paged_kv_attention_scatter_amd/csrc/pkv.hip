@@ -145,6 +145,32 @@ int check_rows(const void* p, int64_t stride, int64_t min_stride, int isz, const
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// 1 / theta^(2j/128) for j < 64: the power in fp64 rounded to fp32, then an
+// fp32 division (kept per host thread for the last theta, a pure function of
+// it), as the step-0 page's fp32 tensors compute it.
+void rope_inv_freq(float rope_theta, float (&out)[pkv::kHeadDim / 2]) {
+  thread_local float freq_theta = 0.f;
+  thread_local float freq[pkv::kHeadDim / 2];
+  if (freq_theta != rope_theta) {
+    for (int j = 0; j < pkv::kHeadDim / 2; ++j) {
+      const float p = (float)std::pow((double)rope_theta, (double)(2 * j) / (double)pkv::kHeadDim);
+      freq[j] = 1.0f / p;
+    }
+    freq_theta = rope_theta;
+  }
+  std::memcpy(out, freq, sizeof freq);
+}
+
+// Validates the q prologue descriptor of the *_qnr entry points.
+int check_qnr(const pkv_q_norm_rope* qnr) {
+  if (!qnr || !qnr->q_norm_weight) return fail(PKV_ERR_NULL, "q prologue or its q_norm_weight is NULL");
+  if (!aligned16(qnr->q_norm_weight)) return fail(PKV_ERR_ALIGN, "q_norm_weight must be 16-byte aligned");
+  if (!(qnr->eps >= 0.f) || !(qnr->rope_theta > 1.f))
+    return fail(PKV_ERR_SHAPE, "need eps >= 0 and rope_theta > 1 (eps %g, rope_theta %g)", qnr->eps,
+                qnr->rope_theta);
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,7 +285,9 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
   if (n < 0) return fail(PKV_ERR_SHAPE, "n = %lld < 0", (long long)n);
   if (loc_type != PKV_I32 && loc_type != PKV_I64)
     return fail(PKV_ERR_DTYPE, "loc_type %d is not PKV_I32 or PKV_I64", loc_type);
-  if (num_q_heads < 1 || num_q_heads % pool->kv_heads)
+  const bool with_q = q != nullptr || q_out != nullptr;
+  if (!with_q) num_q_heads = 0;  // k side only
+  if (with_q && (num_q_heads < 1 || num_q_heads % pool->kv_heads))
     return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of kv_heads %d", num_q_heads,
                 pool->kv_heads);
   if (num_q_heads > 32 || pool->kv_heads > 16)
@@ -269,14 +297,18 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
     return fail(PKV_ERR_SHAPE, "need eps >= 0 and rope_theta > 1 (eps %g, rope_theta %g)", eps, rope_theta);
   if (n == 0) return ok();
   if (!out_loc || !positions) return fail(PKV_ERR_NULL, "out_loc / positions is NULL");
-  if (!q_norm_weight || !k_norm_weight) return fail(PKV_ERR_NULL, "a norm weight is NULL");
-  if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
+  if ((with_q && !q_norm_weight) || !k_norm_weight) return fail(PKV_ERR_NULL, "a norm weight is NULL");
+  if ((with_q && !aligned16(q_norm_weight)) || !aligned16(k_norm_weight))
     return fail(PKV_ERR_ALIGN, "norm weights must be 16-byte aligned");
   const int64_t qrow = (int64_t)num_q_heads * pkv::kHeadDim, kvrow = (int64_t)pool->kv_heads * pkv::kHeadDim;
-  if (q_stride == 0) q_stride = qrow;
-  if (q_out_stride == 0) q_out_stride = qrow;
-  if ((rc = check_rows(q, q_stride, qrow, isz, "q"))) return rc;
-  if ((rc = check_rows(q_out, q_out_stride, qrow, isz, "q_out"))) return rc;
+  if (with_q) {
+    if (q_stride == 0) q_stride = qrow;
+    if (q_out_stride == 0) q_out_stride = qrow;
+    if ((rc = check_rows(q, q_stride, qrow, isz, "q"))) return rc;
+    if ((rc = check_rows(q_out, q_out_stride, qrow, isz, "q_out"))) return rc;
+  } else {
+    q_norm_weight = k_norm_weight;  // never read (no query heads)
+  }
   if ((rc = check_rows(k, k_stride, kvrow, isz, "k"))) return rc;
   if ((rc = check_rows(v, v_stride, kvrow, isz, "v"))) return rc;
   constexpr int TPB = pkv::kQkRopeThreads / pkv::kWave;  // tokens per workgroup
@@ -305,21 +337,10 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
   a.hq = num_q_heads;
   a.hkv = pool->kv_heads;
   a.eps = eps;
-  // 1 / theta^(2j/128): the power in fp64 rounded to fp32, then an fp32
-  // division (kept per host thread for the last theta, a pure function of it)
-  thread_local float freq_theta = 0.f;
-  thread_local float freq[pkv::kHeadDim / 2];
-  if (freq_theta != rope_theta) {
-    for (int j = 0; j < pkv::kHeadDim / 2; ++j) {
-      const float p = (float)std::pow((double)rope_theta, (double)(2 * j) / (double)pkv::kHeadDim);
-      freq[j] = 1.0f / p;
-    }
-    freq_theta = rope_theta;
-  }
-  std::memcpy(a.inv_freq, freq, sizeof freq);
+  rope_inv_freq(rope_theta, a.inv_freq);
   a.faults = ds->faults;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int mq = (num_q_heads + 3) / 4, mk = (pool->kv_heads + 3) / 4;
+  const int mq = std::max(1, (num_q_heads + 3) / 4), mk = (pool->kv_heads + 3) / 4;
   const bool i64 = loc_type == PKV_I64;
 #define PKV_QKR_LAUNCH(T, MQ, MK)                                                                               \
   hipLaunchKernelGGL(i64 ? (pkv::qk_rope_store_kernel<T, int64_t, MQ, MK>) : (pkv::qk_rope_store_kernel<T, int32_t, MQ, MK>), \

@@ -186,3 +186,135 @@ def test_prefill_token_count_every_token():
     _check(to_host(qo), rq, "bf16", "prefill q_out, every token")
     _check(to_host(kp)[loc], rk, "bf16", "prefill K rows, every token")
     assert np.array_equal(_bits(to_host(vp)[loc]), _bits(vh)), "prefill V rows differ"
+
+
+# ---------------------------------------------------------------- q's norm + RoPE in the attention prologue
+# ("第 0 步" layer function: q_norm and rope right before attention; "Mini-SGLang
+# 完整剖析" section 4.6.7). The k side goes through the store call with q =
+# None; the attention call normalises and rotates the raw q itself. Checked
+# through oracle.qk_norm_rope followed by oracle attention over the pool rows
+# the kernels wrote, and against the unfused chain (q_out through the store
+# call, then plain attention).
+
+def _paged(rng, lens, hkv, dtype, extra=50):
+    """Pool with random rows everywhere, one table row per request."""
+    S = np.asarray(lens, np.int32)
+    n_slots = int(S.sum()) + extra
+    perm = rng.permutation(n_slots)
+    width = (int(S.max()) + 31) // 32 * 32
+    table = np.full((len(S), width), n_slots - 1, np.int32)
+    off = 0
+    for r, s in enumerate(S):
+        table[r, :s] = perm[off:off + s]
+        off += s
+    kv = rng.standard_normal((2, n_slots, hkv, 128), dtype=np.float32)
+    if dtype == "bf16":
+        kv = f32_to_bf16_bits(kv)
+    return table, kv
+
+
+def _attn_ref(q64, kp_h, vp_h, table, C, S, dtype):
+    """fp64 attention of the rotated queries q64 (ragged, request order) over
+    the pool rows as the kernels left them."""
+    from oracle.attention import attention_request
+    out, off = [], 0
+    for r in range(len(S)):
+        e = int(S[r] - C[r])
+        rows = table[r, :S[r]]
+        out.append(attention_request(q64[off:off + e], oracle.widen(kp_h[rows], dtype),
+                                     oracle.widen(vp_h[rows], dtype), int(C[r])))
+        off += e
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("dtype,hkv,g", [("bf16", 8, 2), ("f32", 8, 2), ("bf16", 4, 4), ("f32", 4, 1)])
+def test_decode_with_q_prologue(dtype, hkv, g):
+    from gpu_util import check_attention
+    rng = _rng(f"dec-qnr-{dtype}-{hkv}-{g}")
+    hq = hkv * g
+    S = rng.integers(1, 3000, 9).astype(np.int32)
+    S[0] = 1
+    C = S - 1
+    table, kv = _paged(rng, S, hkv, dtype)
+    as_dt = (lambda x: f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    q = as_dt(rng.standard_normal((len(S), hq, 128), dtype=np.float32) * 1.7)
+    k = as_dt(rng.standard_normal((len(S), hkv, 128), dtype=np.float32) * 2.0)
+    v = as_dt(rng.standard_normal((len(S), hkv, 128), dtype=np.float32))
+    wq = as_dt(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    wk = as_dt(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    pos = (S - 1).astype(np.int32)
+    loc = table[np.arange(len(S)), S - 1].astype(np.int32)
+    d = lambda x: to_dev(x, dtype)
+    outs = {}
+    for mode in ("fused", "unfused"):
+        kp, vp = d(kv[0]), d(kv[1])
+        print(f"decode q-prologue case {dtype} hkv={hkv} g={g} {mode}", flush=True)
+        if mode == "fused":
+            pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), None, d(k), d(v), to_dev(pos), None, d(wk),
+                                      eps=EPS, rope_theta=THETA)
+            o = pkv.paged_attention_decode(d(q), kp, vp, to_dev(table), to_dev(C), to_dev(S),
+                                           max_total_kv=int(S.sum()), q_norm_weight=d(wq), eps=EPS,
+                                           rope_theta=THETA)
+        else:
+            qo = pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), d(q), d(k), d(v), to_dev(pos), d(wq), d(wk),
+                                           eps=EPS, rope_theta=THETA)
+            o = pkv.paged_attention_decode(qo, kp, vp, to_dev(table), to_dev(C), to_dev(S),
+                                           max_total_kv=int(S.sum()))
+        torch.cuda.synchronize()
+        outs[mode] = (to_host(o), to_host(kp), to_host(vp))
+    assert pkv.read_faults() == 0
+    # the k side is the same call in both modes: identical pools
+    assert np.array_equal(_bits(outs["fused"][1]), _bits(outs["unfused"][1]))
+    w = lambda x: oracle.widen(x, dtype)
+    rq, _ = oracle.qk_norm_rope(w(q), w(k), pos, w(wq), w(wk), EPS, THETA)
+    ref = _attn_ref(rq, outs["fused"][1], outs["fused"][2], table, C, S, dtype)
+    mx, rel = check_attention(outs["fused"][0], ref, dtype, f"decode with q prologue ({dtype})")
+    print(f"  fused vs oracle: max|d|={mx:.3e} relL2={rel:.3e}", flush=True)
+    check_attention(outs["unfused"][0], ref, dtype, f"unfused chain ({dtype})")
+
+
+@pytest.mark.parametrize("hkv,g", [(8, 2), (4, 1)])
+def test_extend_with_q_prologue(hkv, g):
+    """Three requests over cached prefixes (several 128-row query blocks,
+    ragged tails), bf16: the k side of the new tokens stored by the fused
+    store call, then extend with the q prologue at positions C + t."""
+    from gpu_util import check_attention
+    rng = _rng(f"ext-qnr-{hkv}-{g}")
+    hq = hkv * g
+    C = np.array([5, 0, 300], np.int32)
+    E = np.array([40, 257, 130], np.int32)
+    S = C + E
+    table, kv = _paged(rng, S, hkv, "bf16")
+    n = int(E.sum())
+    q = f32_to_bf16_bits(rng.standard_normal((n, hq, 128), dtype=np.float32) * 1.7)
+    k = f32_to_bf16_bits(rng.standard_normal((n, hkv, 128), dtype=np.float32) * 2.0)
+    v = f32_to_bf16_bits(rng.standard_normal((n, hkv, 128), dtype=np.float32))
+    wq = f32_to_bf16_bits(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    wk = f32_to_bf16_bits(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    pos = np.concatenate([np.arange(c, s) for c, s in zip(C, S)]).astype(np.int32)
+    loc = np.concatenate([table[r, C[r]:S[r]] for r in range(len(S))]).astype(np.int32)
+    d = lambda x: to_dev(x, "bf16")
+    outs = {}
+    for mode in ("fused", "unfused"):
+        kp, vp = d(kv[0]), d(kv[1])
+        print(f"extend q-prologue case hkv={hkv} g={g} {mode}", flush=True)
+        if mode == "fused":
+            pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), None, d(k), d(v), to_dev(pos), None, d(wk),
+                                      eps=EPS, rope_theta=THETA)
+            o = pkv.paged_attention_extend(d(q), kp, vp, to_dev(table), to_dev(C), to_dev(S),
+                                           max_extend=int(E.max()), q_norm_weight=d(wq), eps=EPS, rope_theta=THETA)
+        else:
+            qo = pkv.qk_norm_rope_store_kv(kp, vp, to_dev(loc), d(q), d(k), d(v), to_dev(pos), d(wq), d(wk),
+                                           eps=EPS, rope_theta=THETA)
+            o = pkv.paged_attention_extend(qo, kp, vp, to_dev(table), to_dev(C), to_dev(S),
+                                           max_extend=int(E.max()))
+        torch.cuda.synchronize()
+        outs[mode] = (to_host(o), to_host(kp), to_host(vp))
+    assert pkv.read_faults() == 0
+    assert np.array_equal(_bits(outs["fused"][1]), _bits(outs["unfused"][1]))
+    w = lambda x: oracle.widen(x, "bf16")
+    rq, _ = oracle.qk_norm_rope(w(q), w(k), pos, w(wq), w(wk), EPS, THETA)
+    ref = _attn_ref(rq, outs["fused"][1], outs["fused"][2], table, C, S, "bf16")
+    mx, rel = check_attention(outs["fused"][0], ref, "bf16", "extend with q prologue")
+    print(f"  fused vs oracle: max|d|={mx:.3e} relL2={rel:.3e}", flush=True)
+    check_attention(outs["unfused"][0], ref, "bf16", "unfused extend chain")
