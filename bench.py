@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--small-steps", type=str, default=None, metavar="BS[,BS...]",
                     help="only time eager decode steps (store_kv, decode, sampler) of the first BS requests of "
                          "the 256-request batch over a one-layer pool, for kernel traces; prints per-size times")
+    ap.add_argument("--sampler-only", action="store_true",
+                    help="only time the sampler: the 256-row mixed batch, then the variants; for kernel traces")
     ap.add_argument("--copy-calib", action="store_true",
                     help="before warm-up, run plain 1 GiB device copies (untimed) whose counter "
                          "readings calibrate FETCH_SIZE/WRITE_SIZE")
@@ -117,6 +119,8 @@ def main():
         sys.exit(2)
     if args.small_steps:
         return small_steps(args)
+    if args.sampler_only:
+        return sampler_only(args)
     cpu_pools = None if args.skip_cpu else CpuPools()  # before anything touches the GPU
     import torch
     import paged_kv_attention_scatter_amd as pkv
@@ -334,6 +338,43 @@ def small_steps(args):
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the small-batch steps")
     print(json.dumps({"small_steps": res}), flush=True)
+
+
+def sampler_only(args):
+    """The sampler alone: the 256-row mixed batch of the decode step (128
+    greedy rows, 128 at T = 0.7, top_p = 0.9; four logits buffers rotated),
+    then the variants. Prints one JSON line of the times."""
+    import torch
+    import paged_kv_attention_scatter_amd as pkv
+    from workloads import config, draw_logits, draw_sampling_params, draw_uniforms
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1003)
+    cfg = config(3)
+    bs = cfg.rows
+    bufs = [torch.from_numpy(draw_logits(cfg).view(np.int16)).to(dev).view(torch.bfloat16)]
+    for _ in range(3):
+        bufs.append((torch.randn((bs, cfg.vocab), generator=gen, device=dev) * cfg.logit_sigma).to(torch.bfloat16))
+    T, K, P = pkv.prepare_sampling(*zip(*draw_sampling_params(cfg)), vocab=cfg.vocab)
+    to = lambda x: None if x is None else torch.from_numpy(x).to(dev)
+    d_T, d_K, d_P, d_u = to(T), to(K), to(P), to(draw_uniforms(cfg))
+    tokens = torch.empty(bs, dtype=torch.int32, device=dev)
+    ws = pkv.sample_workspace(bs, cfg.vocab, dev)
+    for i in range(args.warmup):
+        pkv.sample(bufs[i % 4], d_T, d_K, d_P, d_u, out=tokens, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        pkv.sample(bufs[i % 4], d_T, d_K, d_P, d_u, out=tokens, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"sampler decode256 mix: {us:.1f} us ({bs * cfg.vocab * 2 / us / 1e3:.0f} GB/s)")
+    res = {"sample_us": round(us, 2)}
+    res.update(bench_sampler_variants(torch, pkv, gen, dev, args))
+    print(json.dumps(res), flush=True)
 
 
 def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):

@@ -274,8 +274,13 @@ int pkv_paged_attention_decode_noalloc(const pkv_pool* pool, const void* q, int6
  *             E_r <= max_extend and sum(E) <= total_q, else the request is
  *             skipped and flagged.
  *   total_q, max_extend host bounds of sum(E_r) and max(E_r).
- *   ws        unused (may be NULL); ws_bytes may be 0.
- * bf16 only (the MFMA path); fp32 returns PKV_ERR_DTYPE.
+ *   ws        bf16 pools: unused (may be NULL, ws_bytes 0). fp32 pools: device
+ *             workspace of pkv_extend_workspace_size(bs, num_q_heads, total_q,
+ *             PKV_F32) bytes, 16-byte aligned (no initialisation needed).
+ * bf16 pools run the MFMA kernel. fp32 pools (an fp32 engine's prefill) run
+ * every query row as a decode row of C_r + t + 1 keys over the request's
+ * table row, through the decode kernels (fp32 throughout); total_q is then
+ * limited to 4096 rows (PKV_ERR_SHAPE above).
  */
 int pkv_paged_attention_extend(const pkv_pool* pool, const void* q, int64_t q_stride,
                                void* o, int64_t o_stride, int32_t bs, int32_t num_q_heads,
@@ -284,7 +289,10 @@ int pkv_paged_attention_extend(const pkv_pool* pool, const void* q, int64_t q_st
                                const int32_t* device_len, int64_t total_q, int32_t max_extend,
                                float sm_scale, void* ws, size_t ws_bytes, void* stream);
 
-size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_q);
+/* Workspace bytes of pkv_paged_attention_extend for a pool of `dtype`: 0 for
+ * PKV_BF16; for PKV_F32 the rows' decode lengths and a decode workspace (0 if
+ * total_q is outside [1, 4096]). */
+size_t pkv_extend_workspace_size(int32_t bs, int32_t num_q_heads, int64_t total_q, int32_t dtype);
 
 /* pkv_paged_attention_extend with the q prologue (qnr must not be NULL). */
 int pkv_paged_attention_extend_qnr(const pkv_pool* pool, const void* q, int64_t q_stride,

@@ -69,7 +69,7 @@ SIGNATURES = {
                                              c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
                                              c_void_p, c_void_p, c_int64, c_int32, c_float, c_void_p,
                                              c_size_t, c_void_p]),
-    "pkv_extend_workspace_size": (c_size_t, [c_int32, c_int32, c_int64]),
+    "pkv_extend_workspace_size": (c_size_t, [c_int32, c_int32, c_int64, c_int32]),
     "pkv_sample": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "pkv_sample_workspace_size": (c_size_t, [c_int32, c_int32]),

@@ -276,8 +276,9 @@ def paged_attention_decode_noalloc(q, k_pool, v_pool, page_table, cached_len, de
     return out
 
 
-def extend_workspace_size(bs: int, num_q_heads: int, total_q: int) -> int:
-    return int(lib().pkv_extend_workspace_size(bs, num_q_heads, total_q))
+def extend_workspace_size(bs: int, num_q_heads: int, total_q: int, dtype=PKV_BF16) -> int:
+    """Workspace bytes of an extend call on a pool of `dtype` (PKV_BF16 or PKV_F32 code)."""
+    return int(lib().pkv_extend_workspace_size(bs, num_q_heads, total_q, dtype))
 
 
 def paged_attention_extend(q, k_pool, v_pool, page_table, cached_len, device_len, *, max_extend: int,
@@ -304,7 +305,7 @@ def paged_attention_extend(q, k_pool, v_pool, page_table, cached_len, device_len
     _lengths(cached_len, "cached_len", bs)
     if table_idx is not None:
         _lengths(table_idx, "table_idx", bs)
-    ws = _workspace(extend_workspace_size(bs, hq, total_q), q.device, workspace)
+    ws = _workspace(extend_workspace_size(bs, hq, total_q, _dtype_code(k_pool)), q.device, workspace)
     qnr = _qnr(q_norm_weight, eps, rope_theta, k_pool.dtype)
     common = (byref(pool), q.data_ptr(), qs, out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts,
               _ptr(table_idx), cached_len.data_ptr(), device_len.data_ptr(), total_q, int(max_extend), sm_scale)

@@ -58,6 +58,9 @@ struct DecodeArgs {
   const void* q_w;      // [128] norm weight, element type T
   float q_eps;
   float inv_freq[64];   // fp32 rotary frequencies 1 / theta^(2j / 128)
+  // rows of device_len 0 are no rows at all (skipped without a fault, their
+  // output untouched): the padding of the extend rows run as decode rows
+  int32_t skip_empty;
 };
 
 template <typename T>
@@ -229,6 +232,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
     const int32_t s = a.device_len[r];
     const int32_t row = a.table_idx ? a.table_idx[r] : r;
     const bool row_ok = row >= 0 && row < a.pt_rows;
+    if (a.skip_empty && s == 0) return 0;
     const bool len_ok = s >= 1 && (int64_t)s <= a.pt_stride;
     if (report && !row_ok) raise_fault(a.faults, 0x8u);
     if (report && !len_ok) raise_fault(a.faults, 0x2u);
@@ -409,7 +413,7 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeA
   T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride + (int64_t)h * kHeadDim;
   const int t = threadIdx.x, grp = t >> 4, d0 = (t & 15) * 8;
   if (c1 == c0) {  // invalid request: skipped by the main kernel
-    if (t < kHeadDim) store_out<T>(ob + t, 0.f);
+    if (t < kHeadDim && !(a.skip_empty && a.device_len[r] == 0)) store_out<T>(ob + t, 0.f);
     return;
   }
   const int P = decode_num_items(total, a.num_items);
@@ -463,6 +467,59 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeA
     }
     store_out<T>(ob + t, L > 0.f ? Ad / L : 0.f);
   }
+}
+
+// Extend rows as decode rows (the fp32 extend path): query row t of request
+// r attends to keys 0 .. C_r + t, exactly a decode row of C_r + t + 1 keys
+// over the request's table row ("第 0 步" dense attention with its causal
+// mask; "Mini-SGLang 完整剖析" section 4.6.5 for the ragged row order). For
+// every ragged row v < total_q: vlen[v] = C_r + t + 1 and vrow[v] = the
+// request's table row, or vlen[v] = 0 for rows past the batch's and for the
+// rows of an invalid request. The ragged offsets, checks and fault bits are
+// the extend kernel's: a request owns max(S - C, 0) rows whatever else is
+// wrong with it. Each workgroup scans the requests' extend lengths itself.
+constexpr int kExpandThreads = 256;
+
+__global__ void __launch_bounds__(kExpandThreads) extend_rows_kernel(
+    const int32_t* cached_len, const int32_t* device_len, const int32_t* table_idx, int32_t bs, int32_t pt_rows,
+    int64_t pt_stride, int32_t max_extend, int64_t total_q, int32_t* vlen, int32_t* vrow, uint32_t* faults) {
+  extern __shared__ int32_t cu[];  // [bs + 1]
+  const bool report = blockIdx.x == 0;
+  auto valid = [&](int r, int32_t* row) {
+    const int32_t C = cached_len[r], S = device_len[r];
+    *row = table_idx ? table_idx[r] : r;
+    const bool len_ok = C >= 0 && C < S && (int64_t)S <= pt_stride && S - C <= max_extend;
+    const bool row_ok = *row >= 0 && *row < pt_rows;
+    return (len_ok ? 0u : 0x2u) | (row_ok ? 0u : 0x8u);
+  };
+  block_exclusive_scan<kExpandThreads>(cu, bs, [&](int r) -> int32_t {
+    const int32_t C = cached_len[r], S = device_len[r];
+    if (report) {
+      int32_t row;
+      const uint32_t bad = valid(r, &row);
+      if (bad) raise_fault(faults, (bad & 0x8u) ? 0x8u : 0x2u);
+    }
+    return S > C ? S - C : 0;
+  });
+  const int64_t v = (int64_t)blockIdx.x * kExpandThreads + threadIdx.x;
+  if (report && threadIdx.x == 0 && (int64_t)cu[bs] > total_q) raise_fault(faults, 0x10u);
+  if (v >= total_q) return;
+  int32_t len = 0, trow = 0;
+  if (v < cu[bs]) {
+    int lo = 0, hi = bs;  // cu[lo] <= v < cu[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= v) lo = mid; else hi = mid;
+    }
+    const int r = lo;
+    int32_t row;
+    if (!valid(r, &row) && (int64_t)cu[r + 1] <= total_q) {  // a request whose rows do not all fit is skipped
+      len = cached_len[r] + (int32_t)(v - cu[r]) + 1;
+      trow = row;
+    }
+  }
+  vlen[v] = len;
+  vrow[v] = trow;
 }
 
 }  // namespace pkv

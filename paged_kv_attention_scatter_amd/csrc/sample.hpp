@@ -982,6 +982,7 @@ struct SampleWs {
   uint2* meta;         // fp32: [bs * S]: (list floor key, list length)
 };
 
+
 // First of NB bins (ascending) whose running amount reaches goal, by one
 // wave (NB / 64 consecutive bins per lane): *bin = -1 if none, *before = the
 // amount strictly before it, *cnt = count(bin). No barriers.
@@ -1032,6 +1033,13 @@ PKV_INLINE void wave_select_bins(AF amount, CF count, double goal, int* bin, dou
   *cnt = (uint32_t)lane_i32((int32_t)c, l0);
 }
 
+struct SliceLds {
+  uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
+  double wmass[kSliceWaves];
+  uint32_t wave_k[kSliceWaves];
+  int32_t wave_i[kSliceWaves];
+};
+
 // Slice kernel: workgroup b reads slice b / bs of row b % bs (rows vary
 // fastest, so greedy and sampled rows share every CU). Thread t holds
 // chunks t, t + 256, t + 512, t + 768 of the slice. The tokens become biased
@@ -1039,13 +1047,12 @@ PKV_INLINE void wave_select_bins(AF amount, CF count, double goal, int* bin, dou
 // mass relative to its maximum (SampleParams::need_mass) and a count
 // histogram of the keys within 255 of its maximum (bin d = kmax - key;
 // SampleParams::need_cut).
-__global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs a, SampleWs ws) {
-  __shared__ uint32_t hist[kHistBins + kWave];  // + one discard bin per lane
-  __shared__ double wmass[kSliceWaves];
-  __shared__ uint32_t wave_k[kSliceWaves];
-  __shared__ int32_t wave_i[kSliceWaves];
+PKV_INLINE void slice_phase(const SampleArgs& a, const SampleWs& ws, int row, int slice, SliceLds& L) {
+  uint32_t* hist = L.hist;
+  double* wmass = L.wmass;
+  uint32_t* wave_k = L.wave_k;
+  int32_t* wave_i = L.wave_i;
   const int V = a.vocab, S = sample_slices(V);
-  const int row = blockIdx.x % a.bs, slice = blockIdx.x / a.bs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row, V);
@@ -1191,6 +1198,23 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
   }
 }
 
+__global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs a, SampleWs ws) {
+  __shared__ SliceLds L;
+  slice_phase(a, ws, blockIdx.x % a.bs, blockIdx.x / a.bs, L);
+}
+
+template <int NW, int MS>
+struct FinishLds {
+  int32_t sl_delta[MS];
+  double sl_mass[MS];
+  int32_t sl_cut[MS];
+  int32_t h_i[8];
+  double h_f[4];
+  int32_t w_cnt[NW];
+  double w_mass[NW];
+  int32_t w_last[NW];
+};
+
 // Finish kernel: one workgroup per row. The row maximum is the largest
 // slice maximum, so every slice histogram is the row histogram's bins
 // d >= kmax_row - kmax_slice. All tokens of a bin share one key and one
@@ -1202,18 +1226,21 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 // [8t, 8t + 8)). Cuts below the window take the generic path over the
 // row in memory. Per-slice and per-row steps run in wave 0 on DPP scans;
 // the workgroup meets at eight barriers (four for plain rows).
-__global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArgs a, SampleWs ws) {
-  __shared__ SampleLds<kFinishWaves> s;
-  __shared__ int32_t sl_delta[kMaxSlices];
-  __shared__ double sl_mass[kMaxSlices];
-  __shared__ int32_t sl_cut[kMaxSlices];
-  __shared__ int32_t h_i[8];
-  __shared__ double h_f[4];
-  __shared__ int32_t w_cnt[kFinishWaves];
-  __shared__ double w_mass[kFinishWaves];
-  __shared__ int32_t w_last[kFinishWaves];
+template <int NT, int MS>
+PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, SampleLds<NT / kWave>& s,
+                           FinishLds<NT / kWave, MS>& f) {
+  constexpr int NW = NT / kWave;
+  constexpr int DC = kSliceTokens / (8 * NT);  // draw: 16-byte chunks per thread
+  static_assert(DC >= 1 && MS <= NT && MS <= 2 * kWave, "a slice per thread; two slices per lane of wave 0");
+  int32_t* sl_delta = f.sl_delta;
+  double* sl_mass = f.sl_mass;
+  int32_t* sl_cut = f.sl_cut;
+  int32_t* h_i = f.h_i;
+  double* h_f = f.h_f;
+  int32_t* w_cnt = f.w_cnt;
+  double* w_mass = f.w_mass;
+  int32_t* w_last = f.w_last;
   const int V = a.vocab, S = sample_slices(V);
-  const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   SampleParams sp;
   sp.load(a, row, V);
@@ -1230,12 +1257,12 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   // q / 32; thread t takes units t + 1024e.
   const u32x4* hrow = reinterpret_cast<const u32x4*>(ws.hists + slot0 * kHistWords);
   const int NU = S * kHistUnits;
-  constexpr int kU = kMaxSlices * kHistUnits / kFinishThreads;  // 4 units per thread at most
+  constexpr int kU = MS * kHistUnits / NT;  // 4 units per thread at most
   u32x4 v[kU];
   if (!sp.greedy && !plain)
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
-      const int q = e * kFinishThreads + tid;
+      const int q = e * NT + tid;
       v[e] = q < NU ? hrow[q] : u32x4{0u, 0u, 0u, 0u};
     }
 
@@ -1245,7 +1272,8 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   double wall = 0.0;  // (wave 0) mass of the whole row: plain rows and top-p without top-k
   if (wave == 0) {
     const bool in0 = lane < S, in1 = lane + 64 < S;
-    const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull, r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
+    const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull;
+    const uint64_t r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
     const int32_t k0 = (int32_t)(uint32_t)r0, k1 = (int32_t)(uint32_t)r1;
     const int32_t mk = wave_max_i32(max(k0, k1));
     const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
@@ -1293,8 +1321,8 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     // ---- the row histogram
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
-      const int q = e * kFinishThreads + tid;
-      if (e * kFinishThreads < NU && q < NU) {
+      const int q = e * NT + tid;
+      if (e * NT < NU && q < NU) {
         const int b0 = 8 * (q % kHistUnits) + sl_delta[q / kHistUnits];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -1372,7 +1400,7 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     dcut = h_i[3];
     take = (uint32_t)h_i[4];
     if (dcut < 0) {  // the cut lies below the window
-      SampleRow<bf16_t, kFinishWaves> mrow;
+      SampleRow<bf16_t, NW> mrow;
       mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
       const int32_t idx = sample_generic(mrow, s, sp, lmax);
       if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
@@ -1385,10 +1413,10 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     // (relative error below 1e-6 of the slice's kept mass).
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
-      if (e * kFinishThreads < NU) {  // uniform
-        const int q = e * kFinishThreads + tid;
+      if (e * NT < NU) {  // uniform
+        const int q = e * NT + tid;
         const int sl = q / kHistUnits;
-        const int b0 = q < NU ? 8 * (q % kHistUnits) + sl_delta[min(sl, kMaxSlices - 1)] : kHistBins;
+        const int b0 = q < NU ? 8 * (q % kHistUnits) + sl_delta[min(sl, MS - 1)] : kHistBins;
         float m = 0.f, cc = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -1464,13 +1492,13 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   const int32_t tie_base = h_i[5];
 
   // ---- the draw inside slice psl: thread t scans tokens [8t, 8t + 8), in index order
-  const int tok0 = psl * kSliceTokens + 8 * kDrawChunks * tid;
+  const int tok0 = psl * kSliceTokens + 8 * DC * tid;
   const uint32_t cut_key = rkmax - (uint32_t)max(dcut, 0);
-  u32x4 x[kDrawChunks];
+  u32x4 x[DC];
 #pragma unroll
-  for (int i = 0; i < kDrawChunks; ++i) x[i] = crow[min(tok0 / 8 + i, last_chunk)];  // clamped: stays in the row
+  for (int i = 0; i < DC; ++i) x[i] = crow[min(tok0 / 8 + i, last_chunk)];  // clamped: stays in the row
 #pragma unroll
-  for (int i = 0; i < kDrawChunks; ++i)
+  for (int i = 0; i < DC; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // biased keys; key 0 (below every real key) at or past V
       const int tok = tok0 + 8 * i + 2 * j;
@@ -1483,7 +1511,7 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   if (!plain) {
     int32_t n = 0;
 #pragma unroll
-    for (int i = 0; i < kDrawChunks; ++i)
+    for (int i = 0; i < DC; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) n += ((x[i][j] & 0xffffu) == cut_key) + ((x[i][j] >> 16) == cut_key);
     const int32_t inc = wave_incl_scan_i32(n, lane);
@@ -1501,19 +1529,18 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
     const uint32_t vw = bf16x2_from_keys(kw);
     return row_weight(__uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16)), lmax, c2);
   };
-  float kw[kDrawChunks][8];  // kept weights of this thread's tokens
-  double own = 0.0;
+  double own = 0.0;  // kept mass of this thread's tokens (fp32 per chunk)
   int32_t lastk = -1;
   {
     int32_t rank = rank0;
 #pragma unroll
-    for (int i = 0; i < kDrawChunks; ++i) {
+    for (int i = 0; i < DC; ++i) {
       float cs = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        kw[i][e] = kept_w(x[i], e, rank);
-        if (kw[i][e] > 0.f) lastk = tok0 + 8 * i + e;
-        cs += kw[i][e];
+        const float w = kept_w(x[i], e, rank);
+        if (w > 0.f) lastk = tok0 + 8 * i + e;
+        cs += w;
       }
       own += (double)cs;
     }
@@ -1530,27 +1557,36 @@ __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArg
   __syncthreads();  // 7
   double offm = 0.0;
   int32_t lk = -1;  // the slice's last kept token
-  for (int w = 0; w < kFinishWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) offm += w_mass[w];
     lk = max(lk, w_last[w]);
   }
   const double excl = offm + exw, incl = offm + inw;
   if (own > 0.0 && excl <= rem && rem < incl) {  // exactly one thread: the intervals meet bit for bit
-    int32_t res = -1;
+    int32_t res = -1, rank = rank0;
     double run = excl;
 #pragma unroll
-    for (int i = 0; i < kDrawChunks; ++i)
+    for (int i = 0; i < DC; ++i) {
+      float cs = 0.f;  // the chunk's sum as above, so the thread's total is reached bit for bit
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (res < 0 && kw[i][e] > 0.f) {
-          run += (double)kw[i][e];
-          if (run > rem) res = tok0 + 8 * i + e;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float w = kept_w(x[i], e, rank);  // the same weights again (the tie ranks replay too)
+        if (res < 0 && w > 0.f && run + (double)(cs + w) > rem) res = tok0 + 8 * i + e;
+        cs += w;
+      }
+      run += (double)cs;
+    }
     s.result = res >= 0 ? res : lastk;  // rounding ran past the thread's tokens: its last kept one
   }
   __syncthreads();  // 8
   const int32_t r = s.result >= 0 ? s.result : lk;
   if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
+}
+
+__global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArgs a, SampleWs ws) {
+  __shared__ SampleLds<kFinishWaves> s;
+  __shared__ FinishLds<kFinishWaves, kMaxSlices> f;
+  finish_row<kFinishThreads, kMaxSlices>(a, ws, blockIdx.x, s, f);
 }
 
 // ---------------------------------------------------------------- fp32: slice kernel + finish kernel

@@ -221,7 +221,10 @@ def _extend(L, pool, bs=2, hq=16, q=0x60000, o=0x70000, pt=0x80000, cl=0x88000, 
 
 
 @pytest.mark.parametrize("pool,kw,status", [
-    (dict(dtype=0), {}, -2), (dict(), dict(hq=12), -3), (dict(), dict(q=None), -1), (dict(), dict(o=0x70002), -5),
+    (dict(dtype=0), {}, -6),                       # fp32: the decode-row path needs its workspace
+    (dict(dtype=0), dict(total_q=5000), -3),       # fp32: at most 4096 rows
+    (dict(dtype=0), dict(cl=None), -1), (dict(dtype=3), {}, -2),
+    (dict(), dict(hq=12), -3), (dict(), dict(q=None), -1), (dict(), dict(o=0x70002), -5),
     (dict(), dict(cl=None), -1), (dict(), dict(max_e=0), -4), (dict(), dict(rows=0), -3),
     (dict(), dict(bs=1 << 28, max_e=8), -3),
 ])
@@ -232,3 +235,19 @@ def test_extend_argument_errors(L, pool, kw, status):
 
 def test_extend_empty_batch_is_noop(L):
     assert _extend(L, _pool(), bs=0) == 0 and _extend(L, _pool(), total_q=0) == 0
+
+
+def test_extend_workspace_size(L):
+    """bf16 extend needs no workspace; fp32 extend needs the rows' decode
+    lengths and a decode workspace, growing with total_q, up to 4096 rows."""
+    assert L.pkv_extend_workspace_size(8, 16, 20000, 1) == 0
+    a, b = L.pkv_extend_workspace_size(2, 16, 10, 0), L.pkv_extend_workspace_size(2, 16, 4096, 0)
+    assert 0 < a < b
+    assert L.pkv_extend_workspace_size(2, 16, 4097, 0) == 0
+
+
+def test_qk_norm_rope_store_k_side_only_validates(L):
+    """q = q_out = NULL is the k-side-only call: q's arguments are not
+    checked (num_q_heads 0, no q weight), the k side still is."""
+    assert _qkr(L, _pool(), q=None, qo=None, hq=0, wq=None, ks=512) == -3
+    assert _qkr(L, _pool(), q=None, qo=None, hq=0, wq=None, wk=None) == -1

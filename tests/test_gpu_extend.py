@@ -235,3 +235,61 @@ def test_extend_mixed_batch_chunks_full_size():
     print(f"  {got.shape[0]} rows: max|d|={mx:.3e} relL2={rel:.3e}", flush=True)
     worst = np.max(np.abs(oracle.widen(got, "bf16") - refs), axis=(1, 2))
     assert np.all(worst <= 2e-2)
+
+
+# ---------------------------------------------------------------- fp32 pools (rows as decode rows)
+
+@pytest.mark.parametrize("name,C,E,hkv,g", [
+    ("f32_small", [5, 0, 37], [4, 9, 30], 8, 2),
+    ("f32_one_row_each", [16, 1, 2], [1, 1, 1], 8, 2),
+    ("f32_long", [300, 0], [250, 700], 4, 2),
+    ("f32_mha", [9, 33], [17, 5], 8, 1),
+])
+def test_extend_fp32_matches_oracle(name, C, E, hkv, g):
+    """fp32 pools: every query row runs as a decode row of C + t + 1 keys (fp32
+    throughout); max-abs 1e-5 against the oracle on every row. total_q one
+    larger than the rows: the extra output row stays untouched."""
+    c = _make(zlib.crc32(name.encode()) % 1000, C, E, HKV=hkv, G=g)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    n = int(c["E"].sum())
+    kv = rng.standard_normal(c["kv"].shape, dtype=np.float32)
+    q = rng.standard_normal((n + 1, c["HQ"], 128), dtype=np.float32)
+    out = torch.full((n + 1, c["HQ"], 128), 7.0, dtype=torch.float32, device="cuda")
+    print(f"extend fp32 case {name}", flush=True)
+    o = pkv.paged_attention_extend(to_dev(q), to_dev(kv[0]), to_dev(kv[1]), to_dev(c["table"]), to_dev(c["C"]),
+                                   to_dev(c["S"]), max_extend=int(c["E"].max()), out=out)
+    torch.cuda.synchronize()
+    got = to_host(o)
+    assert np.all(got[n] == 7.0), "the row past the batch's rows was written"
+    ref = oracle.attention_extend(q[:n], kv[0], kv[1], c["table"], c["C"], c["S"], "f32")
+    mx, _ = check_attention(got[:n], ref, "f32", name)
+    print(f"  {n} rows: max|d|={mx:.3e}", flush=True)
+    assert pkv.read_faults() == 0
+
+
+def test_extend_fp32_invalid_request_is_skipped():
+    """A request with cached_len >= device_len is skipped and flagged; the
+    other requests' rows are still computed."""
+    c = _make(71, [3, 4, 10], [5, 6, 7])
+    rng = np.random.default_rng(71)
+    kv = rng.standard_normal(c["kv"].shape, dtype=np.float32)
+    n = int(c["E"].sum())
+    q = rng.standard_normal((n, c["HQ"], 128), dtype=np.float32)
+    C_bad = c["C"].copy()
+    C_bad[1] = c["S"][1]                                   # E = 0 and C == S: invalid
+    out = torch.full((n, c["HQ"], 128), 7.0, dtype=torch.float32, device="cuda")
+    print("extend fp32 invalid request", flush=True)
+    pkv.paged_attention_extend(to_dev(q), to_dev(kv[0]), to_dev(kv[1]), to_dev(c["table"]), to_dev(C_bad),
+                               to_dev(c["S"]), max_extend=7, out=out)
+    torch.cuda.synchronize()
+    assert pkv.read_faults() & 0x2
+    got = to_host(out)
+    # request 1 has no rows now; request 2's rows follow request 0's directly
+    E0, E2 = int(c["E"][0]), int(c["E"][2])
+    C2 = np.array([c["C"][0], c["C"][2]], np.int32)
+    S2 = np.array([c["S"][0], c["S"][2]], np.int32)
+    tab2 = c["table"][[0, 2]]
+    q2 = np.concatenate([q[:E0], q[E0:E0 + E2]])
+    ref = oracle.attention_extend(q2, kv[0], kv[1], tab2, C2, S2, "f32")
+    check_attention(got[:E0 + E2], ref, "f32", "fp32 extend around an invalid request")
+    assert np.all(got[E0 + E2:] == 7.0)
