@@ -8,7 +8,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# PKV_LIB_PATH selects another build of the same library (the sanitizer
+# build of the host code, for instance).
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK = 0
 STATUS_NAMES = {
