@@ -15,8 +15,9 @@
 // element fetched serves 128 positions x 2 heads (256 FLOP per byte).
 // The grid is one-dimensional: the KV head is the fastest index (so with 8
 // KV heads each XCD serves one head), then the query blocks of one request
-// from the longest down, then the request -- so the workgroups that run at
-// the same time on an XCD share one request's K/V rows in its L2.
+// from the longest down, then the requests from the most work down -- so the
+// workgroups that run at the same time on an XCD share one request's K/V
+// rows in its L2, and the longest requests do not start last.
 //
 // MFMA layout (v_mfma_f32_16x16x32_bf16): the kernel computes S^T = K . Q^T,
 // so each lane's four accumulators belong to ONE query (lane % 16) and four
@@ -118,7 +119,29 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   const int rest = id / a.kv_heads;
   const int qb = nqb - 1 - rest % nqb;         // longest blocks of a request first
   const int hp = (rest / nqb) % a.head_pairs;
-  const int r = rest / (nqb * a.head_pairs);
+  // Requests in order of their work, the largest first (each request's
+  // blocks stay together, so they share its K/V rows in L2): grid position
+  // rk is the request of rank rk by causal pairs E (2C + E + 1), ties by
+  // index; batches above one request per thread keep the index order.
+  const int rk = rest / (nqb * a.head_pairs);
+  int r = rk;
+  if (a.bs <= kExtThreads) {  // uniform
+    __shared__ int64_t req_cost[kExtThreads];
+    __shared__ int32_t sh_req;
+    if (tid < a.bs) {
+      const int64_t ci = a.cached_len[tid], si = a.device_len[tid];
+      req_cost[tid] = si > ci ? (si - ci) * (2 * ci + (si - ci) + 1) : 0;
+    }
+    __syncthreads();
+    if (tid < a.bs) {
+      const int64_t mine = req_cost[tid];
+      int rank = 0;
+      for (int j = 0; j < a.bs; ++j) rank += (req_cost[j] > mine) || (req_cost[j] == mine && j < tid);
+      if (rank == rk) sh_req = tid;
+    }
+    __syncthreads();
+    r = sh_req;
+  }
 
   const int32_t C = a.cached_len[r], S = a.device_len[r];
   const int32_t row = a.table_idx ? a.table_idx[r] : r;
