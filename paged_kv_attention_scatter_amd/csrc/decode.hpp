@@ -395,17 +395,20 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 
 // Merge the partials of every request that was cut by item boundaries; zero
 // the output of requests whose lengths were invalid. One workgroup per
-// (request, query head), 512 threads: thread t takes the request's items
-// i0 + g, i0 + g + 32, ... (g = t / 16) for dims [8 (t % 16), 8 (t % 16) + 8)
-// and merges them online (four items' loads in flight per step); the 32 item
+// (request, query head) of NT threads: thread t takes the request's items
+// i0 + g, i0 + g + NT/16, ... (g = t / 16) for dims [8 (t % 16), 8 (t % 16) + 8)
+// and merges them online (four items' loads in flight per step); the item
 // groups then meet in LDS. A request cut into many items (small batches use
-// small items) costs a few memory round trips, not one per item.
-constexpr int kCombineThreads = 512;
+// small items) costs a few memory round trips, not one per item; a large
+// batch, whose requests span a handful of items each, takes the narrow form
+// so that idle groups cost no LDS round.
+constexpr int kCombineThreads = 512;      // wide form: 32 item groups
+constexpr int kCombineThreadsNarrow = 64;  // narrow form: 4 item groups
 
-template <typename T, int HQ>
-__global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeArgs a) {
-  constexpr int kGroups = kCombineThreads / 16;  // item groups
-  constexpr int kU = 4;                          // items in flight per thread per step
+template <typename T, int HQ, int NT>
+__global__ void __launch_bounds__(NT) decode_combine_kernel(DecodeArgs a) {
+  constexpr int kGroups = NT / 16;  // item groups
+  constexpr int kU = 4;             // items in flight per thread per step
   const int r = blockIdx.x, h = blockIdx.y;
   const int32_t* cu = a.cu_out;
   const int64_t total = cu[a.bs];
@@ -413,7 +416,8 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeA
   T* ob = reinterpret_cast<T*>(a.o) + (int64_t)r * a.o_stride + (int64_t)h * kHeadDim;
   const int t = threadIdx.x, grp = t >> 4, d0 = (t & 15) * 8;
   if (c1 == c0) {  // invalid request: skipped by the main kernel
-    if (t < kHeadDim && !(a.skip_empty && a.device_len[r] == 0)) store_out<T>(ob + t, 0.f);
+    if (!(a.skip_empty && a.device_len[r] == 0))
+      for (int d = t; d < kHeadDim; d += NT) store_out<T>(ob + d, 0.f);
     return;
   }
   const int P = decode_num_items(total, a.num_items);
@@ -454,7 +458,7 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeA
 #pragma unroll
   for (int e = 0; e < 8; ++e) sm_a[grp][d0 + e] = A[e];
   __syncthreads();
-  if (t < kHeadDim) {
+  for (int d = t; d < kHeadDim; d += NT) {
     float M = -INFINITY;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) M = fmaxf(M, sm_m[g]);
@@ -463,9 +467,9 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeA
     for (int g = 0; g < kGroups; ++g) {
       const float c = sm_m[g] == -INFINITY ? 0.f : fast_exp2(sm_m[g] - M);
       L += sm_l[g] * c;
-      Ad += sm_a[g][t] * c;
+      Ad += sm_a[g][d] * c;
     }
-    store_out<T>(ob + t, L > 0.f ? Ad / L : 0.f);
+    store_out<T>(ob + d, L > 0.f ? Ad / L : 0.f);
   }
 }
 
