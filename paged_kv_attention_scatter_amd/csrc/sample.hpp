@@ -1205,14 +1205,11 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 
 template <int NW, int MS>
 struct FinishLds {
-  int32_t sl_delta[MS];
-  double sl_mass[MS];
-  int32_t sl_cut[MS];
-  int32_t h_i[8];
-  double h_f[4];
-  int32_t w_cnt[NW];
-  double w_mass[NW];
-  int32_t w_last[NW];
+  double sl_mass[MS];   // kept mass of every slice (cut bin excluded)
+  int32_t sl_cut[MS];   // tokens of every slice in the cut bin
+  double w_above[NW];   // draw: mass of each wave's tokens above the cut
+  int32_t w_ties[NW];   // draw: each wave's tokens in the cut bin
+  int32_t cut_bin, cut_take;
 };
 
 // Finish kernel: one workgroup per row. The row maximum is the largest
@@ -1222,31 +1219,24 @@ struct FinishLds {
 // weights; the ties at the cut keep the first n equal-key tokens in index
 // order, which fixes every slice's kept mass without reading a token. The
 // draw (kept weights in index order, first running mass > u * W) picks one
-// slice by those masses and scans its 8192 tokens (thread t: tokens
-// [8t, 8t + 8)). Cuts below the window take the generic path over the
-// row in memory. Per-slice and per-row steps run in wave 0 on DPP scans;
-// the workgroup meets at eight barriers (four for plain rows).
+// slice by those masses, then one wave of it by the waves' kept masses, then
+// one thread of that wave and one of its 8 tokens. Cuts below the window
+// take the generic path over the row in memory.
+//
+// Every wave reads the slice records and works out the row maximum and the
+// slice holding the draw itself (the same data, the same operations, so the
+// same results in every wave); wave 0 alone takes the cuts. The workgroup
+// meets at five barriers (the zeroed histogram, the row histogram, the cuts,
+// the slices' kept masses, the waves' draw masses), one for plain rows.
 template <int NT, int MS>
 PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, SampleLds<NT / kWave>& s,
                            FinishLds<NT / kWave, MS>& f) {
   constexpr int NW = NT / kWave;
   constexpr int DC = kSliceTokens / (8 * NT);  // draw: 16-byte chunks per thread
-  static_assert(DC >= 1 && MS <= NT && MS <= 2 * kWave, "a slice per thread; two slices per lane of wave 0");
-  int32_t* sl_delta = f.sl_delta;
-  double* sl_mass = f.sl_mass;
-  int32_t* sl_cut = f.sl_cut;
-  int32_t* h_i = f.h_i;
-  double* h_f = f.h_f;
-  int32_t* w_cnt = f.w_cnt;
-  double* w_mass = f.w_mass;
-  int32_t* w_last = f.w_last;
+  static_assert(DC >= 1 && MS <= NT && MS <= 2 * kWave && NW <= kWave,
+                "a slice per thread; two slices per lane; one wave per lane");
   const int V = a.vocab, S = sample_slices(V);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  SampleParams sp;
-  sp.load(a, row, V);
-  const bool need_mass = sp.need_mass();
-  const bool plain = sp.plain();
-  const float c2 = sp.c2;
   const u32x4* crow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.logits) +
                                                      (int64_t)row * a.row_stride);
   const int last_chunk = (V - 1) / 8;
@@ -1254,76 +1244,88 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
 
   // The slices' histograms as 16-byte units, loaded first (their addresses
   // need nothing else): unit q holds bins [8u, 8u + 8) (u = q % 32) of slice
-  // q / 32; thread t takes units t + 1024e.
+  // q / 32; thread t takes units t + NT e.
   const u32x4* hrow = reinterpret_cast<const u32x4*>(ws.hists + slot0 * kHistWords);
   const int NU = S * kHistUnits;
   constexpr int kU = MS * kHistUnits / NT;  // 4 units per thread at most
+  // (issued before the row's parameters arrive; a greedy or plain row's
+  // workspace holds stale histograms and masses, read but never used)
   u32x4 v[kU];
-  if (!sp.greedy && !plain)
 #pragma unroll
-    for (int e = 0; e < kU; ++e) {
-      const int q = e * NT + tid;
-      v[e] = q < NU ? hrow[q] : u32x4{0u, 0u, 0u, 0u};
-    }
-
-  // ---- slice records (wave 0; lane l holds slices l and l + 64): row
-  // maximum, its first index, slice offsets, slice masses in units of the
-  // row maximum, the window weights.
-  double wall = 0.0;  // (wave 0) mass of the whole row: plain rows and top-p without top-k
-  if (wave == 0) {
-    const bool in0 = lane < S, in1 = lane + 64 < S;
-    const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull;
-    const uint64_t r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
-    const int32_t k0 = (int32_t)(uint32_t)r0, k1 = (int32_t)(uint32_t)r1;
-    const int32_t mk = wave_max_i32(max(k0, k1));
-    const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
-                                        (in1 && k1 == mk) ? (int32_t)(r1 >> 32) : 0x7fffffff));
-    const int32_t argmax = am == 0x7fffffff ? 0 : am;  // slices are in index order
-    if (sp.greedy) {
-      if (lane == 0) a.out[row] = argmax;
-    } else {
-      const uint32_t rkmax = (uint32_t)mk;
-      const float lmax = key16_value(rkmax);
-      if (in0) sl_delta[lane] = mk - k0;
-      if (in1) sl_delta[lane + 64] = mk - k1;
-      double m0 = 0.0, m1 = 0.0;
-      if (need_mass) {
-        if (in0) m0 = ws.masses[slot0 + lane] * (double)fast_exp2((fmaxf(key16_value((uint32_t)k0), -1e30f) - lmax) * c2);
-        if (in1) m1 = ws.masses[slot0 + lane + 64] * (double)fast_exp2((fmaxf(key16_value((uint32_t)k1), -1e30f) - lmax) * c2);
-        wall = wave_sum_f64(m0 + m1);
-      }
-      if (plain) {
-        sl_mass[lane] = m0;
-        sl_mass[lane + 64] = m1;
-      } else {
-#pragma unroll
-        for (int e = 0; e < kHistBins / kWave; ++e) {
-          const int b = e * kWave + lane;
-          s.hist[b] = 0;
-          s.wtab[b] = (uint32_t)b <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)b), lmax, c2) : 0.f;
-        }
-      }
-      if (lane == 0) {
-        h_i[0] = mk;
-        h_i[1] = argmax;
-      }
-    }
+  for (int e = 0; e < kU; ++e) {
+    const int q = e * NT + tid;
+    v[e] = q < NU ? hrow[q] : u32x4{0u, 0u, 0u, 0u};
   }
-  if (sp.greedy) return;
-  __syncthreads();  // 1
-  const uint32_t rkmax = (uint32_t)h_i[0];
-  const int32_t argmax = h_i[1];
-  const float lmax = key16_value(rkmax);
-
-  int dcut = -1;      // cut bin (rows with top-k or top-p); tokens with d < dcut are kept
-  uint32_t take = 0;  // tokens of bin dcut kept: the first ones in index order
+  // slice records (every wave; lane l holds slices l and l + 64) and masses
+  const bool in0 = lane < S, in1 = lane + 64 < S;
+  const uint64_t r0 = in0 ? ws.recs[slot0 + lane] : 0ull;
+  const uint64_t r1 = in1 ? ws.recs[slot0 + lane + 64] : 0ull;
+  const double mr0 = in0 ? ws.masses[slot0 + lane] : 0.0;  // relative to the slice maxima
+  const double mr1 = in1 ? ws.masses[slot0 + lane + 64] : 0.0;
+  SampleParams sp;
+  sp.load(a, row, V);
+  const bool need_mass = sp.need_mass();
+  const bool plain = sp.plain();
+  const float c2 = sp.c2;
+  if (sp.greedy) {
+    if (wave == 0) {
+      const int32_t k0 = (int32_t)(uint32_t)r0, k1 = (int32_t)(uint32_t)r1;
+      const int32_t mk = wave_max_i32(max(k0, k1));
+      const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
+                                          (in1 && k1 == mk) ? (int32_t)(r1 >> 32) : 0x7fffffff));
+      if (lane == 0) a.out[row] = am == 0x7fffffff ? 0 : am;  // slices are in index order
+    }
+    return;
+  }
   if (!plain) {
-    // ---- the row histogram
+    for (int b = tid; b < kHistBins; b += NT) s.hist[b] = 0;
+    __syncthreads();  // A: the row histogram starts at zero (the loads above are still in flight)
+  }
+
+  // ---- row maximum, its first index, slice distances below it, slice
+  // masses in units of the row maximum
+  const int32_t k0 = (int32_t)(uint32_t)r0, k1 = (int32_t)(uint32_t)r1;
+  const int32_t mk = wave_max_i32(max(k0, k1));
+  const int32_t am = wave_min_i32(min((in0 && k0 == mk) ? (int32_t)(r0 >> 32) : 0x7fffffff,
+                                      (in1 && k1 == mk) ? (int32_t)(r1 >> 32) : 0x7fffffff));
+  const int32_t argmax = am == 0x7fffffff ? 0 : am;
+  const uint32_t rkmax = (uint32_t)mk;
+  const float lmax = key16_value(rkmax);
+  const int32_t dl0 = mk - k0, dl1 = mk - k1;
+  double m0 = 0.0, m1 = 0.0, wall = 0.0;  // wall: mass of the whole row (plain rows, top-p without top-k)
+  if (need_mass) {
+    if (in0) m0 = mr0 * (double)fast_exp2((fmaxf(key16_value((uint32_t)k0), -1e30f) - lmax) * c2);
+    if (in1) m1 = mr1 * (double)fast_exp2((fmaxf(key16_value((uint32_t)k1), -1e30f) - lmax) * c2);
+    wall = wave_sum_f64(m0 + m1);
+  }
+
+  int dcut = -1;      // cut bin (rows with a cut); tokens with d < dcut are kept
+  uint32_t take = 0;  // tokens of bin dcut kept: the first ones in index order
+  double wcut = 0.0;  // their weight
+  double msl0, msl1;  // kept mass of slices lane and lane + 64 (cut bin excluded)
+  int32_t cc0 = 0, cc1 = 0;  // their tokens in the cut bin
+  if (plain) {
+    msl0 = m0;
+    msl1 = m1;
+  } else {
+    // distance of each unit's slice below the row maximum (from the lane
+    // that holds the slice)
+    int32_t ud[kU];
+#pragma unroll
+    for (int e = 0; e < kU; ++e) {
+      ud[e] = 0;
+      if (e * NT + wave * kWave < NU) {  // wave-uniform: waves past the units skip
+        const int sl = min((e * NT + tid) / kHistUnits, MS - 1);
+        const int32_t a0 = __shfl(dl0, sl & 63), a1 = __shfl(dl1, sl & 63);
+        ud[e] = sl < 64 ? a0 : a1;
+      }
+    }
+    // ---- the row histogram; wave 0 writes the window weights
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
       const int q = e * NT + tid;
-      if (e * NT < NU && q < NU) {
-        const int b0 = 8 * (q % kHistUnits) + sl_delta[q / kHistUnits];
+      if (e * NT + wave * kWave < NU && q < NU) {
+        const int b0 = 8 * (q % kHistUnits) + ud[e];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const uint32_t n = (v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu;
@@ -1331,7 +1333,14 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
         }
       }
     }
-    __syncthreads();  // 2
+    if (wave == 0)
+#pragma unroll
+      for (int e = 0; e < kHistBins / kWave; ++e) {
+        const int b = e * kWave + lane;
+        s.wtab[b] = (uint32_t)b <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)b), lmax, c2) : 0.f;
+      }
+    __syncthreads();  // B
+
     // ---- cuts (wave 0)
     if (wave == 0) {
       auto hc = [&](int b) { return s.hist[b]; };
@@ -1392,13 +1401,13 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
         }
       }
       if (lane == 0) {
-        h_i[3] = dc;
-        h_i[4] = (int32_t)tk2;
+        f.cut_bin = dc;
+        f.cut_take = (int32_t)tk2;
       }
     }
-    __syncthreads();  // 3
-    dcut = h_i[3];
-    take = (uint32_t)h_i[4];
+    __syncthreads();  // C
+    dcut = f.cut_bin;
+    take = (uint32_t)f.cut_take;
     if (dcut < 0) {  // the cut lies below the window
       SampleRow<bf16_t, NW> mrow;
       mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
@@ -1406,17 +1415,17 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
       if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
       return;
     }
-    // ---- kept mass of every slice: bins above the cut, plus (below) its
-    // share of the first `take` tokens of the cut bin (slices in index
-    // order). The 32 units of a slice are one half-wave; a unit's eight bins
-    // (exact counts times fp32 weights) and the half-wave tree add in fp32
-    // (relative error below 1e-6 of the slice's kept mass).
+    wcut = (double)s.wtab[dcut];
+    // ---- kept mass of every slice: bins above the cut; and its tokens in
+    // the cut bin. The 32 units of a slice are one half-wave; a unit's eight
+    // bins (exact counts times fp32 weights) and the half-wave tree add in
+    // fp32 (relative error below 1e-6 of the slice's kept mass).
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
-      if (e * NT < NU) {  // uniform
+      if (e * NT + wave * kWave < NU) {  // wave-uniform: waves past the units skip
         const int q = e * NT + tid;
         const int sl = q / kHistUnits;
-        const int b0 = q < NU ? 8 * (q % kHistUnits) + sl_delta[min(sl, MS - 1)] : kHistBins;
+        const int b0 = q < NU ? 8 * (q % kHistUnits) + ud[e] : kHistBins;
         float m = 0.f, cc = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -1427,29 +1436,29 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
         m = group_sum<kHistUnits>(m);
         cc = group_sum<kHistUnits>(cc);
         if (q < NU && q % kHistUnits == 0) {
-          sl_mass[sl] = (double)m;
-          sl_cut[sl] = (int32_t)cc;
+          f.sl_mass[sl] = (double)m;
+          f.sl_cut[sl] = (int32_t)cc;
         }
       }
     }
-    __syncthreads();  // 4
+    __syncthreads();  // D
+    msl0 = in0 ? f.sl_mass[lane] : 0.0;
+    msl1 = in1 ? f.sl_mass[lane + 64] : 0.0;
+    cc0 = in0 ? f.sl_cut[lane] : 0;
+    cc1 = in1 ? f.sl_cut[lane + 64] : 0;
   }
 
-  // ---- the slice holding the draw (wave 0; lane l holds slices l and l + 64)
-  if (wave == 0) {
-    const bool in0 = lane < S, in1 = lane + 64 < S;
-    int32_t cc0 = 0, cc1 = 0;
-    if (!plain) {
-      cc0 = in0 ? sl_cut[lane] : 0;
-      cc1 = in1 ? sl_cut[lane + 64] : 0;
-    }
+  // ---- the slice holding the draw (every wave; lane l holds slices l and l + 64)
+  int psl;            // the slice
+  double rem;         // the draw target within it
+  int32_t tie_base;   // cut-bin tokens of the row before it
+  {
     // cut-bin tokens of the slices before each slice
     const int32_t i0 = wave_incl_scan_i32(cc0, lane);
     const int32_t i1 = lane_i32(i0, 63) + wave_incl_scan_i32(cc1, lane);
     const int32_t cb0 = i0 - cc0, cb1 = i1 - cc1;
-    double ms0 = in0 ? sl_mass[lane] : 0.0, ms1 = in1 ? sl_mass[lane + 64] : 0.0;
+    double ms0 = msl0, ms1 = msl1;
     if (!plain) {
-      const double wcut = (double)s.wtab[dcut];
       ms0 += (double)min(max((int32_t)take - cb0, 0), cc0) * wcut;
       ms1 += (double)min(max((int32_t)take - cb1, 0), cc1) * wcut;
     }
@@ -1463,124 +1472,128 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
     const double target = (double)sp.u * lane_f64(in_1, 63);
     const uint64_t b0 = __ballot(ms0 > 0.0 && ex0 <= target && target < in_0);
     const uint64_t b1 = __ballot(ms1 > 0.0 && ex1 <= target && target < in_1);
-    int32_t psl, tb;
-    double rem;
     if (b0) {
       const int l = __ffsll((unsigned long long)b0) - 1;
       psl = l;
       rem = target - lane_f64(ex0, l);
-      tb = lane_i32(cb0, l);
+      tie_base = lane_i32(cb0, l);
     } else if (b1) {
       const int l = __ffsll((unsigned long long)b1) - 1;
       psl = 64 + l;
       rem = target - lane_f64(ex1, l);
-      tb = lane_i32(cb1, l);
+      tie_base = lane_i32(cb1, l);
     } else {  // rounding left the target past every slice: the last slice with mass
       psl = max(wave_max_i32(max(ms0 > 0.0 ? lane : -1, ms1 > 0.0 ? lane + 64 : -1)), 0);
       rem = INFINITY;
-      tb = psl < 64 ? lane_i32(cb0, psl) : lane_i32(cb1, psl - 64);
-    }
-    if (lane == 0) {
-      h_i[2] = psl;
-      h_f[0] = rem;
-      h_i[5] = tb;
+      tie_base = psl < 64 ? lane_i32(cb0, psl) : lane_i32(cb1, psl - 64);
     }
   }
-  __syncthreads();  // 5
-  const int psl = h_i[2];
-  const double rem = h_f[0];
-  const int32_t tie_base = h_i[5];
 
-  // ---- the draw inside slice psl: thread t scans tokens [8t, 8t + 8), in index order
+  // ---- the draw inside slice psl: thread t holds tokens [8t, 8t + 8) of it
   const int tok0 = psl * kSliceTokens + 8 * DC * tid;
+  // Kept: keys above lo_key (plain rows: every real token, key 0 marks the
+  // tokens at or past V); ties: keys equal to tie_key (none in plain rows).
   const uint32_t cut_key = rkmax - (uint32_t)max(dcut, 0);
-  u32x4 x[DC];
+  const uint32_t lo_key = plain ? 0u : cut_key, tie_key = plain ? 0xffffffffu : cut_key;
+  const float wcut_f = (float)wcut;
+  u32x4 x[DC], kx[DC];  // the tokens (bf16 pairs) and their biased keys
 #pragma unroll
   for (int i = 0; i < DC; ++i) x[i] = crow[min(tok0 / 8 + i, last_chunk)];  // clamped: stays in the row
 #pragma unroll
   for (int i = 0; i < DC; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // biased keys; key 0 (below every real key) at or past V
-      const int tok = tok0 + 8 * i + 2 * j;
-      uint32_t k = bf16x2_keys(x[i][j]);
-      if (tok >= V) k = 0u;
-      else if (tok + 1 >= V) k &= 0xffffu;
-      x[i][j] = k;
-    }
-  int32_t rank0 = 0;  // cut-bin tokens of the row before this thread's first token
-  if (!plain) {
-    int32_t n = 0;
+    for (int j = 0; j < 4; ++j) kx[i][j] = bf16x2_keys(x[i][j]);
+  if (psl == S - 1)  // the tail slice (uniform): key 0, below every real key, at or past V
 #pragma unroll
     for (int i = 0; i < DC; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) n += ((x[i][j] & 0xffffu) == cut_key) + ((x[i][j] >> 16) == cut_key);
-    const int32_t inc = wave_incl_scan_i32(n, lane);
-    if (lane == 63) w_cnt[wave] = inc;
-    __syncthreads();  // 6
-    int32_t off = tie_base;
-    for (int w = 0; w < wave; ++w) off += w_cnt[w];
-    rank0 = off + inc - n;
-  }
-  // kept weight of token e of chunk i; `rank` counts the cut-bin tokens seen
-  auto kept_w = [&](const u32x4& xi, int e, int32_t& rank) -> float {
-    const uint32_t kw = xi[e >> 1];
-    const uint32_t k = (e & 1) ? (kw >> 16) : (kw & 0xffffu);
-    if (k == 0u || !(plain || k > cut_key || (k == cut_key && (uint32_t)(rank++) < take))) return 0.f;
-    const uint32_t vw = bf16x2_from_keys(kw);
-    return row_weight(__uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16)), lmax, c2);
+      for (int j = 0; j < 4; ++j) {
+        const int tok = tok0 + 8 * i + 2 * j;
+        if (tok >= V) kx[i][j] = 0u;
+        else if (tok + 1 >= V) kx[i][j] &= 0xffffu;
+      }
+  auto key_of = [&](int i, int e) -> uint32_t {
+    const uint32_t kw = kx[i][e >> 1];
+    return (e & 1) ? (kw >> 16) : (kw & 0xffffu);
   };
-  double own = 0.0;  // kept mass of this thread's tokens (fp32 per chunk)
-  int32_t lastk = -1;
-  {
-    int32_t rank = rank0;
+  // weight of token e of chunk i if it lies above the cut (0 otherwise)
+  auto above_w = [&](int i, int e) -> float {
+    const uint32_t w = x[i][e >> 1];
+    const float wt = row_weight(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)), lmax, c2);
+    return key_of(i, e) > lo_key ? wt : 0.f;
+  };
+  // this thread's mass above the cut (fp32 over its tokens) and its cut-bin tokens
+  float above = 0.f;
+  int32_t nt = 0;
 #pragma unroll
-    for (int i = 0; i < DC; ++i) {
-      float cs = 0.f;
+  for (int i = 0; i < DC; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = kept_w(x[i], e, rank);
-        if (w > 0.f) lastk = tok0 + 8 * i + e;
-        cs += w;
-      }
-      own += (double)cs;
+    for (int e = 0; e < 8; ++e) {
+      above += above_w(i, e);
+      nt += key_of(i, e) == tie_key ? 1 : 0;
     }
+  double exA;
+  const double inA = wave_scan_f64((double)above, lane, &exA);
+  const int32_t inN = wave_incl_scan_i32(nt, lane), exN = inN - nt;
+  if (lane == 63) {
+    f.w_above[wave] = inA;
+    f.w_ties[wave] = inN;
   }
-  // running kept mass over the threads in index order: wave scans, then the
-  // waves before (accumulated in wave order, so consecutive threads'
-  // [excl, incl) intervals meet exactly)
-  double exw;
-  const double inw = wave_scan_f64(own, lane, &exw);
-  const int32_t lkw = wave_max_i32(lastk);
-  if (lane == 63) w_mass[wave] = inw;
-  if (lane == 0) w_last[wave] = lkw;
-  if (tid == 0) s.result = -1;
-  __syncthreads();  // 7
-  double offm = 0.0;
-  int32_t lk = -1;  // the slice's last kept token
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) offm += w_mass[w];
-    lk = max(lk, w_last[w]);
+  __syncthreads();  // E
+
+  // ---- the wave holding the draw: lane w < NW takes wave w's kept mass
+  // M_w = A_w + wcut * (its kept cut-bin tokens); a scan over the lanes gives
+  // the waves' [R_w, R_{w+1}) in wave order
+  const double Aw = lane < NW ? f.w_above[lane] : 0.0;
+  const int32_t Nw = lane < NW ? f.w_ties[lane] : 0;
+  const int32_t TBw = tie_base + wave_incl_scan_i32(Nw, lane) - Nw;  // cut-bin tokens of the row before wave `lane`
+  const int32_t Kw = max((int32_t)take - TBw, 0);                    // of them, still to keep
+  const double Mw = Aw + wcut * (double)min(Kw, Nw);
+  double Rx;
+  const double Ri = wave_scan_f64(Mw, lane, &Rx);
+  const uint64_t whit = __ballot(Mw > 0.0 && Rx <= rem && rem < Ri);
+  const bool past = !whit;  // rounding left the target past every wave: the last kept token
+  const int wsel = whit ? __ffsll((unsigned long long)whit) - 1
+                        : wave_max_i32(Mw > 0.0 ? lane : -1);
+  if (wsel < 0) {  // nothing kept in the slice (every weight underflowed): the argmax
+    if (tid == 0) a.out[row] = argmax;
+    return;
   }
-  const double excl = offm + exw, incl = offm + inw;
-  if (own > 0.0 && excl <= rem && rem < incl) {  // exactly one thread: the intervals meet bit for bit
-    int32_t res = -1, rank = rank0;
-    double run = excl;
+  const double Rsel = lane_f64(Rx, wsel);
+  if (wave != wsel) return;
+  // Lane intervals [excl, incl) of the chosen wave: consecutive lanes meet
+  // exactly (the scans hand the previous lane's inclusive values on); the
+  // last lane ends at R_wsel + M_wsel, within rounding of R_{wsel+1} (a
+  // target in between takes the wave's last kept token).
+  const int32_t K = lane_i32(Kw, wsel);
+  const double excl = Rsel + (exA + wcut * (double)min(K, exN));
+  const double incl = Rsel + (inA + wcut * (double)min(K, inN));
+  // replay: kept weights in index order (the cut-bin tokens of rank < take)
+  int32_t rank = lane_i32(TBw, wsel) + exN;
+  double run = excl;
+  int32_t res = -1, lastk = -1;
 #pragma unroll
-    for (int i = 0; i < DC; ++i) {
-      float cs = 0.f;  // the chunk's sum as above, so the thread's total is reached bit for bit
+  for (int i = 0; i < DC; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = kept_w(x[i], e, rank);  // the same weights again (the tie ranks replay too)
-        if (res < 0 && w > 0.f && run + (double)(cs + w) > rem) res = tok0 + 8 * i + e;
-        cs += w;
+    for (int e = 0; e < 8; ++e) {
+      float w = above_w(i, e);
+      if (key_of(i, e) == tie_key && (uint32_t)(rank++) < take) w = wcut_f;
+      if (w > 0.f) {
+        const int idx = tok0 + 8 * i + e;
+        if (res < 0 && run + (double)w > rem) res = idx;
+        lastk = idx;
+        run += (double)w;
       }
-      run += (double)cs;
     }
-    s.result = res >= 0 ? res : lastk;  // rounding ran past the thread's tokens: its last kept one
+  const uint64_t hit = __ballot(!past && excl <= rem && rem < incl);
+  int32_t r;
+  if (hit) {
+    const int l = __ffsll((unsigned long long)hit) - 1;
+    r = lane_i32(res >= 0 ? res : lastk, l);  // rounding ran past the lane's tokens: its last kept one
+  } else {
+    r = wave_max_i32(lastk);  // the wave's last kept token
   }
-  __syncthreads();  // 8
-  const int32_t r = s.result >= 0 ? s.result : lk;
-  if (tid == 0) a.out[row] = r >= 0 ? r : argmax;
+  if (lane == 0) a.out[row] = r >= 0 ? r : argmax;
 }
 
 __global__ void __launch_bounds__(kFinishThreads) sample_finish_kernel(SampleArgs a, SampleWs ws) {
