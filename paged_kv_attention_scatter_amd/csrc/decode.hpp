@@ -296,11 +296,15 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
     const int32_t wj0 = min(j1, j0 + wave * per);
     const int32_t wj1 = min(j1, wj0 + per);
 
+    // Page-table entries one 64-key chunk ahead: the next chunk's slots are
+    // in flight while this chunk's rows are read.
+    int32_t next = lane < wj1 - wj0 ? pt[wj0 + lane] : -1;
     for (int32_t jb = wj0; jb < wj1; jb += kWave) {
       const int32_t nchunk = min(kWave, wj1 - jb);
+      const int32_t s = next;
+      next = lane < wj1 - (jb + kWave) ? pt[jb + kWave + lane] : -1;
       int32_t myslot = -1;
       if (lane < nchunk) {
-        const int32_t s = pt[jb + lane];
         if (s >= 0 && (int64_t)s < a.num_slots) myslot = s;
         else raise_fault(a.faults, 0x4u);
       }

@@ -1205,11 +1205,12 @@ __global__ void __launch_bounds__(kSliceThreads) sample_slice_kernel(SampleArgs 
 
 template <int NW, int MS>
 struct FinishLds {
-  double sl_mass[MS];   // kept mass of every slice (cut bin excluded)
-  int32_t sl_cut[MS];   // tokens of every slice in the cut bin
+  u32x4 units[MS * kHistUnits];    // the slices' histograms (16-byte units)
+  float uprefix[MS * kHistUnits];  // each unit's slice mass before it (row window weights)
   double w_above[NW];   // draw: mass of each wave's tokens above the cut
   int32_t w_ties[NW];   // draw: each wave's tokens in the cut bin
-  int32_t cut_bin, cut_take;
+  double sel_rem;       // wave 0's results: the draw target in its slice,
+  int32_t sel_dcut, sel_take, sel_psl, sel_tie;  // the cut, its ties, the slice, ties before it
 };
 
 // Finish kernel: one workgroup per row. The row maximum is the largest
@@ -1223,11 +1224,14 @@ struct FinishLds {
 // one thread of that wave and one of its 8 tokens. Cuts below the window
 // take the generic path over the row in memory.
 //
-// Every wave reads the slice records and works out the row maximum and the
-// slice holding the draw itself (the same data, the same operations, so the
-// same results in every wave); wave 0 alone takes the cuts. The workgroup
-// meets at five barriers (the zeroed histogram, the row histogram, the cuts,
-// the slices' kept masses, the waves' draw masses), one for plain rows.
+// Every wave reads the slice records and works out the row maximum itself
+// (the same data, the same operations, so the same results in every wave).
+// While the row histogram is built, every 16-byte unit of a slice histogram
+// is staged in LDS with its slice's mass before it, so wave 0 alone takes the
+// cuts, every slice's kept mass (a prefix and at most seven bins) and the
+// draw's slice in one go. The workgroup meets at four barriers (the zeroed
+// histogram, the row histogram, wave 0's choice, the waves' draw masses);
+// plain rows pick the slice in every wave and meet once.
 template <int NT, int MS>
 PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, SampleLds<NT / kWave>& s,
                            FinishLds<NT / kWave, MS>& f) {
@@ -1302,11 +1306,50 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
   int dcut = -1;      // cut bin (rows with a cut); tokens with d < dcut are kept
   uint32_t take = 0;  // tokens of bin dcut kept: the first ones in index order
   double wcut = 0.0;  // their weight
-  double msl0, msl1;  // kept mass of slices lane and lane + 64 (cut bin excluded)
-  int32_t cc0 = 0, cc1 = 0;  // their tokens in the cut bin
+  int psl = 0;        // the slice holding the draw
+  double rem = 0.0;   // the draw target within it
+  int32_t tie_base = 0;  // cut-bin tokens of the row before it
+
+  // The slice holding the draw, from the kept mass of slices lane and lane +
+  // 64 (cut bin excluded) and their cut-bin tokens; one wave.
+  auto select_slice = [&](double ms0, double ms1, int32_t cc0, int32_t cc1) {
+    // cut-bin tokens of the slices before each slice
+    const int32_t i0 = wave_incl_scan_i32(cc0, lane);
+    const int32_t i1 = lane_i32(i0, 63) + wave_incl_scan_i32(cc1, lane);
+    const int32_t cb0 = i0 - cc0, cb1 = i1 - cc1;
+    if (!plain) {
+      ms0 += (double)min(max((int32_t)take - cb0, 0), cc0) * wcut;
+      ms1 += (double)min(max((int32_t)take - cb1, 0), cc1) * wcut;
+    }
+    // running kept mass over the slices in index order; consecutive slices'
+    // [excl, incl) intervals meet exactly
+    double ex0, ex1;
+    const double in_0 = wave_scan_f64(ms0, lane, &ex0);
+    const double t0 = lane_f64(in_0, 63);
+    const double in_1 = wave_scan_f64(ms1, lane, &ex1) + t0;
+    ex1 += t0;
+    const double target = (double)sp.u * lane_f64(in_1, 63);
+    const uint64_t b0 = __ballot(ms0 > 0.0 && ex0 <= target && target < in_0);
+    const uint64_t b1 = __ballot(ms1 > 0.0 && ex1 <= target && target < in_1);
+    if (b0) {
+      const int l = __ffsll((unsigned long long)b0) - 1;
+      psl = l;
+      rem = target - lane_f64(ex0, l);
+      tie_base = lane_i32(cb0, l);
+    } else if (b1) {
+      const int l = __ffsll((unsigned long long)b1) - 1;
+      psl = 64 + l;
+      rem = target - lane_f64(ex1, l);
+      tie_base = lane_i32(cb1, l);
+    } else {  // rounding left the target past every slice: the last slice with mass
+      psl = max(wave_max_i32(max(ms0 > 0.0 ? lane : -1, ms1 > 0.0 ? lane + 64 : -1)), 0);
+      rem = INFINITY;
+      tie_base = psl < 64 ? lane_i32(cb0, psl) : lane_i32(cb1, psl - 64);
+    }
+  };
+
   if (plain) {
-    msl0 = m0;
-    msl1 = m1;
+    select_slice(m0, m1, 0, 0);  // every wave: the same data, the same result
   } else {
     // distance of each unit's slice below the row maximum (from the lane
     // that holds the slice)
@@ -1320,17 +1363,43 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
         ud[e] = sl < 64 ? a0 : a1;
       }
     }
-    // ---- the row histogram; wave 0 writes the window weights
+    // ---- the row histogram; every unit staged in LDS with its slice's mass
+    // before it (exact counts times the window weights, fp32: the unit's eight
+    // bins, then an exclusive scan over the slice's 32 units, one half-wave);
+    // wave 0 writes the window weights
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
-      const int q = e * NT + tid;
-      if (e * NT + wave * kWave < NU && q < NU) {
+      if (e * NT + wave * kWave < NU) {  // wave-uniform
+        const int q = e * NT + tid;
+        const bool in = q < NU;
         const int b0 = 8 * (q % kHistUnits) + ud[e];
+        float um = 0.f;
+        if (in) {
+          f.units[q] = v[e];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t n = (v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-          if (n && b0 + c < kHistBins) atomicAdd(&s.hist[b0 + c], n);
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t n = (v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+            const int b = b0 + c;
+            if (n && b < kHistBins) {
+              atomicAdd(&s.hist[b], n);
+              um = fmaf((float)n, (uint32_t)b <= rkmax ? row_weight(key16_value(rkmax - (uint32_t)b), lmax, c2) : 0.f,
+                        um);
+            }
+          }
         }
+        // exclusive prefix over the 32 units of the slice (lanes 32h .. 32h +
+        // 31): Kogge-Stone inside each 16-lane row (row_shr 1, 2, 4, 8), the
+        // half's first row total added to its second row, then the previous
+        // lane's inclusive value
+        float inc = um;
+        inc += dpp<0x111>(inc);
+        inc += dpp<0x112>(inc);
+        inc += dpp<0x114>(inc);
+        inc += dpp<0x118>(inc);
+        const float row_tot = __shfl(inc, (lane & 32) + 15, 64);
+        if (lane & 16) inc += row_tot;
+        const float prev = __shfl(inc, (lane + 63) & 63, 64);
+        if (in) f.uprefix[q] = (lane & 31) ? prev : 0.f;
       }
     }
     if (wave == 0)
@@ -1341,7 +1410,7 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
       }
     __syncthreads();  // B
 
-    // ---- cuts (wave 0)
+    // ---- cuts, every slice's kept mass and the draw's slice (wave 0)
     if (wave == 0) {
       auto hc = [&](int b) { return s.hist[b]; };
       int dk = -1;
@@ -1400,14 +1469,44 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
           tk2 = 0;
         }
       }
+      if (dc >= 0) {
+        dcut = dc;
+        take = tk2;
+        wcut = (double)s.wtab[dc];
+        // slice s's kept mass: its bins above the cut (slice bins below
+        // j = dcut - distance), the units before j's unit from the staged
+        // prefix, the rest of j's unit bin by bin; its cut-bin tokens: bin j
+        auto slice_cut = [&](int sl, int32_t dist, double* msl, int32_t* cc) {
+          *msl = 0.0;
+          *cc = 0;
+          if (sl >= S) return;
+          const int j = dc - dist;
+          if (j < 0) return;  // the whole slice lies below the cut
+          const int u = j >> 3;
+          const u32x4 x = f.units[sl * kHistUnits + u];
+          float m = f.uprefix[sl * kHistUnits + u];
+#pragma unroll
+          for (int c = 0; c < 7; ++c)
+            if (c < (j & 7)) m = fmaf((float)((x[c >> 1] >> (16 * (c & 1))) & 0xffffu), s.wtab[8 * u + c + dist], m);
+          *msl = (double)m;
+          *cc = (int32_t)((x[(j & 7) >> 1] >> (16 * (j & 1))) & 0xffffu);
+        };
+        double ms0, ms1;
+        int32_t c0, c1;
+        slice_cut(lane, dl0, &ms0, &c0);
+        slice_cut(lane + 64, dl1, &ms1, &c1);
+        select_slice(ms0, ms1, c0, c1);
+      }
       if (lane == 0) {
-        f.cut_bin = dc;
-        f.cut_take = (int32_t)tk2;
+        f.sel_dcut = dc;
+        f.sel_take = (int32_t)tk2;
+        f.sel_psl = psl;
+        f.sel_tie = tie_base;
+        f.sel_rem = rem;
       }
     }
     __syncthreads();  // C
-    dcut = f.cut_bin;
-    take = (uint32_t)f.cut_take;
+    dcut = f.sel_dcut;
     if (dcut < 0) {  // the cut lies below the window
       SampleRow<bf16_t, NW> mrow;
       mrow.init(reinterpret_cast<const bf16_t*>(a.logits) + (int64_t)row * a.row_stride, V, wave, lane);
@@ -1415,78 +1514,11 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
       if (tid == 0) a.out[row] = idx >= 0 ? idx : argmax;
       return;
     }
+    take = (uint32_t)f.sel_take;
+    psl = f.sel_psl;
+    tie_base = f.sel_tie;
+    rem = f.sel_rem;
     wcut = (double)s.wtab[dcut];
-    // ---- kept mass of every slice: bins above the cut; and its tokens in
-    // the cut bin. The 32 units of a slice are one half-wave; a unit's eight
-    // bins (exact counts times fp32 weights) and the half-wave tree add in
-    // fp32 (relative error below 1e-6 of the slice's kept mass).
-#pragma unroll
-    for (int e = 0; e < kU; ++e) {
-      if (e * NT + wave * kWave < NU) {  // wave-uniform: waves past the units skip
-        const int q = e * NT + tid;
-        const int sl = q / kHistUnits;
-        const int b0 = q < NU ? 8 * (q % kHistUnits) + ud[e] : kHistBins;
-        float m = 0.f, cc = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float n = (float)((v[e][c >> 1] >> (16 * (c & 1))) & 0xffffu);
-          if (b0 + c < dcut) m = fmaf(n, s.wtab[b0 + c], m);
-          else if (b0 + c == dcut) cc = n;
-        }
-        m = group_sum<kHistUnits>(m);
-        cc = group_sum<kHistUnits>(cc);
-        if (q < NU && q % kHistUnits == 0) {
-          f.sl_mass[sl] = (double)m;
-          f.sl_cut[sl] = (int32_t)cc;
-        }
-      }
-    }
-    __syncthreads();  // D
-    msl0 = in0 ? f.sl_mass[lane] : 0.0;
-    msl1 = in1 ? f.sl_mass[lane + 64] : 0.0;
-    cc0 = in0 ? f.sl_cut[lane] : 0;
-    cc1 = in1 ? f.sl_cut[lane + 64] : 0;
-  }
-
-  // ---- the slice holding the draw (every wave; lane l holds slices l and l + 64)
-  int psl;            // the slice
-  double rem;         // the draw target within it
-  int32_t tie_base;   // cut-bin tokens of the row before it
-  {
-    // cut-bin tokens of the slices before each slice
-    const int32_t i0 = wave_incl_scan_i32(cc0, lane);
-    const int32_t i1 = lane_i32(i0, 63) + wave_incl_scan_i32(cc1, lane);
-    const int32_t cb0 = i0 - cc0, cb1 = i1 - cc1;
-    double ms0 = msl0, ms1 = msl1;
-    if (!plain) {
-      ms0 += (double)min(max((int32_t)take - cb0, 0), cc0) * wcut;
-      ms1 += (double)min(max((int32_t)take - cb1, 0), cc1) * wcut;
-    }
-    // running kept mass over the slices in index order; consecutive slices'
-    // [excl, incl) intervals meet exactly
-    double ex0, ex1;
-    const double in_0 = wave_scan_f64(ms0, lane, &ex0);
-    const double t0 = lane_f64(in_0, 63);
-    const double in_1 = wave_scan_f64(ms1, lane, &ex1) + t0;
-    ex1 += t0;
-    const double target = (double)sp.u * lane_f64(in_1, 63);
-    const uint64_t b0 = __ballot(ms0 > 0.0 && ex0 <= target && target < in_0);
-    const uint64_t b1 = __ballot(ms1 > 0.0 && ex1 <= target && target < in_1);
-    if (b0) {
-      const int l = __ffsll((unsigned long long)b0) - 1;
-      psl = l;
-      rem = target - lane_f64(ex0, l);
-      tie_base = lane_i32(cb0, l);
-    } else if (b1) {
-      const int l = __ffsll((unsigned long long)b1) - 1;
-      psl = 64 + l;
-      rem = target - lane_f64(ex1, l);
-      tie_base = lane_i32(cb1, l);
-    } else {  // rounding left the target past every slice: the last slice with mass
-      psl = max(wave_max_i32(max(ms0 > 0.0 ? lane : -1, ms1 > 0.0 ? lane + 64 : -1)), 0);
-      rem = INFINITY;
-      tie_base = psl < 64 ? lane_i32(cb0, psl) : lane_i32(cb1, psl - 64);
-    }
   }
 
   // ---- the draw inside slice psl: thread t holds tokens [8t, 8t + 8) of it
@@ -1522,14 +1554,16 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
     const float wt = row_weight(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)), lmax, c2);
     return key_of(i, e) > lo_key ? wt : 0.f;
   };
-  // this thread's mass above the cut (fp32 over its tokens) and its cut-bin tokens
-  float above = 0.f;
+  // this thread's mass above the cut (fp32 over its tokens) and its cut-bin
+  // tokens; the weights stay in registers for the replay
+  float above = 0.f, wt[DC][8];
   int32_t nt = 0;
 #pragma unroll
   for (int i = 0; i < DC; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      above += above_w(i, e);
+      wt[i][e] = above_w(i, e);
+      above += wt[i][e];
       nt += key_of(i, e) == tie_key ? 1 : 0;
     }
   double exA;
@@ -1576,7 +1610,7 @@ PKV_INLINE void finish_row(const SampleArgs& a, const SampleWs& ws, int row, Sam
   for (int i = 0; i < DC; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float w = above_w(i, e);
+      float w = wt[i][e];
       if (key_of(i, e) == tie_key && (uint32_t)(rank++) < take) w = wcut_f;
       if (w > 0.f) {
         const int idx = tok0 + 8 * i + e;
