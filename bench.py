@@ -46,7 +46,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3])
     ap.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--skip-extend", action="store_true")
@@ -110,6 +110,25 @@ def copy_calibration(torch, dev):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+SETTLE_MS = 100.0
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Untimed calls of fn for about ms of wall time. The GPU's clocks climb
+    over tens of milliseconds of load (an MFMA-bound extend call runs ~20%
+    slower straight after an idle second), and the host-side set-up before
+    each component leaves the GPU idle, so every timed loop starts from the
+    loaded state. The host waits every 8 calls, so wall time is GPU time."""
+    t_end = time.perf_counter() + ms / 1e3
+    n = 0
+    while n < 3 or time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def main():
@@ -409,10 +428,13 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
            lambda i: pkv.paged_attention_decode(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_table,
                                                 d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws),
            lambda i: pkv.sample(bufs[i % len(bufs)], None, None, None, None, out=tokens, workspace=s_ws)]
-    for i in range(5):
+    it = iter(range(1 << 30))
+
+    def one_step():
+        i = next(it)
         for op in ops:
             op(i)
-    torch.cuda.synchronize()
+    settle(torch, one_step)
     n = max(20, args.steps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
     for i in range(n):
@@ -463,12 +485,11 @@ def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
     o = torch.empty_like(q)
     flops = 4.0 * HEAD_DIM * HQ * float(np.sum(E.astype(np.float64) * C + E * (E + 1) / 2.0))
     try:
-        for _ in range(3):
-            pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
+        pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
     except pkv.PkvError as e:
         log(f"extend skipped: {e}")
         return {"extend": f"unavailable: {e}"}
-    torch.cuda.synchronize()
+    settle(torch, lambda: pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o))
     n = max(10, args.steps // 2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -518,10 +539,9 @@ def bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
                   wq.data_ptr(), wk.data_ptr(), 1e-6, 1_000_000.0, torch.cuda.current_stream().cuda_stream)
         fn = pkv.lib().pkv_qk_norm_rope_store_kv
         run = lambda: fn(*c_args)
-        for _ in range(3):
-            if run() != 0:
-                raise RuntimeError(pkv.lib().pkv_last_error().decode())
-        torch.cuda.synchronize()
+        if run() != 0:
+            raise RuntimeError(pkv.lib().pkv_last_error().decode())
+        settle(torch, run)
         reps = max(20, args.steps)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -584,9 +604,7 @@ def bench_q_prologue(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
 
         times = {}
         for label, fn in (("unfused", unfused), ("fused", fused)):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            settle(torch, fn)
             reps = max(20, args.steps // 2)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -620,10 +638,9 @@ def bench_embedding(torch, pkv, gen, dev, args):
         fn = pkv.lib().pkv_embedding_gather
         c_args = (W.data_ptr(), 1, V, H, H, ids.data_ptr(), n, 0, V, o.data_ptr(), H,
                   torch.cuda.current_stream().cuda_stream)
-        for _ in range(3):
-            if fn(*c_args) != 0:
-                raise RuntimeError(pkv.lib().pkv_last_error().decode())
-        torch.cuda.synchronize()
+        if fn(*c_args) != 0:
+            raise RuntimeError(pkv.lib().pkv_last_error().decode())
+        settle(torch, lambda: fn(*c_args))
         reps = max(20, args.steps)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -673,7 +690,8 @@ def bench_sampler_variants(torch, pkv, gen, dev, args):
             for c in calls:
                 if fn(*c) != 0:
                     raise RuntimeError(pkv.lib().pkv_last_error().decode())
-            torch.cuda.synchronize()
+            it = iter(range(1 << 30))
+            settle(torch, lambda: fn(*calls[next(it) % nbuf]), SETTLE_MS / 2)
             reps = max(8, args.steps // 4) * nbuf
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -719,9 +737,7 @@ def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
     reps = max(50, args.steps)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle(torch, fn, SETTLE_MS / 2)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -830,9 +846,8 @@ def bench_mixed(torch, pkv, dev, args):
         pkv.sample(bufs[i % len(bufs)], d_T, d_K, d_P, d_u, min_p=d_mp, out=tokens, workspace=s_ws)
 
     def timed(fn, n):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        it = iter(range(1 << 30))
+        settle(torch, lambda: fn(next(it)))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(n):
