@@ -3,8 +3,10 @@
     python bench.py [--steps K] [--warmup W] [--config 3|2] [--skip-cpu]
 
 A step is one decode step of the whole path over one synthetic batch, on the
-current HIP stream: store_kv of the batch's new K/V rows, decode attention
-over the paged pool, then the sampler over the batch's logits. The default
+current HIP stream: decode attention over the paged pool with the store_kv
+of the batch's new K/V rows fused into it (one call), then the sampler over
+the batch's logits. The separate store_kv and decode calls are timed beside
+it for reference. The default
 workload is the 256-request decode batch (device_len ~ U[1024, 8192], bf16,
 16 query / 8 KV heads, head_dim 128, page_size 1, pool sized for 28 layers
 from 0.9 x free HBM at 114688 bytes per page; logits [256, 151936], 128
@@ -55,7 +57,7 @@ def parse():
     ap.add_argument("--skip-components", action="store_true",
                     help="skip the q/k norm + RoPE + store, embedding and graph-replay timings")
     ap.add_argument("--small-steps", type=str, default=None, metavar="BS[,BS...]",
-                    help="only time eager decode steps (store_kv, decode, sampler) of the first BS requests of "
+                    help="only time eager decode steps (decode with its store, sampler) of the first BS requests of "
                          "the 256-request batch over a one-layer pool, for kernel traces; prints per-size times")
     ap.add_argument("--sampler-only", action="store_true",
                     help="only time the sampler: the 256-row mixed batch, then the variants; for kernel traces")
@@ -197,11 +199,13 @@ def main():
     tokens = torch.empty(bs, dtype=torch.int32, device=dev)
     s_ws = pkv.sample_workspace(bs, cfg.vocab, dev)
 
+    def attend(kp, vp):  # store_kv of the new rows fused into decode attention
+        pkv.paged_attention_decode_store(q, kp, vp, d_table, d_C, d_S, d_loc, new_k, new_v, max_total_kv=total_kv,
+                                         out=o, workspace=ws)
+
     def step(i):
         layer = i % LAYERS_FILLED
-        kp, vp = pool[0, layer], pool[1, layer]
-        pkv.store_kv(kp, vp, d_loc, new_k, new_v)
-        pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
+        attend(pool[0, layer], pool[1, layer])
         pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
 
     # ---------------------------------------------------------------- timed region
@@ -217,10 +221,23 @@ def main():
     kv_bytes = total_kv * HKV * HEAD_DIM * 2 * 2           # K and V rows read, bf16
     logit_bytes = bs * cfg.vocab * 2
 
-    # per-op durations with HIP events (same stream as the launches)
+    # per-op durations with HIP events (same stream as the launches): the
+    # step's two calls, then store_kv and decode attention as separate calls
     E = lambda: torch.cuda.Event(enable_timing=True)
     n = args.steps
-    ev = [[E() for _ in range(4)] for _ in range(n)]
+    ev = [[E() for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        layer = i % LAYERS_FILLED
+        ev[i][0].record()
+        attend(pool[0, layer], pool[1, layer])
+        ev[i][1].record()
+        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(2)] for i in range(n)])
+    decode_ms, sample_ms = (float(np.mean(ms[:, j])) for j in range(2))
+    decode_p = np.percentile(ms[:, 0], [10, 50, 90])
+    ev = [[E() for _ in range(3)] for _ in range(n)]
     for i in range(n):
         layer = i % LAYERS_FILLED
         kp, vp = pool[0, layer], pool[1, layer]
@@ -229,16 +246,14 @@ def main():
         ev[i][1].record()
         pkv.paged_attention_decode(q, kp, vp, d_table, d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws)
         ev[i][2].record()
-        pkv.sample(logit_bufs[i % len(logit_bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
-        ev[i][3].record()
     torch.cuda.synchronize()
-    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(n)])
-    store_ms, decode_ms, sample_ms = (float(np.mean(ms[:, j])) for j in range(3))
-    decode_p = np.percentile(ms[:, 1], [10, 50, 90])
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(2)] for i in range(n)])
+    store_ms, unfused_ms = (float(np.mean(ms[:, j])) for j in range(2))
     decode_gbs = kv_bytes / (decode_ms * 1e-3) / 1e9
     sample_gbs = logit_bytes / (sample_ms * 1e-3) / 1e9
-    log(f"step {ms_per_step:.3f} ms | store {store_ms * 1e3:.1f} us | decode {decode_ms * 1e3:.1f} us "
-        f"({decode_gbs:.0f} GB/s) | sample {sample_ms * 1e3:.1f} us ({sample_gbs:.0f} GB/s)")
+    log(f"step {ms_per_step:.3f} ms | decode with its store {decode_ms * 1e3:.1f} us ({decode_gbs:.0f} GB/s) | "
+        f"sample {sample_ms * 1e3:.1f} us ({sample_gbs:.0f} GB/s) | separate calls: store {store_ms * 1e3:.1f} us, "
+        f"decode {unfused_ms * 1e3:.1f} us")
 
     result = {
         "metric": "decode-attn KV GB/s (% HBM peak) at bs=256; sampler tokens/s; extend TFLOP/s",
@@ -253,20 +268,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: decode step (store_kv + decode attention + sampler), "
+        "config": {"workload": f"{cfg.name}: decode step (store_kv fused into decode attention + sampler), "
                                f"bs={bs}, device_len~U[{int(S.min())}..{int(S.max())}], sum={total_kv}, "
                                "16q/8kv heads, head_dim 128, page_size 1, 28-layer pool, "
                                f"logits [{bs}, {cfg.vocab}] bf16",
                    "bs": bs, "sum_device_len": total_kv, "num_pages": num_pages, "page_size": 1},
-        "roofline": {"bound": "hbm", "kernel": "decode attention (split-K + combine, one call)",
+        "roofline": {"bound": "hbm", "kernel": "decode attention with its store_kv fused in (split-K + combine, one call)",
                      "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": kv_bytes, "avg_launch_us": round(decode_ms * 1e3, 2),
                      "p10_p50_p90_us": [round(x * 1e3, 2) for x in decode_p]},
         "components": {
-            "store_kv_us": round(store_ms * 1e3, 2),
             "decode_us": round(decode_ms * 1e3, 2),
             "decode_kv_gbs": round(decode_gbs, 1),
+            "store_kv_separate_us": round(store_ms * 1e3, 2),
+            "decode_separate_us": round(unfused_ms * 1e3, 2),
             "sample_us": round(sample_ms * 1e3, 2),
             "sampler_tokens_per_s": round(bs / (sample_ms * 1e-3), 1),
             "sampler_gbs": round(sample_gbs, 1),
@@ -338,8 +354,8 @@ def small_steps(args):
         ws_s = pkv.sample_workspace(bs, cfg.vocab, dev)
 
         def step(i):
-            pkv.store_kv(kp, vp, s_loc, s_k, s_v)
-            pkv.paged_attention_decode(s_q, kp, vp, s_table, s_C, s_S, max_total_kv=max_kv, out=o, workspace=ws_d)
+            pkv.paged_attention_decode_store(s_q, kp, vp, s_table, s_C, s_S, s_loc, s_k, s_v, max_total_kv=max_kv,
+                                             out=o, workspace=ws_d)
             pkv.sample(logits[i % 4], T, None, P, u, out=tok, workspace=ws_s)
 
         for i in range(args.warmup):
@@ -427,7 +443,11 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
     ops = [lambda i: pkv.store_kv(pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_loc, new_k, new_v),
            lambda i: pkv.paged_attention_decode(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_table,
                                                 d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws),
-           lambda i: pkv.sample(bufs[i % len(bufs)], None, None, None, None, out=tokens, workspace=s_ws)]
+           lambda i: pkv.sample(bufs[i % len(bufs)], None, None, None, None, out=tokens, workspace=s_ws),
+           lambda i: pkv.paged_attention_decode_store(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED],
+                                                      d_table, d_C, d_S, d_loc, new_k, new_v, max_total_kv=total_kv,
+                                                      out=o, workspace=ws)]
+    step_ops = (ops[3], ops[2])  # the step: store fused into decode, then the argmax
     it = iter(range(1 << 30))
 
     def one_step():
@@ -436,19 +456,19 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
             op(i)
     settle(torch, one_step)
     n = max(20, args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(n)]
     for i in range(n):
         for j, op in enumerate(ops):
             ev[i][j].record()
             op(i)
-        ev[i][3].record()
+        ev[i][len(ops)].record()
     torch.cuda.synchronize()
-    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(n)])
-    st_us, dec_us, am_us = (float(np.mean(ms[:, j])) * 1e3 for j in range(3))
+    ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(ops))] for i in range(n)])
+    st_us, dec_us, am_us, fused_us = (float(np.mean(ms[:, j])) * 1e3 for j in range(len(ops)))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
-        for op in ops:
+        for op in step_ops:
             op(i)
     e1.record()
     torch.cuda.synchronize()
@@ -456,12 +476,14 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
     kv = total_kv * HKV * HEAD_DIM * 2 * 2
     lg = bs * cfg.vocab * 2
     log(f"decode64: store {st_us:.1f} us | decode {dec_us:.1f} us ({kv / dec_us / 1e3:.0f} GB/s) | "
-        f"argmax {am_us:.1f} us ({lg / am_us / 1e3:.0f} GB/s) | step {step_us:.1f} us")
+        f"decode with its store {fused_us:.1f} us | argmax {am_us:.1f} us ({lg / am_us / 1e3:.0f} GB/s) | "
+        f"step {step_us:.1f} us")
     if pkv.read_faults():
         raise RuntimeError("device fault word set during the decode64 timing")
     return {"decode64_workload": f"bs=64, device_len {int(S.min())}..{int(S.max())}, sum {total_kv}, "
                                  f"page_size 1, all greedy (argmax) over [64, {cfg.vocab}] bf16",
             "decode64_store_us": round(st_us, 2), "decode64_decode_us": round(dec_us, 2),
+            "decode64_decode_store_us": round(fused_us, 2),
             "decode64_decode_kv_gbs": round(kv / dec_us / 1e3, 1),
             "decode64_decode_frac_hbm": round(kv / dec_us / 1e3 / HBM_PEAK_GBS, 4),
             "decode64_argmax_us": round(am_us, 2), "decode64_argmax_gbs": round(lg / am_us / 1e3, 1),
@@ -764,9 +786,8 @@ def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
         ws_s = pkv.sample_workspace(bs, V, dev)
 
         def eager():
-            pkv.store_kv(kp, vp, b_loc, b_k, b_v)
-            pkv.paged_attention_decode(b_q, kp, vp, d_tab, b_C, b_S, table_idx=b_idx, max_total_kv=max_kv, out=o,
-                                       workspace=ws_d)
+            pkv.paged_attention_decode_store(b_q, kp, vp, d_tab, b_C, b_S, b_loc, b_k, b_v, table_idx=b_idx,
+                                             max_total_kv=max_kv, out=o, workspace=ws_d)
             pkv.sample(b_lg, b_T, None, b_P, b_u, out=tok, workspace=ws_s)
 
         args_run = (b_q, b_k, b_v, b_loc, b_idx, b_C, b_S, b_lg, b_T, b_P, b_u)

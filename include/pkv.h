@@ -10,6 +10,8 @@
  *      (pkv_embedding_gather        the embedding rows of the step's token ids,
  *                                   the first op of forward_batch)
  *   2. pkv_paged_attention_decode   GQA attention of one new token per request
+ *      (pkv_paged_attention_decode_store   the same with step 1's store done by
+ *                                   the attention call itself);
  *      pkv_paged_attention_extend   causal GQA attention of a chunk of new tokens
  *                                   over a cached prefix (prefill / extend);
  *   3. pkv_sample                   temperature -> top-k -> top-p (-> min_p) -> draw per row,
@@ -78,6 +80,7 @@ typedef enum { PKV_I32 = 0, PKV_I64 = 1 } pkv_itype;
 #define PKV_FAULT_TABLE_SLOT   0x4u  /* attention: a page-table entry outside [0, num_slots) */
 #define PKV_FAULT_TABLE_ROW    0x8u  /* attention: table_idx[r] outside [0, pt_rows) */
 #define PKV_FAULT_QROWS        0x10u /* extend: sum of extend lengths exceeds total_q or max_extend */
+#define PKV_FAULT_OUT_LOC      0x20u /* decode_store: page_table[t_r, S_r - 1] != out_loc[r] */
 
 /*
  * One layer of the paged KV pool, token-granular view ([DISS] 4.4.3: the pool
@@ -205,6 +208,38 @@ int pkv_paged_attention_decode(const pkv_pool* pool, const void* q, int64_t q_st
                                void* ws, size_t ws_bytes, void* stream);
 
 size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_total_kv);
+
+/*
+ * store_kv fused into decode attention: the decode step's store, then
+ * attention ([DISS] 4.6.7: the new rows are stored before the layer's
+ * attention reads them; 4.9.4 for the store), in one call. For every request
+ * r with valid lengths:
+ *   pool.k[out_loc[r]] = k[r], pool.v[out_loc[r]] = v[r] (rows copied bit for
+ *   bit, as pkv_store_kv), and
+ *   o[r] = decode attention as pkv_paged_attention_decode, with key S_r - 1
+ *   taken from the new row k[r] / v[r] and keys j < S_r - 1 from the pool.
+ * This is pkv_store_kv followed by pkv_paged_attention_decode, bit for bit,
+ * whenever page_table[t_r, S_r - 1] == out_loc[r] and no other key of the
+ * batch reads an out_loc slot -- what an engine that takes out_loc from the
+ * page table's new entries has. A request whose table entry S_r - 1 is not
+ * out_loc[r] still attends to its new row as key S_r - 1 and sets
+ * PKV_FAULT_OUT_LOC; an out_loc[r] outside [0, num_slots) is not written and
+ * sets PKV_FAULT_STORE_SLOT; a request skipped for invalid lengths (its output
+ * zero-filled, PKV_FAULT_LENGTH) stores nothing.
+ *   out_loc   device, [bs] of int32 (loc_type PKV_I32) or int64 (PKV_I64).
+ *   k, v      device, [bs, kv_heads, 128] in pool.dtype, rows k_stride /
+ *             v_stride elements apart (0 = dense; strides * itemsize multiples
+ *             of 16).
+ * The other arguments, the workspace and the errors are those of
+ * pkv_paged_attention_decode (k and v checked as in pkv_store_kv).
+ */
+int pkv_paged_attention_decode_store(const pkv_pool* pool, const void* out_loc, int32_t loc_type,
+                                     const void* k, int64_t k_stride, const void* v, int64_t v_stride,
+                                     const void* q, int64_t q_stride, void* o, int64_t o_stride, int32_t bs,
+                                     int32_t num_q_heads, const int32_t* page_table, int32_t pt_rows,
+                                     int64_t pt_stride, const int32_t* table_idx, const int32_t* cached_len,
+                                     const int32_t* device_len, int64_t max_total_kv, float sm_scale,
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Qwen3's q prologue folded into attention ([TINY] its rmsnorm and rope

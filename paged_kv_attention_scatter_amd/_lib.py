@@ -24,7 +24,7 @@ PKV_PREP_ALL_GREEDY, PKV_PREP_USE_TOP_K, PKV_PREP_USE_TOP_P = 0x1, 0x2, 0x4
 NOALLOC_SCRATCH_BYTES = 16 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 FAULT_BITS = {
     0x1: "PKV_FAULT_STORE_SLOT", 0x2: "PKV_FAULT_LENGTH", 0x4: "PKV_FAULT_TABLE_SLOT",
-    0x8: "PKV_FAULT_TABLE_ROW", 0x10: "PKV_FAULT_QROWS",
+    0x8: "PKV_FAULT_TABLE_ROW", 0x10: "PKV_FAULT_QROWS", 0x20: "PKV_FAULT_OUT_LOC",
 }
 
 
@@ -56,6 +56,11 @@ SIGNATURES = {
                                              c_void_p, c_void_p, c_int64, c_float, c_void_p, c_size_t,
                                              c_void_p]),
     "pkv_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int64]),
+    "pkv_paged_attention_decode_store": (c_int32, [POINTER(PkvPool), c_void_p, c_int32, c_void_p, c_int64,
+                                                   c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                                   c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
+                                                   c_void_p, c_void_p, c_int64, c_float, c_void_p, c_size_t,
+                                                   c_void_p]),
     "pkv_paged_attention_decode_qnr": (c_int32, [POINTER(PkvPool), c_void_p, c_int64, c_void_p, c_int64,
                                                  c_int32, c_int32, c_void_p, c_int32, c_int64, c_void_p,
                                                  c_void_p, c_void_p, c_int64, c_float, POINTER(PkvQNormRope),

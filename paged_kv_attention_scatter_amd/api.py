@@ -247,6 +247,45 @@ def paged_attention_decode(q, k_pool, v_pool, page_table, cached_len, device_len
     return out
 
 
+def paged_attention_decode_store(q, k_pool, v_pool, page_table, cached_len, device_len, out_loc, k, v, *,
+                                 table_idx=None, max_total_kv=None, sm_scale: float = 0.0, page_size: int = 1,
+                                 out=None, workspace=None, stream=None):
+    """store_kv fused into decode attention (pkv_paged_attention_decode_store):
+    writes k[r] / v[r] to pool slot out_loc[r] and attends with the new row as
+    key device_len - 1 of request r. Same result as store_kv followed by
+    paged_attention_decode when out_loc holds each request's last page-table
+    entry. k, v: [bs, kv_heads, 128] in the pool's dtype."""
+    torch = _torch()
+    pool = make_pool(k_pool, v_pool, page_size)
+    bs, hq = q.shape[0], q.shape[1]
+    qs = _rows(q, "q", hq * HEAD_DIM)
+    if q.dtype != k_pool.dtype or k.dtype != k_pool.dtype or v.dtype != k_pool.dtype:
+        raise ValueError("q, k and v must have the pool's dtype")
+    row = k_pool.shape[1] * HEAD_DIM
+    ks, vs = _rows(k, "k", row), _rows(v, "v", row)
+    if k.shape[0] != bs or v.shape[0] != bs or out_loc.shape[0] != bs:
+        raise ValueError("k, v and out_loc need one row per request")
+    loc_type = {torch.int32: PKV_I32, torch.int64: PKV_I64}.get(out_loc.dtype)
+    if loc_type is None:
+        raise ValueError("out_loc must be int32 or int64")
+    if out is None:
+        out = torch.empty((bs, hq, HEAD_DIM), dtype=q.dtype, device=q.device)
+    os_ = _rows(out, "out", hq * HEAD_DIM)
+    rows, pts = _table(page_table)
+    _lengths(device_len, "device_len", bs)
+    if table_idx is not None:
+        _lengths(table_idx, "table_idx", bs)
+    if max_total_kv is None:
+        max_total_kv = bs * pts
+    ws = _workspace(decode_workspace_size(bs, hq, max_total_kv), q.device, workspace)
+    check(lib().pkv_paged_attention_decode_store(
+        byref(pool), out_loc.data_ptr(), loc_type, k.data_ptr(), ks, v.data_ptr(), vs, q.data_ptr(), qs,
+        out.data_ptr(), os_, bs, hq, page_table.data_ptr(), rows, pts, _ptr(table_idx), _ptr(cached_len),
+        device_len.data_ptr(), int(max_total_kv), sm_scale, _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
 def paged_attention_decode_noalloc(q, k_pool, v_pool, page_table, cached_len, device_len, *, table_idx=None,
                                    max_total_kv=None, sm_scale: float = 0.0, page_size: int = 1, out=None,
                                    stream=None):

@@ -61,6 +61,15 @@ struct DecodeArgs {
   // rows of device_len 0 are no rows at all (skipped without a fault, their
   // output untouched): the padding of the extend rows run as decode rows
   int32_t skip_empty;
+  // store_kv fused in (k_new == nullptr: no store): key S - 1 of request r is
+  // the new row k_new[r] / v_new[r], which the wave that reads it also writes
+  // to pool slot out_loc[r]
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_stride;    // elements between new rows
+  int64_t vn_stride;
+  const void* out_loc;  // [bs] int32, or int64 when loc64
+  int32_t loc64;
 };
 
 template <typename T>
@@ -116,6 +125,13 @@ __device__ __forceinline__ void load_lane_row(uint32_t (&w)[NWD], const T* base)
     w[4 * i + 2] = x.z;
     w[4 * i + 3] = x.w;
   }
+}
+
+template <int NWD>
+__device__ __forceinline__ void store_lane_row(void* base, const uint32_t (&w)[NWD]) {
+  u32x4* p = reinterpret_cast<u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < NWD / 4; ++i) p[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
 }
 
 template <typename T, int NWD>
@@ -301,12 +317,12 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
     int32_t next = lane < wj1 - wj0 ? pt[wj0 + lane] : -1;
     for (int32_t jb = wj0; jb < wj1; jb += kWave) {
       const int32_t nchunk = min(kWave, wj1 - jb);
-      const int32_t s = next;
+      const int32_t s = next, pt_raw = next;
       next = lane < wj1 - (jb + kWave) ? pt[jb + kWave + lane] : -1;
       int32_t myslot = -1;
       if (lane < nchunk) {
         if (s >= 0 && (int64_t)s < a.num_slots) myslot = s;
-        else raise_fault(a.faults, 0x4u);
+        else if (!(a.k_new && jb + lane == S - 1)) raise_fault(a.faults, 0x4u);  // the new key's entry: checked below
       }
       for (int32_t kb = 0; kb < nchunk; kb += KB) {
         uint32_t kw[KB][NWD], vw[KB][NWD];
@@ -314,7 +330,23 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
           sl[kk] = (kb + kk < nchunk) ? __builtin_amdgcn_readlane(myslot, kb + kk) : -1;
-          if (sl[kk] >= 0) {
+          // the new row (wave-uniform; a block may run past this wave's keys,
+          // whose key S - 1 is then another wave's): read from k_new / v_new
+          if (a.k_new && kb + kk < nchunk && jb + kb + kk == S - 1) {
+            const int32_t tslot = __builtin_amdgcn_readlane(pt_raw, kb + kk);
+            load_lane_row<T, NWD>(kw[kk], reinterpret_cast<const T*>(a.k_new) + (int64_t)r * a.kn_stride + head_ofs);
+            load_lane_row<T, NWD>(vw[kk], reinterpret_cast<const T*>(a.v_new) + (int64_t)r * a.vn_stride + head_ofs);
+            const int64_t loc = a.loc64 ? reinterpret_cast<const int64_t*>(a.out_loc)[r]
+                                        : (int64_t)reinterpret_cast<const int32_t*>(a.out_loc)[r];
+            if (loc >= 0 && loc < a.num_slots) {
+              store_lane_row<NWD>(const_cast<T*>(kpool) + loc * a.pool_row + head_ofs, kw[kk]);
+              store_lane_row<NWD>(const_cast<T*>(vpool) + loc * a.pool_row + head_ofs, vw[kk]);
+            } else if (lane == 0) {
+              raise_fault(a.faults, 0x1u);
+            }
+            if (lane == 0 && (int64_t)tslot != loc) raise_fault(a.faults, 0x20u);
+            sl[kk] = 0;  // a key (its slot is not read)
+          } else if (sl[kk] >= 0) {
             load_lane_row<T, NWD>(kw[kk], kpool + (int64_t)sl[kk] * a.pool_row + head_ofs);
             load_lane_row<T, NWD>(vw[kk], vpool + (int64_t)sl[kk] * a.pool_row + head_ofs);
           } else {

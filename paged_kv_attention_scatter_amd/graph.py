@@ -10,7 +10,8 @@ holds only the dummy page's slot, so everything the padding rows write lands
 there.
 
 DecodeGraphRunner does that for one decode step of this library: store_kv of
-the new K/V rows, decode attention over the pool, then the sampler. The
+the new K/V rows and decode attention over the pool (one fused call), then
+the sampler. The
 graphs replay the library's kernels on static buffers; run() copies a batch
 into them (padding rows: the dummy request, one key long, greedy), replays
 the graph of the next captured size, and returns views of the outputs. Every
@@ -92,11 +93,12 @@ class DecodeGraphRunner:
         torch.cuda.synchronize()
 
     def _step(self, n):
-        api.store_kv(self.k_pool, self.v_pool, self.out_loc[:n], self.k[:n], self.v[:n], page_size=self.page_size)
-        api.paged_attention_decode(self.q[:n], self.k_pool, self.v_pool, self.page_table, self.cached_len[:n],
-                                   self.device_len[:n], table_idx=self.table_idx[:n],
-                                   max_total_kv=n * self.max_context, page_size=self.page_size,
-                                   out=self.o[:n], workspace=self.ws_d)
+        # store_kv and decode attention in one call (the attention kernel
+        # writes each request's new row and reads it as its last key)
+        api.paged_attention_decode_store(self.q[:n], self.k_pool, self.v_pool, self.page_table, self.cached_len[:n],
+                                         self.device_len[:n], self.out_loc[:n], self.k[:n], self.v[:n],
+                                         table_idx=self.table_idx[:n], max_total_kv=n * self.max_context,
+                                         page_size=self.page_size, out=self.o[:n], workspace=self.ws_d)
         api.sample(self.logits[:n], self.T[:n], None if self.K is None else self.K[:n], self.P[:n], self.u[:n],
                    out=self.tokens[:n], workspace=self.ws_s)
 

@@ -182,6 +182,26 @@ def test_decode_argument_errors(L, pool, kw, status):
     assert _decode(L, _pool(**pool), **kw) == status
 
 
+def _decode_store(L, pool, loc=0xB0000, lt=0, k=0xC0000, ks=0, v=0xD0000, vs=0, bs=4, q=0x60000, ws=0xA0000):
+    return L.pkv_paged_attention_decode_store(ctypes.byref(pool), loc, lt, k, ks, v, vs, q, 0, 0x70000, 0, bs, 16,
+                                              0x80000, 4, 64, None, None, 0x90000, 100, 0.0, ws, 1 << 30, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(loc=None), -1), (dict(lt=2), -2), (dict(k=None), -1), (dict(v=None), -1), (dict(k=0xC0008), -5),
+    (dict(ks=100), -3), (dict(vs=1028), -5), (dict(q=None), -1), (dict(ws=None), -6),
+])
+def test_decode_store_argument_errors(L, kw, status):
+    """The fused store + decode checks the store's arguments as store_kv does
+    and the rest as decode does (no device work: every case fails on the host)."""
+    assert _decode_store(L, _pool(), **kw) == status
+    assert L.pkv_last_error().decode()
+
+
+def test_decode_store_zero_rows_is_noop(L):
+    assert _decode_store(L, _pool(), bs=0, loc=None, k=None, v=None) == 0
+
+
 def test_decode_workspace_size_grows_with_batch(L):
     a = L.pkv_decode_workspace_size(4, 16, 1000)
     b = L.pkv_decode_workspace_size(256, 16, 1_200_000)

@@ -255,3 +255,133 @@ def test_decode_full_size_every_request(cid):
     print(f"  {len(dec)} requests: max|d|={mx:.3e} relL2={rel:.3e}", flush=True)
     worst = np.max(np.abs(oracle.widen(got, "bf16") - refs), axis=(1, 2))
     assert np.all(worst <= 2e-2)
+
+
+# ---------------------------------------------------------------- store_kv fused into decode
+
+def _fused_vs_separate(case, loc_dtype=torch.int32):
+    """pkv_paged_attention_decode_store on one copy of the pool, store_kv then
+    decode on another: the outputs and the whole pools must be equal bit for
+    bit; the separate path is itself held to the oracle above."""
+    d1, d2 = _upload_case(case), _upload_case(case)
+    ps = case["cfg"].page_size
+    kw = dict(max_total_kv=int(case["device_len"].sum()), page_size=ps)
+    loc = d1["out_loc"].to(loc_dtype)
+    pkv.store_kv(d1["k_pool"], d1["v_pool"], loc, d1["new_k"], d1["new_v"], page_size=ps)
+    o_sep = pkv.paged_attention_decode(d1["q"], d1["k_pool"], d1["v_pool"], d1["page_table"], d1["cached_len"],
+                                       d1["device_len"], **kw)
+    o_fus = pkv.paged_attention_decode_store(d2["q"], d2["k_pool"], d2["v_pool"], d2["page_table"],
+                                             d2["cached_len"], d2["device_len"], loc, d2["new_k"], d2["new_v"], **kw)
+    torch.cuda.synchronize()
+    i16 = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    assert torch.equal(i16(o_fus), i16(o_sep)), f"{case['cfg'].name}: fused output differs"
+    assert torch.equal(i16(d2["k_pool"]), i16(d1["k_pool"])) and torch.equal(i16(d2["v_pool"]), i16(d1["v_pool"]))
+    assert pkv.read_faults() == 0
+
+
+@pytest.mark.parametrize("cid,loc_dtype", [(1, torch.int32), (2, torch.int64)])
+def test_decode_store_fused_equals_store_then_decode(cid, loc_dtype):
+    print(f"decode_store case config {cid}", flush=True)
+    _fused_vs_separate(draw_case(config(cid)), loc_dtype)
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_decode_store_fused_full_size(cid):
+    """The fused call at the full sizes of the 256-request batch and of the
+    mixed batch's 240 decode rows (page_size 16, rows through table_idx), pools
+    drawn on the device: outputs and pools equal to store_kv then decode, bit
+    for bit (the separate path is held to the oracle on every request above)."""
+    from workloads import default_num_pages, draw_lengths, draw_page_table, draw_q
+    cfg = config(cid)
+    C, S = draw_lengths(cfg)
+    nump = default_num_pages(cfg, S)
+    table = draw_page_table(cfg, S, nump)
+    q_all = draw_q(cfg, C, S)
+    E = (S - C).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(E)])
+    dec = np.nonzero(E == 1)[0].astype(np.int32)
+    Cd, Sd = C[dec], S[dec]
+    num_slots = (nump + 1) * cfg.page_size
+    print(f"decode_store full-size case {cfg.name}: {len(dec)} rows, sum S {int(Sd.sum())}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(2000 + cid)
+    kp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((num_slots, 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    kp2, vp2 = kp.clone(), vp.clone()
+    nk = torch.randn((len(dec), 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    nv = torch.randn((len(dec), 8, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    q = to_dev(q_all[cu[dec]], "bf16")
+    loc, dt, dC, dS, di = (to_dev(table[dec, Cd].astype(np.int32)), to_dev(table), to_dev(Cd), to_dev(Sd),
+                           to_dev(dec))
+    kw = dict(table_idx=di, max_total_kv=int(Sd.sum()), page_size=cfg.page_size)
+    pkv.store_kv(kp, vp, loc, nk, nv, page_size=cfg.page_size)
+    o_sep = pkv.paged_attention_decode(q, kp, vp, dt, dC, dS, **kw)
+    o_fus = pkv.paged_attention_decode_store(q, kp2, vp2, dt, dC, dS, loc, nk, nv, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fus.view(torch.int16), o_sep.view(torch.int16))
+    assert torch.equal(kp2.view(torch.int16), kp.view(torch.int16))
+    assert torch.equal(vp2.view(torch.int16), vp.view(torch.int16))
+    assert pkv.read_faults() == 0
+
+
+def test_decode_store_strided_rows_and_table_idx():
+    """New rows as column slices of a fused qkv buffer; requests through
+    table_idx; lengths from 1 to 3000 (items of every kind)."""
+    c = _random_decode(41, 6, [1, 2, 700, 3000, 33, 129], table_idx=True)
+    rng = np.random.default_rng(42)
+    bs = 6
+    S, rows, table = c["S"], c["rows"], c["table"]
+    loc = table[rows, S - 1].astype(np.int32)
+    qkv = f32_to_bf16_bits(rng.standard_normal((bs, (16 + 16) * 128), dtype=np.float32))
+    qkv_d = to_dev(qkv, "bf16")
+    k, v = qkv_d[:, 16 * 128:24 * 128].view(bs, 8, 128), qkv_d[:, 24 * 128:].view(bs, 8, 128)
+    pools = [(to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16")) for _ in range(2)]
+    q = to_dev(c["q"], "bf16").view(bs, 16, 128)
+    kw = dict(table_idx=to_dev(rows), max_total_kv=int(S.sum()))
+    dt, dC, dS, dl = to_dev(table), to_dev(c["C"]), to_dev(S), to_dev(loc)
+    pkv.store_kv(pools[0][0], pools[0][1], dl, k, v)
+    o_sep = pkv.paged_attention_decode(q, pools[0][0], pools[0][1], dt, dC, dS, **kw)
+    o_fus = pkv.paged_attention_decode_store(q, pools[1][0], pools[1][1], dt, dC, dS, dl, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fus.view(torch.int16), o_sep.view(torch.int16))
+    assert torch.equal(pools[1][0].view(torch.int16), pools[0][0].view(torch.int16))
+    assert torch.equal(pools[1][1].view(torch.int16), pools[0][1].view(torch.int16))
+    assert pkv.read_faults() == 0
+
+
+def test_decode_store_fault_paths():
+    """out_loc[r] off the table's last entry: the new row is still key S - 1
+    (against the oracle with that row in place) and PKV_FAULT_OUT_LOC is set;
+    out_loc[r] outside the pool: nothing written, PKV_FAULT_STORE_SLOT."""
+    c = _random_decode(43, 3, [50, 300, 7], slots_extra=8)
+    S, table = c["S"], c["table"]
+    n_slots = c["kv"].shape[1]
+    rng = np.random.default_rng(44)
+    new = f32_to_bf16_bits(rng.standard_normal((2, 3, 8, 128), dtype=np.float32))
+    loc = table[np.arange(3), S - 1].astype(np.int32)
+    free = np.setdiff1d(np.arange(n_slots - 1), table[:3][table[:3] != n_slots - 1])
+    loc[1] = int(free[0])                                   # not the table's entry for key S - 1
+    dk, dv = to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16")
+    q = to_dev(c["q"], "bf16").view(3, 16, 128)
+    o = pkv.paged_attention_decode_store(q, dk, dv, to_dev(table), to_dev(c["C"]), to_dev(S), to_dev(loc),
+                                         to_dev(new[0], "bf16"), to_dev(new[1], "bf16"), max_total_kv=int(S.sum()))
+    torch.cuda.synchronize()
+    assert pkv.read_faults() == 0x20
+    kp, vp = c["kv"][0].copy(), c["kv"][1].copy()
+    kp[loc], vp[loc] = new[0], new[1]
+    assert np.array_equal(to_host(dk), kp) and np.array_equal(to_host(dv), vp)
+    # the reference: every request's key S - 1 is its new row, wherever out_loc points
+    kr, vr = c["kv"][0].copy(), c["kv"][1].copy()
+    kr[table[np.arange(3), S - 1]], vr[table[np.arange(3), S - 1]] = new[0], new[1]
+    ref = oracle.attention_decode(c["q"].reshape(3, 16, 128), kr, vr, table, c["C"], S, "bf16")
+    check_attention(to_host(o), ref, "bf16", "decode_store out_loc off the table")
+    # out of the pool
+    loc2 = table[np.arange(3), S - 1].astype(np.int64)
+    loc2[2] = n_slots + 5
+    before = to_host(dk).copy()
+    pkv.paged_attention_decode_store(q, dk, dv, to_dev(table), to_dev(c["C"]), to_dev(S), to_dev(loc2),
+                                     to_dev(new[0], "bf16"), to_dev(new[1], "bf16"), max_total_kv=int(S.sum()))
+    torch.cuda.synchronize()
+    assert pkv.read_faults() & 0x1
+    after = to_host(dk)
+    changed = np.nonzero(np.any(after != before, axis=(1, 2)))[0]
+    assert set(changed.tolist()) <= set(loc2[:2].tolist())
