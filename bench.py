@@ -314,8 +314,8 @@ def main():
 
 def small_steps(args):
     """Eager decode steps of the first bs requests of the 256-request batch
-    (store_kv of their new rows, decode attention, the sampler with their
-    mixed parameters), over one layer's pool with the 28-layer page count, so
+    (decode attention with the store_kv of their new rows fused in, then the
+    sampler with their mixed parameters), over one layer's pool with the 28-layer page count, so
     the slots are as scattered as in the full pool. For kernel traces of the
     small-batch path; prints one line per batch size."""
     import torch
@@ -415,8 +415,9 @@ def sampler_only(args):
 def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
     """The 64-request decode batch (device_len ~ U[256, 2048], bf16, page_size
     1, same 28-layer pool) with an all-greedy sampler (no temperature array:
-    the argmax path) over [64, 151936] logits: store_kv, decode attention and
-    argmax timed apart with HIP events on the launch stream, and as one step.
+    the argmax path) over [64, 151936] logits: store_kv, decode attention,
+    decode with the store fused in and the argmax timed apart with HIP events
+    on the launch stream, and the step (decode with its store, argmax).
     Rotates over the filled layers and four logits buffers."""
     from workloads import (HEAD_DIM, HKV, HQ, config, draw_lengths, draw_logits, draw_page_table, draw_q,
                            draw_sampling_params)
@@ -735,7 +736,7 @@ def bench_sampler_variants(torch, pkv, gen, dev, args):
 
 
 def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
-    """Decode steps (store_kv, decode attention, sampler) of the first bs
+    """Decode steps (decode attention with the store fused in, sampler) of the first bs
     requests of the 256-request batch over layer 0 of the pool, through the
     graph runner: sizes 1, 2, 4, 8, 16, ..., 256 captured largest first into
     one pool, a batch padded to the next captured size with the dummy
