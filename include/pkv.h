@@ -224,8 +224,9 @@ size_t pkv_decode_workspace_size(int32_t bs, int32_t num_q_heads, int64_t max_to
  * page table's new entries has. A request whose table entry S_r - 1 is not
  * out_loc[r] still attends to its new row as key S_r - 1 and sets
  * PKV_FAULT_OUT_LOC; an out_loc[r] outside [0, num_slots) is not written and
- * sets PKV_FAULT_STORE_SLOT; a request skipped for invalid lengths (its output
- * zero-filled, PKV_FAULT_LENGTH) stores nothing.
+ * sets PKV_FAULT_STORE_SLOT; a request skipped for an invalid length or table
+ * row (its output zero-filled, PKV_FAULT_LENGTH or PKV_FAULT_TABLE_ROW) stores
+ * nothing.
  *   out_loc   device, [bs] of int32 (loc_type PKV_I32) or int64 (PKV_I64).
  *   k, v      device, [bs, kv_heads, 128] in pool.dtype, rows k_stride /
  *             v_stride elements apart (0 = dense; strides * itemsize multiples
