@@ -385,3 +385,42 @@ def test_decode_store_fault_paths():
     after = to_host(dk)
     changed = np.nonzero(np.any(after != before, axis=(1, 2)))[0]
     assert set(changed.tolist()) <= set(loc2[:2].tolist())
+
+
+def test_decode_store_skipped_request_stores_nothing():
+    """A request skipped for an invalid table row (table_idx out of range) or
+    an invalid length (device_len beyond the table width): its output row is
+    zero, nothing is written at its out_loc, the fault bits are set, and the
+    other requests equal store_kv then decode bit for bit."""
+    c = _random_decode(45, 4, [40, 300, 9, 1000], table_idx=True)
+    S, rows, table = c["S"].copy(), c["rows"].copy(), c["table"]
+    loc = table[rows, S - 1].astype(np.int32)
+    rng = np.random.default_rng(46)
+    new = f32_to_bf16_bits(rng.standard_normal((2, 4, 8, 128), dtype=np.float32))
+    bad = rows.copy()
+    bad[1] = table.shape[0] + 7                      # request 1: table row out of range
+    S_bad = S.copy()
+    S_bad[3] = table.shape[1] + 1                    # request 3: longer than the table
+    q = to_dev(c["q"], "bf16").view(4, 16, 128)
+    dk, dv = to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16")
+    o = pkv.paged_attention_decode_store(q, dk, dv, to_dev(table), to_dev(S_bad - 1), to_dev(S_bad), to_dev(loc),
+                                         to_dev(new[0], "bf16"), to_dev(new[1], "bf16"), table_idx=to_dev(bad),
+                                         max_total_kv=int(S_bad.sum()))
+    torch.cuda.synchronize()
+    assert pkv.read_faults() == (0x8 | 0x2)
+    got = to_host(o)
+    assert not np.any(got[1]) and not np.any(got[3])
+    kp, vp = c["kv"][0].copy(), c["kv"][1].copy()
+    kp[loc[[0, 2]]], vp[loc[[0, 2]]] = new[0][[0, 2]], new[1][[0, 2]]
+    assert np.array_equal(to_host(dk), kp) and np.array_equal(to_host(dv), vp)
+    # requests 0 and 2 against the separate calls on a copy of the pool
+    d2k, d2v = to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16")
+    keep = np.array([0, 2])
+    pkv.store_kv(d2k, d2v, to_dev(loc[keep]), to_dev(new[0][keep], "bf16"), to_dev(new[1][keep], "bf16"))
+    o2 = pkv.paged_attention_decode(to_dev(c["q"][keep], "bf16").view(2, 16, 128), d2k, d2v, to_dev(table),
+                                    to_dev(S[keep] - 1), to_dev(S[keep]), table_idx=to_dev(rows[keep]),
+                                    max_total_kv=int(S[keep].sum()))
+    torch.cuda.synchronize()
+    assert pkv.read_faults() == 0
+    # equal values (the two calls merge the same partials; only a -0 could differ in bits)
+    assert np.array_equal(oracle.widen(got[keep], "bf16"), oracle.widen(to_host(o2), "bf16"))
