@@ -82,6 +82,22 @@ struct ExtendArgs {
 constexpr int kExtBlockQ = 128;  // query positions per workgroup
 constexpr int kExtThreads = 512; // 8 waves
 constexpr int kExtBlockK = 64;   // keys per LDS tile
+constexpr int kExtReadAhead = 6; // LDS operand reads in flight ahead of the MFMAs
+
+// Issue order for a loop of 16 LDS operand reads, each feeding `nh` MFMAs:
+// the reads run kExtReadAhead ahead of the products that use them, so the
+// LDS latency is hidden behind MFMAs rather than waited out before each one
+// (left to itself the scheduler keeps only one or two reads in flight).
+template <int nh>
+__device__ __forceinline__ void lds_read_ahead_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kExtReadAhead, 0); // DS reads
+#pragma unroll
+  for (int i = 0; i < 16 - kExtReadAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, nh, 0); // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, nh * kExtReadAhead, 0);
+}
 constexpr int kTileElems = kExtBlockK * kHeadDim;
 // The running maximum is only moved when a score exceeds it by more than
 // 2^kRescaleLog2 in weight: every weight then stays <= 2^kRescaleLog2, and
@@ -370,6 +386,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         for (int hh = 0; hh < NH; ++hh)
           s[hh][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[hh][ks], s[hh][kt], 0, 0, 0);
       }
+    lds_read_ahead_order<NH>();
 
     __builtin_amdgcn_s_setprio(0);
     // Online softmax for this lane's query, on raw scores: weights are
@@ -457,6 +474,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         for (int hh = 0; hh < NH; ++hh)
           oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
       }
+    lds_read_ahead_order<NH>();
 
     __builtin_amdgcn_s_setprio(0);
     // Tile kb + 1 (loaded during this tile) into the other buffer; rows of
