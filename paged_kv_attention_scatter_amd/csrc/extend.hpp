@@ -329,8 +329,10 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       bad_slot |= !ok && slot != -1;
       zero_bits |= ok ? 0u : (1u << e);
       const uint64_t off = (uint64_t)(ok ? (uint32_t)slot : 0u) * a.row_bytes;
-      kreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
-      vreg[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+      // Plain loads: the request's other query blocks read the same rows,
+      // and they find them in L2.
+      kreg[e] = *reinterpret_cast<const u32x4*>(kbase + off);
+      vreg[e] = *reinterpret_cast<const u32x4*>(vbase + off);
     }
   };
   auto store_tile = [&](auto bufc) {
@@ -389,6 +391,15 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     lds_read_ahead_order<NH>();
 
     __builtin_amdgcn_s_setprio(0);
+    // Tile kb + 1 (loaded during the previous tile) into the other buffer,
+    // which no wave reads after the previous tile's barrier; rows of tile
+    // kb + 2 and the slots of tile kb + 3 go out. Done here, the LDS stores
+    // complete and the loads travel while the softmax arithmetic runs.
+    if (kb + 1 < nkb) {
+      store_tile(std::integral_constant<int, buf ^ 1>{});
+      load_tile();
+      load_slots(kb + 3);
+    }
     // Online softmax for this lane's query, on raw scores: weights are
     // exp2(s * sc - m * sc) against the running maximum m (score units). The
     // key of s[kt][i] is kb*64 + kt*16 + 4*lg + i; only the tiles that cross
@@ -477,13 +488,6 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     lds_read_ahead_order<NH>();
 
     __builtin_amdgcn_s_setprio(0);
-    // Tile kb + 1 (loaded during this tile) into the other buffer; rows of
-    // tile kb + 2 and the slots of tile kb + 3 go out.
-    if (kb + 1 < nkb) {
-      store_tile(std::integral_constant<int, buf ^ 1>{});
-      load_tile();
-      load_slots(kb + 3);
-    }
     __syncthreads();
   };
 
