@@ -71,7 +71,8 @@ struct ExtendArgs {
   const int32_t* device_len;
   int64_t total_q;
   int32_t max_extend;
-  float scale_log2;      // sm_scale * log2(e)
+  float scale_log2;      // |sm_scale| * log2(e)
+  int32_t q_negate;      // sm_scale < 0: scores are taken with q negated
   uint32_t* faults;
   // q prologue (Qwen3's q_norm + rotary embedding), or q_w == nullptr
   const void* q_w;       // [128] bf16 norm weight
@@ -275,6 +276,17 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         qreg[hh][ks] = __builtin_bit_cast(bf16x8_v, packed);
       }
     }
+  }
+
+  if (a.q_negate) {
+    // The running maximum below is taken over raw scores scaled afterwards,
+    // which needs a positive scale: a negative sm_scale is applied as its
+    // magnitude to the scores of -q (a sign flip, exact in bf16).
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qreg[hh][ks] = __builtin_bit_cast(bf16x8_v, __builtin_bit_cast(u32x4, qreg[hh][ks]) ^ 0x80008000u);
   }
 
   f32x4_v oacc[NH][8];

@@ -52,22 +52,22 @@ def _make(seed, C, E, HKV=8, G=2, ps=1, q_pad=0, table_idx=False, extra_slots=40
                 ps=ps)
 
 
-def _run(c):
+def _run(c, sm_scale=0.0):
     HQ = c["HQ"]
     n = c["q"].shape[0]
     qd = to_dev(c["q"], "bf16")[:, :HQ * 128].view(n, HQ, 128)
     o = pkv.paged_attention_extend(
         qd, to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16"), to_dev(c["table"]), to_dev(c["C"]),
         to_dev(c["S"]), max_extend=int(c["E"].max()), page_size=c["ps"],
-        table_idx=None if c["rows"] is None else to_dev(c["rows"]))
+        table_idx=None if c["rows"] is None else to_dev(c["rows"]), sm_scale=sm_scale)
     torch.cuda.synchronize()
     return to_host(o)
 
 
-def _oracle(c, rows=None):
+def _oracle(c, rows=None, scale=None):
     qh = c["q"][:, :c["HQ"] * 128].reshape(-1, c["HQ"], 128)
     return oracle.attention_extend(qh, c["kv"][0], c["kv"][1], c["table"], c["C"], c["S"], "bf16",
-                                   table_idx=c["rows"], requests=rows)
+                                   table_idx=c["rows"], requests=rows, scale=scale)
 
 
 CASES = [
@@ -110,6 +110,20 @@ def test_extend_growing_scores(grow):
     ref = _oracle(c)
     mx, rel = check_attention(got, ref, "bf16", f"grow {grow}")
     print(f"  grow {grow}: max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0
+
+
+@pytest.mark.parametrize("scale,G", [(0.03, 2), (-0.0884, 2), (-0.0884, 1)])
+def test_extend_explicit_scale(scale, G):
+    """A softmax scale other than 1/sqrt(head_dim), negative ones included:
+    the kernel's running maximum is over unscaled scores, so a negative
+    scale must reach it through q's sign, not leave every weight at zero."""
+    c = _make(23, C=[100, 0, 333], E=[150, 70, 65], G=G)
+    print(f"extend scale {scale} G {G}", flush=True)
+    got = _run(c, sm_scale=scale)
+    ref = _oracle(c, scale=scale)
+    mx, rel = check_attention(got, ref, "bf16", f"scale {scale}")
+    print(f"  max|d|={mx:.3e} relL2={rel:.3e}")
     assert pkv.read_faults() == 0
 
 

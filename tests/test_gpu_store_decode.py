@@ -113,7 +113,7 @@ def _random_decode(seed, bs, lens, HKV=8, G=2, dtype="bf16", slots_extra=64, q_p
     return dict(S=S, C=S - 1, table=table, rows=rows if table_idx else None, kv=kv, q=qf, HQ=HQ, HKV=HKV)
 
 
-def _run_decode(c, dtype, max_total_kv=None):
+def _run_decode(c, dtype, max_total_kv=None, sm_scale=0.0):
     dk, dv = to_dev(c["kv"][0], dtype), to_dev(c["kv"][1], dtype)
     qd = to_dev(c["q"], dtype)
     bs = len(c["S"])
@@ -121,11 +121,11 @@ def _run_decode(c, dtype, max_total_kv=None):
     o = pkv.paged_attention_decode(
         qv, dk, dv, to_dev(c["table"]), to_dev(c["C"]), to_dev(c["S"]),
         table_idx=None if c["rows"] is None else to_dev(c["rows"]),
-        max_total_kv=int(c["S"].sum()) if max_total_kv is None else max_total_kv)
+        max_total_kv=int(c["S"].sum()) if max_total_kv is None else max_total_kv, sm_scale=sm_scale)
     torch.cuda.synchronize()
     qh = c["q"][:, :c["HQ"] * 128].reshape(bs, c["HQ"], 128)
     ref = oracle.attention_decode(qh, c["kv"][0], c["kv"][1], c["table"], c["C"], c["S"], dtype,
-                                  table_idx=c["rows"])
+                                  table_idx=c["rows"], scale=sm_scale if sm_scale != 0.0 else None)
     return to_host(o), ref
 
 
@@ -155,6 +155,17 @@ def test_decode_shapes(name, kw):
     print(f"decode shape case {name}", flush=True)
     got, ref = _run_decode(c, dtype)
     check_attention(got, ref, dtype, name)
+    assert pkv.read_faults() == 0
+
+
+@pytest.mark.parametrize("dtype,scale", [("bf16", 0.03), ("bf16", -0.0884), ("f32", -0.2)])
+def test_decode_explicit_scale(dtype, scale):
+    """A softmax scale other than 1/sqrt(head_dim), negative ones included:
+    the weights are those of the scaled scores, whatever the sign."""
+    c = _random_decode(31, 5, [1, 700, 64, 3000, 129], dtype=dtype)
+    print(f"decode scale {scale} ({dtype})", flush=True)
+    got, ref = _run_decode(c, dtype, sm_scale=scale)
+    check_attention(got, ref, dtype, f"scale {scale}")
     assert pkv.read_faults() == 0
 
 
