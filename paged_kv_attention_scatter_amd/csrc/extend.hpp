@@ -294,10 +294,15 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
-  float m[NH], l[NH];
+  // Running maximum m (score units), the score above which it moves (m +
+  // kRescaleLog2 / sc) and the exponent offset -m * sc, the last two kept so
+  // that a tile without a move costs one compare per head.
+  float m[NH], l[NH], mth[NH], moff[NH];
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
     m[hh] = -INFINITY;
+    mth[hh] = -INFINITY;
+    moff[hh] = 0.f;
     l[hh] = 0.f;
   }
 
@@ -373,6 +378,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   };
 
   const float sc = a.scale_log2;
+  const float thr = kRescaleLog2 / sc;
   const int t_min_wave = qb * kExtBlockQ + wave * 16;
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   const bf16x2_v ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -438,28 +444,29 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       }
       // IEEE maximum (NaN-propagating) needs no quieting of its inputs and
       // maps to the three-input v_maximum3_f32.
-      float ml[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ml[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[4 * i], v[4 * i + 1]),
-                                              __builtin_elementwise_maximum(v[4 * i + 2], v[4 * i + 3]));
-      const float mloc = __builtin_elementwise_maximum(__builtin_elementwise_maximum(ml[0], ml[1]),
-                                                       __builtin_elementwise_maximum(ml[2], ml[3]));
+      // A tree of three-input maxima over the 16 scores.
+      auto max3 = [](float x, float y, float z) {
+        return __builtin_elementwise_maximum(x, __builtin_elementwise_maximum(y, z));
+      };
+      const float a0 = max3(v[0], v[1], v[2]), a1 = max3(v[3], v[4], v[5]), a2 = max3(v[6], v[7], v[8]);
+      const float a3 = max3(v[9], v[10], v[11]), a4 = max3(v[12], v[13], v[14]);
+      const float mloc = __builtin_elementwise_maximum(max3(a0, a1, a2), max3(a3, a4, v[15]));
       // m = -inf (first tile) always moves; a lane whose keys are all masked
       // (mloc = -inf) never asks for a move.
-      if (__any((mloc - m[hh]) * sc > kRescaleLog2)) {
+      if (__any(mloc > mth[hh])) {
         float mb = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
         mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
         const float mn = fmaxf(m[hh], mb);
         const float corr = fast_exp2((m[hh] - mn) * sc);  // m = -inf: corr = 0
         m[hh] = mn;
+        mth[hh] = mn + thr;
+        moff[hh] = -mn * sc;
         l[hh] *= corr;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
       }
-      const float off = -m[hh] * sc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = fast_exp2(fmaf(v[i], sc, off));
+      for (int i = 0; i < 16; ++i) v[i] = fast_exp2(fmaf(v[i], sc, moff[hh]));
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8_v bq;
