@@ -418,7 +418,10 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
     the argmax path) over [64, 151936] logits: store_kv, decode attention,
     decode with the store fused in and the argmax timed apart with HIP events
     on the launch stream, and the step (decode with its store, argmax).
-    Rotates over the filled layers and four logits buffers."""
+    Calls that read the pool rotate over the filled layers and four
+    relabelings of the slots (8 sets of K/V rows, 2.3 GB), so that no call
+    finds its rows left in L2 or the MALL by the one before it; the argmax
+    rotates over four logits buffers."""
     from workloads import (HEAD_DIM, HKV, HQ, config, draw_lengths, draw_logits, draw_page_table, draw_q,
                            draw_sampling_params)
     cfg = config(2)
@@ -426,9 +429,13 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
     bs = len(S)
     table = draw_page_table(cfg, S, num_pages)
     q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
-    d_table = torch.from_numpy(table).to(dev)
+    sets = []
+    for r in range(4):
+        t = ((table.astype(np.int64) + r * 600_011) % num_pages).astype(np.int32)
+        d_t = torch.from_numpy(t).to(dev)
+        d_l = torch.from_numpy(t[np.arange(bs), S - 1].copy()).to(dev)
+        sets += [(pool[0, layer], pool[1, layer], d_t, d_l) for layer in range(LAYERS_FILLED)]
     d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
-    d_loc = torch.from_numpy(table[np.arange(bs), S - 1].astype(np.int32)).to(dev)
     new_k = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
     new_v = torch.randn((bs, HKV, HEAD_DIM), generator=gen, device=dev).to(torch.bfloat16)
     total_kv = int(S.sum())
@@ -441,12 +448,16 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
         bufs.append((torch.randn((bs, cfg.vocab), generator=gen, device=dev) * cfg.logit_sigma).to(torch.bfloat16))
     tokens = torch.empty(bs, dtype=torch.int32, device=dev)
     s_ws = pkv.sample_workspace(bs, cfg.vocab, dev)
-    ops = [lambda i: pkv.store_kv(pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_loc, new_k, new_v),
-           lambda i: pkv.paged_attention_decode(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED], d_table,
-                                                d_C, d_S, max_total_kv=total_kv, out=o, workspace=ws),
+    # Per iteration i: the separate store and decode on set 2i, the fused call
+    # on set 2i + 1 (mod 8).
+    def sset(i, j):
+        return sets[(2 * i + j) % len(sets)]
+    ops = [lambda i: pkv.store_kv(sset(i, 0)[0], sset(i, 0)[1], sset(i, 0)[3], new_k, new_v),
+           lambda i: pkv.paged_attention_decode(q, sset(i, 0)[0], sset(i, 0)[1], sset(i, 0)[2], d_C, d_S,
+                                                max_total_kv=total_kv, out=o, workspace=ws),
            lambda i: pkv.sample(bufs[i % len(bufs)], None, None, None, None, out=tokens, workspace=s_ws),
-           lambda i: pkv.paged_attention_decode_store(q, pool[0, i % LAYERS_FILLED], pool[1, i % LAYERS_FILLED],
-                                                      d_table, d_C, d_S, d_loc, new_k, new_v, max_total_kv=total_kv,
+           lambda i: pkv.paged_attention_decode_store(q, sset(i, 1)[0], sset(i, 1)[1], sset(i, 1)[2], d_C, d_S,
+                                                      sset(i, 1)[3], new_k, new_v, max_total_kv=total_kv,
                                                       out=o, workspace=ws)]
     step_ops = (ops[3], ops[2])  # the step: store fused into decode, then the argmax
     it = iter(range(1 << 30))
@@ -495,29 +506,38 @@ def bench_decode64(torch, pkv, pool, num_pages, gen, dev, args):
 
 def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
     """Causal extend over a cached prefix: 8 requests, E ~ U[512, 4096],
-    prefix 0-50%, page_size 1, over layer 0 of the same pool."""
+    prefix 0-50%, page_size 1, over the same pool. Calls rotate over the
+    filled layers and four relabelings of the slots (8 sets of K/V rows, about
+    1 GB), so that no call finds its rows left in L2 or the MALL by the
+    previous calls, as when each layer of a prefill reads its own rows."""
     from workloads import HEAD_DIM, HQ, config, draw_lengths, draw_page_table, draw_q
     cfg = config(4)
     C, S = draw_lengths(cfg)
     E = S - C
     table = draw_page_table(cfg, S, num_pages)
     q = torch.from_numpy(draw_q(cfg, C, S).view(np.int16)).to(dev).view(torch.bfloat16)
-    d_table = torch.from_numpy(table).to(dev)
+    tables = [torch.from_numpy(((table.astype(np.int64) + r * 600_011) % num_pages).astype(np.int32)).to(dev)
+              for r in range(4)]
+    sets = [(pool[0, layer], pool[1, layer], t) for t in tables for layer in range(LAYERS_FILLED)]
     d_C, d_S = torch.from_numpy(C).to(dev), torch.from_numpy(S).to(dev)
-    kp, vp = pool[0, 0], pool[1, 0]
     o = torch.empty_like(q)
     flops = 4.0 * HEAD_DIM * HQ * float(np.sum(E.astype(np.float64) * C + E * (E + 1) / 2.0))
-    try:
+    it = iter(range(1 << 30))
+
+    def call():
+        kp, vp, d_table = sets[next(it) % len(sets)]
         pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
+    try:
+        call()
     except pkv.PkvError as e:
         log(f"extend skipped: {e}")
         return {"extend": f"unavailable: {e}"}
-    settle(torch, lambda: pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o))
-    n = max(10, args.steps // 2)
+    settle(torch, call)
+    n = max(16, args.steps // 2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(n):
-        pkv.paged_attention_extend(q, kp, vp, d_table, d_C, d_S, max_extend=int(E.max()), out=o)
+        call()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
@@ -526,7 +546,8 @@ def bench_extend(torch, pkv, pool, num_pages, gen, dev, args):
     return {"extend_us": round(us, 2), "extend_tflop": round(flops / 1e12, 4),
             "extend_tflops": round(tflops, 1), "extend_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "extend_workload": f"8 requests, extend_len {int(E.min())}..{int(E.max())}, "
-                               f"prefix {int(C.min())}..{int(C.max())}, bf16, page_size 1"}
+                               f"prefix {int(C.min())}..{int(C.max())}, bf16, page_size 1, "
+                               f"K/V rows rotated over {len(sets)} sets"}
 
 
 def bench_qk_rope(torch, pkv, pool, num_pages, table, C, S, gen, dev, args):
@@ -743,7 +764,10 @@ def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
     request. For bs = 1, 5, 8, 60, 64 and 256: the step issued eagerly through
     the Python binding (unpadded), the padded graph replay with its inputs
     already in the runner's buffers, and run() (copying the batch in, then
-    the replay)."""
+    the replay). These three repeat one batch over the same K/V rows, which
+    for small batches stay in L2 and the MALL from one step to the next; a
+    fourth leg issues the eager step over 8 sets of rows in turn (the filled
+    layers x four relabelings of the slots), as the layers of a model would."""
     from paged_kv_attention_scatter_amd.graph import DecodeGraphRunner
     from workloads import HEAD_DIM, HKV, HQ, config, draw_sampling_params
     V = config(3).vocab
@@ -769,6 +793,13 @@ def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3
 
+    cold_sets = []
+    for r in range(4):
+        t = tab.astype(np.int64)
+        t[:-1] = (t[:-1] + r * 600_011) % dummy_slot
+        d_t = torch.from_numpy(t.astype(np.int32)).to(dev)
+        cold_sets += [(pool[0, layer], pool[1, layer], d_t, t) for layer in range(LAYERS_FILLED)]
+
     for bs in (1, 5, 8, 60, 64, 256):
         n = runner.size_for(bs)
         b_q = q[:bs].clone()
@@ -791,14 +822,26 @@ def bench_graph(torch, pkv, pool, table, C, S, q, gen, dev, args):
                                              max_total_kv=max_kv, out=o, workspace=ws_d)
             pkv.sample(b_lg, b_T, None, b_P, b_u, out=tok, workspace=ws_s)
 
+        cold_locs = [torch.from_numpy(cs[3][np.arange(bs), S[:bs] - 1].astype(np.int32)).to(dev) for cs in cold_sets]
+        it = iter(range(1 << 30))
+
+        def eager_cold():
+            i = next(it) % len(cold_sets)
+            ck, cv, ct, _ = cold_sets[i]
+            pkv.paged_attention_decode_store(b_q, ck, cv, ct, b_C, b_S, cold_locs[i], b_k, b_v, table_idx=b_idx,
+                                             max_total_kv=max_kv, out=o, workspace=ws_d)
+            pkv.sample(b_lg, b_T, None, b_P, b_u, out=tok, workspace=ws_s)
+
         args_run = (b_q, b_k, b_v, b_loc, b_idx, b_C, b_S, b_lg, b_T, b_P, b_u)
         runner.run(*args_run)                            # stage this batch (and pad it) once
         t_eager = timed(eager)
         t_replay = timed(runner.graphs[n].replay)
         t_run = timed(lambda: runner.run(*args_run))
+        t_cold = timed(eager_cold)
         log(f"decode step bs={bs} (graph size {n}): eager {t_eager:.1f} us, graph replay {t_replay:.1f} us, "
-            f"copy-in + replay {t_run:.1f} us")
+            f"copy-in + replay {t_run:.1f} us; eager over 8 sets of rows {t_cold:.1f} us")
         out[f"step_bs{bs}_eager_us"] = round(t_eager, 2)
+        out[f"step_bs{bs}_eager_rotated_us"] = round(t_cold, 2)
         out[f"step_bs{bs}_graph_us"] = round(t_replay, 2)
         out[f"step_bs{bs}_graph_run_us"] = round(t_run, 2)
     del runner
@@ -813,7 +856,9 @@ def bench_mixed(torch, pkv, dev, args):
     page_size 16, one layer's pool sized 1.25 x the pages the batch uses; the
     sampler over [242, 151936] logits, every row at T=1, top_k=50,
     top_p=0.95. One decode launch, one extend launch and the sampler on one
-    stream: timed apart and as one step."""
+    stream: timed apart and as one step. Timed alone, the extend rotates over
+    four relabelings of the chunks' pages, so that no call finds its K/V rows
+    left in L2 or the MALL by the previous ones."""
     from workloads import (HEAD_DIM, HKV, HQ, config, default_num_pages, draw_lengths, draw_page_table,
                            draw_q, draw_sampling_params, draw_uniforms)
     cfg = config(5)
@@ -855,9 +900,15 @@ def bench_mixed(torch, pkv, dev, args):
         pkv.paged_attention_decode(q_dec, kp, vp, d_table, Cd, Sd, table_idx=d_dec, max_total_kv=dec_kv,
                                    page_size=ps, out=o_dec, workspace=ws)
 
-    def extend():
-        pkv.paged_attention_extend(q_ext, kp, vp, d_table, Ce, Se, table_idx=d_ext, max_extend=max_ext,
-                                   page_size=ps, out=o_ext)
+    ext_tables = []
+    for r in range(4):
+        t = table.astype(np.int64)
+        t[ext] = (t[ext] + r * 100_003 * cfg.page_size) % (nump * cfg.page_size)
+        ext_tables.append(torch.from_numpy(t.astype(np.int32)).to(dev))
+
+    def extend(i=0):
+        pkv.paged_attention_extend(q_ext, kp, vp, ext_tables[i % len(ext_tables)], Ce, Se, table_idx=d_ext,
+                                   max_extend=max_ext, page_size=ps, out=o_ext)
 
     def sample(i):
         pkv.sample(bufs[i % len(bufs)], d_T, d_K, d_P, d_u, out=tokens, workspace=s_ws)
@@ -880,7 +931,7 @@ def bench_mixed(torch, pkv, dev, args):
 
     n = max(10, args.steps // 4)
     dec_us = timed(lambda i: decode(), n)
-    ext_us = timed(lambda i: extend(), n)
+    ext_us = timed(extend, n)
     smp_us = timed(sample, 4 * n)
     smp_mp_us = timed(sample_min_p, 4 * n)
     step_us = timed(lambda i: (decode(), extend(), sample(i)), n)

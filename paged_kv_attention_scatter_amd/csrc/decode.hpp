@@ -116,10 +116,13 @@ template <typename T, int NWD>
 __device__ __forceinline__ void load_lane_row(uint32_t (&w)[NWD], const T* base) {
   // NWD words = NWD * 4 bytes, 16-byte aligned (DPL * sizeof(T) >= 16 for the
   // supported shapes).
+  // Plain loads: with the caches cold (each row read once per step), they
+  // measured about 1% faster at bs 256 than non-temporal ones, and more on
+  // small batches.
   const u32x4* p = reinterpret_cast<const u32x4*>(base);
 #pragma unroll
   for (int i = 0; i < NWD / 4; ++i) {
-    u32x4 x = __builtin_nontemporal_load(p + i);
+    u32x4 x = p[i];
     w[4 * i + 0] = x.x;
     w[4 * i + 1] = x.y;
     w[4 * i + 2] = x.z;
