@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   const int nkb = (n_keys + kExtBlockK - 1) / kExtBlockK;
 
   // Tile loader: thread -> 2 consecutive keys (kq*2 ..) x 8 dims (dg*8 ..).
-  // Page-table entries are fetched one tile ahead of the K/V rows they
+  // Page-table entries are fetched two tiles ahead of the K/V rows they
   // address, and K/V rows one tile ahead of their use, so neither latency
   // sits between two tiles of MFMA work. Keys past the block's last key and
   // slots outside the pool load slot 0's row and are zeroed before they reach
@@ -334,6 +334,22 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       slot_raw[e] = pt[key_ok[e] ? j : 0];
     }
   };
+  // Page-table entries of later tiles: wave 0 reads a tile's 64 entries (one
+  // per lane) and puts them in LDS, where every thread finds its two.
+  __shared__ __attribute__((aligned(8))) int32_t pt_ring[2][kExtBlockK];
+  auto pt_entry = [&](int kb) {  // wave 0: this lane's entry of tile kb
+    const int j = kb * kExtBlockK + lane;
+    return j < n_keys ? pt[j] : 0;
+  };
+  auto slots_from_ring = [&](int kb, auto rbufc) {
+    constexpr int rb = decltype(rbufc)::value;
+    const int2 v = *reinterpret_cast<const int2*>(&pt_ring[rb][kq * KPT]);
+    slot_raw[0] = v.x;
+    slot_raw[1] = v.y;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) key_ok[e] = kb * kExtBlockK + kq * KPT + e < n_keys;
+  };
+  int32_t pt_next = 0;  // wave 0: the entry of the tile after the one in the ring
   u32x4 kreg[KPT], vreg[KPT];
   uint32_t zero_bits = 0;  // keys of the loaded tile to store as zeros
   bool bad_slot = false;
@@ -415,8 +431,12 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
     // complete and the loads travel while the softmax arithmetic runs.
     if (kb + 1 < nkb) {
       store_tile(std::integral_constant<int, buf ^ 1>{});
+      slots_from_ring(kb + 2, bufc);
       load_tile();
-      load_slots(kb + 3);
+      if (wave == 0) {
+        pt_ring[buf ^ 1][lane] = pt_next;  // tile kb + 3
+        pt_next = pt_entry(kb + 4);
+      }
     }
     // Online softmax for this lane's query, on raw scores: weights are
     // exp2(s * sc - m * sc) against the running maximum m (score units). The
@@ -515,7 +535,10 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   load_slots(1);
   store_tile(std::integral_constant<int, 0>{});
   load_tile();        // tile 1
-  load_slots(2);
+  if (wave == 0) {
+    pt_ring[0][lane] = pt_entry(2);
+    pt_next = pt_entry(3);
+  }
   __syncthreads();
   for (int kb = 0; kb < nkb; kb += 2) {
     step(kb, std::integral_constant<int, 0>{});
