@@ -424,11 +424,11 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
       }
     lds_read_ahead_order<NH>();
 
-    __builtin_amdgcn_s_setprio(0);
     // Tile kb + 1 (loaded during the previous tile) into the other buffer,
     // which no wave reads after the previous tile's barrier; rows of tile
     // kb + 2 and the slots of tile kb + 3 go out. Done here, the LDS stores
-    // complete and the loads travel while the softmax arithmetic runs.
+    // complete and the loads travel while the softmax arithmetic runs; the
+    // wave keeps its raised priority until they are issued.
     if (kb + 1 < nkb) {
       store_tile(std::integral_constant<int, buf ^ 1>{});
       slots_from_ring(kb + 2, bufc);
@@ -438,6 +438,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         pt_next = pt_entry(kb + 4);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // Online softmax for this lane's query, on raw scores: weights are
     // exp2(s * sc - m * sc) against the running maximum m (score units). The
     // key of s[kt][i] is kb*64 + kt*16 + 4*lg + i; only the tiles that cross
