@@ -196,7 +196,8 @@ int pkv_qk_norm_rope_store_kv(const pkv_pool* pool, const void* out_loc, int32_t
  *   device_len device int32 [bs]; 1 <= S_r <= pt_stride, else the row is
  *             zero-filled and flagged.
  *   max_total_kv host upper bound of sum(S_r); sizes the split-K plan.
- *   sm_scale  0 => 1/sqrt(head_dim).
+ *   sm_scale  0 => 1/sqrt(head_dim); any other value, negative ones
+ *             included, scales the scores as given (also for extend).
  *   ws        device workspace of at least pkv_decode_workspace_size(...) bytes
  *             for split-K partial results (no initialisation needed).
  */
