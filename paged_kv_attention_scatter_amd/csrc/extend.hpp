@@ -297,13 +297,14 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   // Running maximum m (score units), the score above which it moves (m +
   // kRescaleLog2 / sc) and the exponent offset -m * sc, the last two kept so
   // that a tile without a move costs one compare per head.
-  float m[NH], l[NH], mth[NH], moff[NH];
+  float m[NH], mth[NH], moff[NH];
+  f32x4_v lacc[NH];  // row sums (every element of a lane's vector holds its query's)
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
     m[hh] = -INFINITY;
     mth[hh] = -INFINITY;
     moff[hh] = 0.f;
-    l[hh] = 0.f;
+    lacc[hh] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
   }
 
   // Keys this workgroup needs: j <= C + (last valid position of the block).
@@ -397,7 +398,9 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   const float thr = kRescaleLog2 / sc;
   const int t_min_wave = qb * kExtBlockQ + wave * 16;
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-  const bf16x2_v ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8_v ones8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones8[j] = (__bf16)1.0f;
 
   // One key tile from LDS buffer `buf` (a compile-time constant, so every
   // LDS address below is a loop-invariant register plus an immediate).
@@ -482,7 +485,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         m[hh] = mn;
         mth[hh] = mn + thr;
         moff[hh] = -mn * sc;
-        l[hh] *= corr;
+        lacc[hh] *= corr;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[hh][dt] *= corr;
       }
@@ -495,20 +498,6 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
         for (int j = 0; j < 8; ++j) bq[j] = (__bf16)v[(2 * k2 + (j >> 2)) * 4 + (j & 3)];
         pb[hh][k2] = bq;
       }
-      // Row sum of the rounded weights (the ones the PV product uses).
-      float ls[2] = {0.f, 0.f};
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const u32x4 pw = __builtin_bit_cast(u32x4, pb[hh][k2]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // Copy the element out first: a bit cast of a vector element
-          // expression reads the vector's first element in this compiler.
-          const uint32_t pair = pw[w];
-          ls[k2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pair), ones, ls[k2], false);
-        }
-      }
-      l[hh] += ls[0] + ls[1];
     }
 
     __builtin_amdgcn_s_setprio(1);
@@ -526,6 +515,14 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
           oacc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh][k2], oacc[hh][dt], 0, 0, 0);
       }
     lds_read_ahead_order<NH>();
+    __builtin_amdgcn_sched_barrier(0);
+    // Row sums of the rounded weights (the ones the PV product uses) on the
+    // MFMA unit: an all-ones V^T tile turns every output row into the sum.
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+        lacc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb[hh][k2], lacc[hh], 0, 0, 0);
 
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
@@ -550,9 +547,7 @@ __global__ void __launch_bounds__(kExtThreads, 1) extend_kernel(ExtendArgs a) {
   // Normalise and write: lane holds dims dt*16 + 4*lg + i of query t.
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
-    float lt = l[hh];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = lacc[hh][0];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (t_ok) {
       bf16_t* orow = reinterpret_cast<bf16_t*>(a.o) + (int64_t)(qstart + t) * a.o_stride +
