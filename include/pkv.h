@@ -77,7 +77,7 @@ typedef enum { PKV_I32 = 0, PKV_I64 = 1 } pkv_itype;
 /* Device fault bits (see pkv_read_faults). */
 #define PKV_FAULT_STORE_SLOT   0x1u  /* store_kv: out_loc[i] outside [0, num_slots) */
 #define PKV_FAULT_LENGTH       0x2u  /* attention: a request's lengths are invalid */
-#define PKV_FAULT_TABLE_SLOT   0x4u  /* attention: a page-table entry outside [0, num_slots) */
+#define PKV_FAULT_TABLE_SLOT   0x4u  /* attention: a page-table entry outside [0, num_slots); its key reads as a zero K and V row */
 #define PKV_FAULT_TABLE_ROW    0x8u  /* attention: table_idx[r] outside [0, pt_rows) */
 #define PKV_FAULT_QROWS        0x10u /* extend: sum of extend lengths exceeds total_q or max_extend */
 #define PKV_FAULT_OUT_LOC      0x20u /* decode_store: page_table[t_r, S_r - 1] != out_loc[r] */

@@ -322,10 +322,16 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
       const int32_t nchunk = min(kWave, wj1 - jb);
       const int32_t s = next, pt_raw = next;
       next = lane < wj1 - (jb + kWave) ? pt[jb + kWave + lane] : -1;
+      // -1: no key (past this wave's range); -2: an entry outside the pool,
+      // whose key reads as a zero K and V row.
       int32_t myslot = -1;
       if (lane < nchunk) {
-        if (s >= 0 && (int64_t)s < a.num_slots) myslot = s;
-        else if (!(a.k_new && jb + lane == S - 1)) raise_fault(a.faults, 0x4u);  // the new key's entry: checked below
+        if (s >= 0 && (int64_t)s < a.num_slots) {
+          myslot = s;
+        } else {
+          myslot = -2;
+          if (!(a.k_new && jb + lane == S - 1)) raise_fault(a.faults, 0x4u);  // the new key's entry: checked below
+        }
       }
       for (int32_t kb = 0; kb < nchunk; kb += KB) {
         uint32_t kw[KB][NWD], vw[KB][NWD];
@@ -363,7 +369,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_splitk_kernel(DecodeArgs a)
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) {
             const float d = group_sum<LPH>(lane_dot<T, NWD>(qw[hh], kw[kk]));
-            sc[kk][hh] = sl[kk] >= 0 ? d * a.scale_log2 : -INFINITY;
+            sc[kk][hh] = sl[kk] != -1 ? d * a.scale_log2 : -INFINITY;
           }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {

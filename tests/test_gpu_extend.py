@@ -127,6 +127,26 @@ def test_extend_explicit_scale(scale, G):
     assert pkv.read_faults() == 0
 
 
+def test_extend_out_of_pool_slot_reads_as_zero_row():
+    """A page-table entry outside the pool: that key's K and V rows read as
+    zeros and PKV_FAULT_TABLE_SLOT (0x4) is raised; every output row equals
+    the oracle's over a pool in which the key's row is zero."""
+    c = _make(41, C=[300, 70, 0], E=[150, 90, 40])
+    n_slots = c["kv"].shape[1]
+    bad_r, bad_j = 0, 123            # a cached key of request 0, seen by all its queries
+    gpu_table = c["table"].copy()
+    gpu_table[bad_r, bad_j] = n_slots + 5
+    ref_table = c["table"].copy()
+    ref_table[bad_r, bad_j] = n_slots
+    zero = np.zeros((1,) + c["kv"].shape[2:], c["kv"].dtype)
+    ref_kv = np.stack([np.concatenate([c["kv"][0], zero]), np.concatenate([c["kv"][1], zero])])
+    got = _run(dict(c, table=gpu_table))
+    ref = _oracle(dict(c, table=ref_table, kv=ref_kv))
+    mx, rel = check_attention(got, ref, "bf16", "out-of-pool slot")
+    print(f"  max|d|={mx:.3e} relL2={rel:.3e}")
+    assert pkv.read_faults() == 0x4
+
+
 def test_extend_paged_equals_contiguous_bitwise():
     """The same rows through an identity page table and through a permuted one."""
     c = _make(77, C=[100, 0, 9], E=[150, 64, 300])

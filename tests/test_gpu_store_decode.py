@@ -169,6 +169,30 @@ def test_decode_explicit_scale(dtype, scale):
     assert pkv.read_faults() == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_out_of_pool_slot_reads_as_zero_row(dtype):
+    """A page-table entry outside the pool: that key's K and V rows read as
+    zeros and PKV_FAULT_TABLE_SLOT (0x4) is raised; every output row equals
+    the oracle's over a pool in which the key's row is zero."""
+    c = _random_decode(43, 4, [700, 1, 65, 2000], dtype=dtype)
+    n_slots = c["kv"].shape[1]
+    bad_r, bad_j = 3, 1500
+    ref_table = c["table"].copy()
+    ref_table[bad_r, bad_j] = n_slots
+    c["table"][bad_r, bad_j] = n_slots + 5
+    zero = np.zeros((1,) + c["kv"].shape[2:], c["kv"].dtype)
+    ref_kv = np.stack([np.concatenate([c["kv"][0], zero]), np.concatenate([c["kv"][1], zero])])
+    qv = to_dev(c["q"], dtype).view(4, c["HQ"], 128)
+    o = pkv.paged_attention_decode(qv, to_dev(c["kv"][0], dtype), to_dev(c["kv"][1], dtype), to_dev(c["table"]),
+                                   to_dev(c["C"]), to_dev(c["S"]), max_total_kv=int(c["S"].sum()))
+    torch.cuda.synchronize()
+    got = to_host(o)
+    qh = c["q"][:, :c["HQ"] * 128].reshape(4, c["HQ"], 128)
+    ref = oracle.attention_decode(qh, ref_kv[0], ref_kv[1], ref_table, c["C"], c["S"], dtype)
+    check_attention(got, ref, dtype, f"out-of-pool slot ({dtype})")
+    assert pkv.read_faults() == 0x4
+
+
 def test_decode_loose_bound_same_result():
     """A loose max_total_kv bound changes the work split, not the answer
     (beyond float reassociation)."""
