@@ -309,7 +309,7 @@ int pkv_paged_attention_decode_noalloc(const pkv_pool* pool, const void* q, int6
  *             not touched.
  *   cached_len, device_len device int32 [bs]; need 0 <= C_r < S_r <= pt_stride,
  *             E_r <= max_extend and sum(E) <= total_q, else the request is
- *             skipped and flagged.
+ *             skipped (its output rows are not written) and flagged.
  *   total_q, max_extend host bounds of sum(E_r) and max(E_r).
  *   ws        bf16 pools: unused (may be NULL, ws_bytes 0). fp32 pools: device
  *             workspace of pkv_extend_workspace_size(bs, num_q_heads, total_q,

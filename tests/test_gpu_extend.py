@@ -147,6 +147,31 @@ def test_extend_out_of_pool_slot_reads_as_zero_row():
     assert pkv.read_faults() == 0x4
 
 
+def test_extend_bad_table_row_request_is_skipped():
+    """bf16 pools: a request whose table_idx lies outside the page table is
+    skipped and flagged (PKV_FAULT_TABLE_ROW), its output rows are not
+    written, and the other requests' rows match the oracle."""
+    c = _make(73, C=[40, 100, 7], E=[70, 33, 129], table_idx=True)
+    n_rows = c["table"].shape[0]
+    rows_ok = c["rows"].copy()
+    c["rows"] = c["rows"].copy()
+    c["rows"][1] = n_rows + 3
+    HQ, n = c["HQ"], c["q"].shape[0]
+    out = torch.full((n, HQ, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    qd = to_dev(c["q"], "bf16")[:, :HQ * 128].view(n, HQ, 128)
+    pkv.paged_attention_extend(qd, to_dev(c["kv"][0], "bf16"), to_dev(c["kv"][1], "bf16"), to_dev(c["table"]),
+                               to_dev(c["C"]), to_dev(c["S"]), max_extend=int(c["E"].max()),
+                               table_idx=to_dev(c["rows"]), out=out)
+    torch.cuda.synchronize()
+    assert pkv.read_faults() == 0x8
+    got = oracle.widen(to_host(out), "bf16")
+    ref = _oracle(dict(c, rows=rows_ok), rows=[0, 2])
+    E0, E1 = int(c["E"][0]), int(c["E"][1])
+    keep = np.r_[0:E0, E0 + E1:n]
+    check_attention(to_host(out)[keep], ref[keep], "bf16", "around a skipped request")
+    assert np.all(got[E0:E0 + E1] == 7.0)
+
+
 def test_extend_paged_equals_contiguous_bitwise():
     """The same rows through an identity page table and through a permuted one."""
     c = _make(77, C=[100, 0, 9], E=[150, 64, 300])
